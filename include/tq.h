@@ -1,0 +1,197 @@
+/*
+ * tq.h - C ABI of the TurboQuant compressed KV-cache hot path for MI355X (gfx950).
+ *
+ * What the calls compute (sources are web pages on TurboQuant; cited by title and section):
+ *  - "Когда в марте 2026 года Google опубликовала статью..." (ai-news.ru overview): each
+ *    key/value vector is multiplied by a random orthogonal matrix, each rotated coordinate
+ *    is quantized with a Lloyd-Max codebook computed once for the (near-normal) post-rotation
+ *    law, with no per-group scales and no calibration data, and the residual gets a 1-bit
+ *    QJL correction.
+ *  - "Google TurboQuant простыми словами" (tproger.ru), section "Как работает TurboQuant",
+ *    step 2: QJL is a Johnson-Lindenstrauss projection of the residual that keeps one sign
+ *    bit per projected coordinate and removes the bias of the inner-product estimate.
+ *    Section "Бенчмарки TurboQuant", list "Из независимых реализаций": 52 bytes per 128
+ *    values at 3 bits (48 bytes of codes plus a 4-byte side value).
+ *  - "KV cache benchmark Qwen 3.6-35B-A3B" (ai-manual.ru), section "Неочевидный совет":
+ *    decode over a long context is bound by memory bandwidth, so attention reads the
+ *    compressed cache directly.
+ *
+ * Conventions for every call:
+ *  - d (head dimension) is 128; the sketch has m = d rows.
+ *  - Device pointers are plain HIP device addresses; host pointers are ordinary memory.
+ *  - The library never allocates or frees device memory and never synchronizes: kernels
+ *    are enqueued on the caller's stream (hip_stream, a hipStream_t; NULL = default
+ *    stream) and results are valid once that stream has been synchronized.
+ *  - Return value 0 (TQ_OK) or a negative TQ_ERR_* code.  Every argument check runs on the
+ *    host before any launch; tq_last_error() then describes the failure (thread-local).
+ *  - Non-finite inputs give unspecified codes; they are not checked.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+#define TQ_HEAD_DIM 128
+#define TQ_BLOCK_TOKENS 64
+
+enum {
+  TQ_OK = 0,
+  TQ_ERR_INVALID = -1,     /* NULL / misaligned pointer, bad shape, bad size */
+  TQ_ERR_UNSUPPORTED = -2, /* d != 128, bit width or group size not supported */
+  TQ_ERR_WORKSPACE = -3,   /* workspace too small; required size written back */
+  TQ_ERR_DEVICE = -4       /* HIP runtime error at launch */
+};
+
+typedef enum { TQ_DTYPE_BF16 = 0, TQ_DTYPE_F32 = 1 } tq_dtype;
+
+/* Cache configuration.  k_bits: scalar code bits per key coordinate (0..4; 0 = keys keep
+ * only the sign sketch); k_qjl: 1 = keys carry the 1-bit sign sketch of their residual;
+ * v_bits: value code bits (1..4); seed: fixes the rotation and the sketch.  Presets:
+ * turbo3 = (2, 1, 3), turbo4 = (3, 1, 4), sign-only keys = (0, 1, 3). */
+typedef struct tq_config {
+  int32_t d;
+  int32_t k_bits;
+  int32_t k_qjl;
+  int32_t v_bits;
+  uint64_t seed;
+} tq_config;
+
+/* Static Lloyd-Max tables for N(0,1), stored as fp32 copies of fp64 values: 2^bits levels
+ * (ascending) and 2^bits - 1 decision thresholds (midpoints).  A coordinate z of the
+ * rotated, sqrt(d)-scaled unit vector gets code #{l : z >= threshold[l]}.  *_mse is the
+ * fp64 Gaussian distortion of the table. */
+typedef struct tq_codebook {
+  tq_config cfg;
+  float k_centroids[16];
+  float k_thresholds[16];
+  float v_centroids[16];
+  float v_thresholds[16];
+  double k_mse;
+  double v_mse;
+} tq_codebook;
+
+/* Device copies of the bf16 matrices written by tq_build_codebook (row-major d x d,
+ * bf16 bit patterns).  The rotation applied is R_eff = r_hi + r_lo (y = R_eff x); the
+ * sketch is s_qjl (u = s_qjl r).  s_qjl may be NULL when keys carry no sketch. */
+typedef struct tq_dev_params {
+  const uint16_t* r_hi;
+  const uint16_t* r_lo;
+  const uint16_t* s_qjl;
+} tq_dev_params;
+
+/* Packed cache of B batch rows x Hkv kv-heads x T_cap token slots (T_cap a multiple of 64).
+ * All arrays are device memory owned by the caller, contiguous, 16-byte aligned:
+ *   k_codes [B][Hkv][T_cap/64][1024*k_bits] bytes   (NULL when k_bits == 0)
+ *   k_signs [B][Hkv][T_cap/64][1024] bytes           (NULL when k_qjl == 0)
+ *   k_norm  [B][Hkv][T_cap] fp32  key norms ||x||
+ *   k_rnorm [B][Hkv][T_cap] fp32  residual norms    (NULL unless k_qjl && k_bits > 0)
+ *   v_codes [B][Hkv][T_cap/64][1024*v_bits] bytes
+ *   v_norm  [B][Hkv][T_cap] fp32  value norms
+ * Inside a 64-token block the bits follow this fixed arrangement (64 chunks; chunk L has
+ * c = L % 16, g = L / 16; bit k is bit k % 8 of byte k / 8):
+ *   key codes (b bits): chunk L = 16 b bytes holds tokens 16 t + c (t = 0..3) and
+ *     coordinates 32 g + j (j = 0..31); code (t, j) starts at bit 32 b t + b j.
+ *   sign bits: chunk L = 16 bytes; bit 32 t + j is the sign of sketch row 32 g + j of
+ *     token 16 t + c.
+ *   value codes (b bits): chunk L = 16 b bytes holds coordinates 16 mt + c (mt = 0..7) of
+ *     tokens 16 t + 4 g + r (t, r = 0..3); code (mt, t, r) starts at bit 4 b (4 mt + t) + b r.
+ * Slots never written hold whatever the memory held; attention reads only slots below
+ * seq_len. */
+typedef struct tq_kv_cache {
+  uint8_t* k_codes;
+  uint8_t* k_signs;
+  float* k_norm;
+  float* k_rnorm;
+  uint8_t* v_codes;
+  float* v_norm;
+  int32_t B;
+  int32_t Hkv;
+  int32_t T_cap;
+} tq_kv_cache;
+
+/* Byte sizes of the arrays of tq_kv_cache for a configuration (0 for arrays not used). */
+typedef struct tq_cache_sizes {
+  size_t k_codes;
+  size_t k_signs;
+  size_t k_norm;
+  size_t k_rnorm;
+  size_t v_codes;
+  size_t v_norm;
+  size_t bytes_per_token; /* stored bytes per token and kv-head, all arrays */
+} tq_cache_sizes;
+
+/* One-time parameter build, host only, deterministic in cfg->seed.
+ * Fills *cb with the key and value codebooks (Lloyd-Max fixed point for N(0,1)).  Writes
+ * the bf16 bit patterns of R_hi, R_lo and S_b (row-major 128 x 128, caller-allocated host
+ * buffers of 16384 uint16 each; any of the three may be NULL to skip it):
+ *   G = 128x128 N(0,1) from SplitMix64 started at state 2*seed (Box-Muller, row-major);
+ *   R = Q diag(sign U_ii) from the Householder QR G = Q U (a Haar rotation);
+ *   R_hi = bf16(R), R_lo = bf16(R - R_hi), bf16() = round to fp32 then to bf16, ties to even;
+ *   S_b = bf16(S), S = 128x128 N(0,1) from the stream started at 2*seed + 1.
+ * Errors: TQ_ERR_INVALID (NULL cfg/cb), TQ_ERR_UNSUPPORTED (d != 128, k_bits outside 0..4,
+ * v_bits outside 1..4, k_qjl not 0/1, or k_bits == 0 with k_qjl == 0). */
+int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, uint16_t* r_hi, uint16_t* r_lo,
+                      uint16_t* s_qjl);
+
+/* Sizes of the cache arrays for B x Hkv x T_cap slots (T_cap a positive multiple of 64).
+ * Errors: TQ_ERR_INVALID (bad sizes / NULL), TQ_ERR_UNSUPPORTED (bad config). */
+int tq_cache_layout(const tq_config* cfg, int B, int Hkv, int T_cap, tq_cache_sizes* out);
+
+/* Quantize-on-write of n_new tokens per (batch row, kv-head) into the packed cache.
+ * k, v: device inputs, element (b, h, t, j) at offset b*stride_b + h*stride_h + t*stride_t + j
+ *   (strides in elements; the 128 coordinates of a vector are contiguous); dtype in_dtype.
+ *   Either may be NULL to write only keys or only values.
+ * start_pos: device int32 [B]; token t of row b goes to slot start_pos[b] + t.  Slots at or
+ *   beyond T_cap are skipped (the positions live in device memory, so they are not checked
+ *   on the host).  n_new = 1 is the per-step append, n_new = T the bulk (prefill) fill.
+ * Per vector x: n = ||x||, y = R_eff x / n, z = sqrt(d) y, code = #{l : z >= threshold[l]};
+ *   keys with the sketch: r = y - c[code]/sqrt(d) (r = y when k_bits == 0), stored residual
+ *   norm ||r||, sign bits [S_b r >= 0].  A zero vector gets code 2^(b-1), residual norm 0,
+ *   all sign bits 1.
+ * Errors: TQ_ERR_INVALID (NULL cb/p/cache/start_pos, both k and v NULL, B/Hkv mismatch with
+ *   the cache, n_new < 1, misaligned input, bad strides), TQ_ERR_UNSUPPORTED (config),
+ *   TQ_ERR_DEVICE (launch failure). */
+int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, const void* k, const void* v,
+                   tq_dtype in_dtype, int B, int Hkv, int n_new, int64_t stride_b,
+                   int64_t stride_h, int64_t stride_t, const int32_t* start_pos,
+                   const tq_kv_cache* cache, void* hip_stream);
+
+/* One decode step of attention for all (batch row, q-head) straight from the packed cache.
+ * q: device [B][Hq][128] in q_dtype.  q-head h reads kv-head h / (Hq / Hkv); Hq / Hkv must
+ *   be 1, 2, 4, 8 or 16.
+ * seq_len: device int32 [B], keys 0 .. seq_len[b]-1 are attended (1 <= seq_len[b] <= max_seq_len;
+ *   values outside that range are clamped into it on the device).
+ * max_seq_len: host bound on seq_len (<= T_cap); sizes the split of the context.
+ * scale: logit scale; 0 selects 1/sqrt(128).
+ * For q-head h: q1 = R_eff q, q2 = S_b q1; for key i
+ *   score_i = n_i (sum_j q1_j c[code_ij]/sqrt(d) + rnorm_i sqrt(pi/2)/m sum_j q2_j (2 sign_ij - 1))
+ *   (rnorm = 1 when k_bits == 0); p = softmax(scale * score);
+ *   out = R_eff^T sum_i p_i nv_i cv[codev_i]/sqrt(d)   (fp32 [B][Hq][128]).
+ * scores_out: NULL or device fp32 [B][Hq][T_cap]; receives scale * score_i for i < seq_len[b].
+ * workspace: device scratch of *workspace_bytes bytes (256-byte aligned).  Call with
+ *   workspace == NULL to get the required size in *workspace_bytes (returns TQ_OK).
+ * Errors: TQ_ERR_INVALID (NULL arguments, Hq not a multiple of Hkv, max_seq_len outside
+ *   1..T_cap), TQ_ERR_UNSUPPORTED (group size or config), TQ_ERR_WORKSPACE (too small;
+ *   required size written to *workspace_bytes), TQ_ERR_DEVICE (launch failure). */
+int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache,
+                     const void* q, tq_dtype q_dtype, int Hq, const int32_t* seq_len,
+                     int max_seq_len, float scale, float* out, float* scores_out,
+                     void* workspace, size_t* workspace_bytes, void* hip_stream);
+
+/* Description of the last error on this thread ("" when none). */
+const char* tq_last_error(void);
+
+/* TQ_ABI_VERSION of the built library. */
+int tq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,193 @@
+"""TurboQuant compressed KV-cache hot path for MI355X: Python binding of libtq.
+
+The functions here carry the names of the C entry points (include/tq.h) and only
+marshal arguments: torch tensors own the device memory and supply the stream; every
+step of the path runs in the HIP kernels of libtq.so.  Importing this package fails
+if libtq.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import _lib
+from ._lib import (BLOCK_TOKENS, HEAD_DIM, TQ_DTYPE_BF16, TQ_DTYPE_F32, TQCacheSizes, TQCodebook,
+                   TQConfig, TQDevParams, TQError, TQKVCache, check, lib)
+
+PRESETS = {"turbo3": (2, 1, 3), "turbo4": (3, 1, 4), "qjl1": (0, 1, 3)}
+
+__all__ = [
+    "PRESETS", "Codebook", "DeviceParams", "KVCache", "TQError", "tq_build_codebook", "tq_cache_layout",
+    "tq_quantize_kv", "tq_attend_decode", "tq_abi_version", "upload_params", "attend_workspace_bytes",
+]
+
+
+def tq_abi_version() -> int:
+    return lib.tq_abi_version()
+
+
+@dataclass
+class Codebook:
+    """Host result of tq_build_codebook: the C struct plus the bf16 bit patterns of R_hi, R_lo, S_b."""
+    cb: TQCodebook
+    r_hi: np.ndarray
+    r_lo: np.ndarray
+    s_qjl: np.ndarray
+
+    @property
+    def cfg(self) -> TQConfig:
+        return self.cb.cfg
+
+    def k_centroids(self):
+        return np.array(self.cb.k_centroids[: 1 << self.cfg.k_bits], dtype=np.float32) if self.cfg.k_bits else None
+
+    def k_thresholds(self):
+        return np.array(self.cb.k_thresholds[: (1 << self.cfg.k_bits) - 1], dtype=np.float32) if self.cfg.k_bits else None
+
+    def v_centroids(self):
+        return np.array(self.cb.v_centroids[: 1 << self.cfg.v_bits], dtype=np.float32)
+
+    def v_thresholds(self):
+        return np.array(self.cb.v_thresholds[: (1 << self.cfg.v_bits) - 1], dtype=np.float32)
+
+
+def _config(k_bits, k_qjl, v_bits, seed) -> TQConfig:
+    return TQConfig(HEAD_DIM, int(k_bits), int(k_qjl), int(v_bits), int(seed))
+
+
+def tq_build_codebook(k_bits: int, k_qjl: int, v_bits: int, seed: int = 0) -> Codebook:
+    cfg = _config(k_bits, k_qjl, v_bits, seed)
+    cb = TQCodebook()
+    n = HEAD_DIM * HEAD_DIM
+    r_hi = np.zeros(n, dtype=np.uint16)
+    r_lo = np.zeros(n, dtype=np.uint16)
+    s_b = np.zeros(n, dtype=np.uint16)
+    check(lib.tq_build_codebook(ctypes.byref(cfg), ctypes.byref(cb), r_hi.ctypes.data, r_lo.ctypes.data,
+                                s_b.ctypes.data), "tq_build_codebook")
+    return Codebook(cb, r_hi.reshape(HEAD_DIM, HEAD_DIM), r_lo.reshape(HEAD_DIM, HEAD_DIM),
+                    s_b.reshape(HEAD_DIM, HEAD_DIM))
+
+
+def tq_cache_layout(k_bits: int, k_qjl: int, v_bits: int, B: int, Hkv: int, T_cap: int) -> dict:
+    cfg = _config(k_bits, k_qjl, v_bits, 0)
+    out = TQCacheSizes()
+    check(lib.tq_cache_layout(ctypes.byref(cfg), B, Hkv, T_cap, ctypes.byref(out)), "tq_cache_layout")
+    return {name: getattr(out, name) for name, _ in TQCacheSizes._fields_}
+
+
+class DeviceParams:
+    """Device copies (torch int16 storage) of R_hi, R_lo and S_b."""
+
+    def __init__(self, codebook: Codebook, device):
+        import torch
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+
+        self.r_hi = up(codebook.r_hi)
+        self.r_lo = up(codebook.r_lo)
+        self.s_qjl = up(codebook.s_qjl)
+        self.struct = TQDevParams(self.r_hi.data_ptr(), self.r_lo.data_ptr(), self.s_qjl.data_ptr())
+
+
+def upload_params(codebook: Codebook, device="cuda") -> DeviceParams:
+    return DeviceParams(codebook, device)
+
+
+class KVCache:
+    """Packed cache tensors for B x Hkv x T_cap slots, allocated with torch on `device`."""
+
+    def __init__(self, codebook: Codebook, B: int, Hkv: int, T_cap: int, device="cuda", zero: bool = True):
+        import torch
+
+        c = codebook.cfg
+        if T_cap % BLOCK_TOKENS:
+            raise ValueError("T_cap must be a multiple of 64")
+        sizes = tq_cache_layout(c.k_bits, c.k_qjl, c.v_bits, B, Hkv, T_cap)
+        alloc = torch.zeros if zero else torch.empty
+        nb = T_cap // BLOCK_TOKENS
+        self.B, self.Hkv, self.T_cap = B, Hkv, T_cap
+        self.k_codes = alloc((B, Hkv, nb, 1024 * c.k_bits), dtype=torch.uint8, device=device) if c.k_bits else None
+        self.k_signs = alloc((B, Hkv, nb, 1024), dtype=torch.uint8, device=device) if c.k_qjl else None
+        self.k_norm = alloc((B, Hkv, T_cap), dtype=torch.float32, device=device)
+        self.k_rnorm = (alloc((B, Hkv, T_cap), dtype=torch.float32, device=device)
+                        if (c.k_qjl and c.k_bits) else None)
+        self.v_codes = alloc((B, Hkv, nb, 1024 * c.v_bits), dtype=torch.uint8, device=device)
+        self.v_norm = alloc((B, Hkv, T_cap), dtype=torch.float32, device=device)
+        self.bytes_per_token = sizes["bytes_per_token"]
+        self.struct = TQKVCache(*(0 if t is None else t.data_ptr() for t in
+                                  (self.k_codes, self.k_signs, self.k_norm, self.k_rnorm, self.v_codes,
+                                   self.v_norm)), B, Hkv, T_cap)
+
+    def tensors(self) -> dict:
+        return {n: getattr(self, n) for n in ("k_codes", "k_signs", "k_norm", "k_rnorm", "v_codes", "v_norm")}
+
+
+def _stream(device):
+    import torch
+
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return TQ_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return TQ_DTYPE_F32
+    raise TypeError(f"inputs must be bfloat16 or float32, got {t.dtype}")
+
+
+def tq_quantize_kv(codebook: Codebook, params: DeviceParams, cache: KVCache, k, v, start_pos):
+    """Quantize k/v ([B, Hkv, n_new, 128], last dim contiguous; either may be None) into the cache
+    at slots start_pos[b] + t (start_pos: int32 device tensor [B])."""
+    ref = k if k is not None else v
+    if ref is None:
+        raise ValueError("k and v are both None")
+    if k is not None and v is not None and (k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype):
+        raise ValueError("k and v must share shape, strides and dtype")
+    if ref.dim() != 4 or ref.shape[-1] != HEAD_DIM or ref.stride(-1) != 1:
+        raise ValueError("inputs must be [B, Hkv, n_new, 128] with contiguous rows")
+    B, Hkv, n_new, _ = ref.shape
+    sb, sh, st, _ = ref.stride()
+    check(lib.tq_quantize_kv(ctypes.byref(codebook.cb), ctypes.byref(params.struct),
+                             k.data_ptr() if k is not None else None, v.data_ptr() if v is not None else None,
+                             _dtype_code(ref), B, Hkv, n_new, sb, sh, st, start_pos.data_ptr(),
+                             ctypes.byref(cache.struct), _stream(ref.device)), "tq_quantize_kv")
+
+
+def attend_workspace_bytes(codebook: Codebook, params: DeviceParams, cache: KVCache, Hq: int,
+                           max_seq_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    # a workspace query needs no device data; dummy non-NULL pointers satisfy the argument check
+    check(lib.tq_attend_decode(ctypes.byref(codebook.cb), ctypes.byref(params.struct), ctypes.byref(cache.struct),
+                               ctypes.c_void_p(16), TQ_DTYPE_F32, Hq, ctypes.c_void_p(16), max_seq_len, 0.0,
+                               ctypes.c_void_p(16), None, None, ctypes.byref(n), None), "tq_attend_decode")
+    return n.value
+
+
+def tq_attend_decode(codebook: Codebook, params: DeviceParams, cache: KVCache, q, seq_len, max_seq_len: int,
+                     scale: float = 0.0, out=None, scores_out=None, workspace=None):
+    """One decode step: q [B, Hq, 128] (bf16/fp32, contiguous), seq_len int32 device [B].
+    Returns out [B, Hq, 128] fp32.  scores_out (optional) is [B, Hq, T_cap] fp32."""
+    import torch
+
+    if q.dim() != 3 or q.shape[-1] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, 128] tensor")
+    B, Hq, _ = q.shape
+    if B != cache.B:
+        raise ValueError("q batch does not match the cache")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = attend_workspace_bytes(codebook, params, cache, Hq, max_seq_len)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(workspace.numel())
+    check(lib.tq_attend_decode(ctypes.byref(codebook.cb), ctypes.byref(params.struct), ctypes.byref(cache.struct),
+                               q.data_ptr(), _dtype_code(q), Hq, seq_len.data_ptr(), max_seq_len, float(scale),
+                               out.data_ptr(), scores_out.data_ptr() if scores_out is not None else None,
+                               workspace.data_ptr(), ctypes.byref(n), _stream(q.device)), "tq_attend_decode")
+    return out

@@ -1,0 +1,623 @@
+// Decode attention straight from the packed cache, for gfx950, and its C-ABI entry point
+// tq_attend_decode.
+//
+// What is computed (pages: "Когда в марте 2026 года Google опубликовала статью..." - the
+// speed-up is in attention, and the 1-bit correction passes through the softmax;
+// "Google TurboQuant простыми словами", step 2 - the sign sketch keeps scores unbiased;
+// "KV cache benchmark Qwen 3.6-35B-A3B", section "Неочевидный совет" - decode is bound by
+// memory bandwidth):
+//   q1 = R_eff q, q2 = S_b q1;
+//   score_i = n_i (sum_j q1_j c[code_ij]/sqrt(d) + rnorm_i sqrt(pi/2)/m sum_j q2_j (2 sign_ij - 1));
+//   p = softmax(scale * score);  out = R_eff^T sum_i p_i nv_i cv[codev_i] / sqrt(d).
+//
+// Three launches on the caller's stream:
+//  1. prologue: q1, q2 per (batch row, q-head), stored as f16 with a power-of-two scale;
+//  2. main: one workgroup of 4 waves per (batch row, kv-head, context slice); each wave
+//     streams 64-key blocks of its sub-slice.  Codes are turned into f16 MFMA operands by
+//     table lookups in LDS (4 or 8 codes per lookup); keys sit on the M side of the score
+//     MFMAs (one key read serves all G q-heads of the group), the softmax weights of a
+//     score tile feed the value MFMA directly from the accumulator layout, and the value
+//     sum stays in the rotated domain.  The 4 waves merge their online-softmax states in
+//     LDS and write one partial per (q-head, slice);
+//  3. merge: log-sum-exp over slices, then the unrotation R_eff^T (fp32).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+#include <type_traits>
+#include <vector>
+
+#include "tq_common.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float KAPPA = 0.009791666936874390f;  // sqrt(pi/2)/128
+constexpr float NEG_BIG = -1.0e30f;
+constexpr int QREC = 288;   // f16 elements per prologue record: q1[128], q2[128], scales
+constexpr int PREC = 132;   // floats per partial record: acc[128], m, l, mv, pad
+
+// ---- LDS code tables ----------------------------------------------------------------------
+// A lookup turns CPL codes of B bits (one KEYBITS-bit window) into CPL f16 values.
+template <int B>
+struct Tab {
+  static constexpr int CPL = (B == 1) ? 8 : (B == 4) ? 2 : 4;
+  static constexpr int KEYBITS = B * CPL;
+  static constexpr int ENTRIES = 1 << KEYBITS;
+  static constexpr int EBYTES = 2 * CPL;
+  static constexpr int BYTES = ENTRIES * EBYTES;
+};
+
+template <int B>
+__device__ void build_table(uint8_t* tab, const float* cent, int tid, int nthreads) {
+  using T = Tab<B>;
+  _Float16 c16[1 << B];
+#pragma unroll
+  for (int l = 0; l < (1 << B); ++l) c16[l] = static_cast<_Float16>(cent[l]);
+  for (int e = tid; e < T::ENTRIES; e += nthreads) {
+    _Float16* dst = reinterpret_cast<_Float16*>(tab + e * T::EBYTES);
+#pragma unroll
+    for (int i = 0; i < T::CPL; ++i) dst[i] = c16[(e >> (B * i)) & ((1 << B) - 1)];
+  }
+}
+
+__device__ void build_sign_table(uint8_t* tab, int tid, int nthreads) {
+  for (int e = tid; e < 256; e += nthreads) {
+    _Float16* dst = reinterpret_cast<_Float16*>(tab + e * 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = ((e >> i) & 1) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
+  }
+}
+
+// Window W of 8*B bits (bits 8*B*W ..) of a little-endian dword array.
+template <int B, int W>
+__device__ __forceinline__ uint32_t window(const uint32_t* dw) {
+  constexpr int bit = 8 * B * W;
+  constexpr int word = bit >> 5, off = bit & 31;
+  uint32_t v = dw[word] >> off;
+  if constexpr (off + 8 * B > 32) v |= dw[word + 1] << (32 - off);
+  if constexpr (8 * B < 32) v &= (1u << (8 * B)) - 1u;
+  return v;
+}
+
+// 8 codes of a window -> f16x8 operand (element e = code at bits B*e of the window).
+template <int B>
+__device__ __forceinline__ f16x8 decode8(const uint8_t* tab, uint32_t w) {
+  if constexpr (B == 1) {
+    return *reinterpret_cast<const f16x8*>(tab + w * 16);
+  } else if constexpr (B == 2) {
+    const f16x4 a = *reinterpret_cast<const f16x4*>(tab + (w & 0xFFu) * 8);
+    const f16x4 b = *reinterpret_cast<const f16x4*>(tab + (w >> 8) * 8);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else if constexpr (B == 3) {
+    const f16x4 a = *reinterpret_cast<const f16x4*>(tab + (w & 0xFFFu) * 8);
+    const f16x4 b = *reinterpret_cast<const f16x4*>(tab + (w >> 12) * 8);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 a = *reinterpret_cast<const f16x2*>(tab + (w & 0xFFu) * 4);
+    const f16x2 b = *reinterpret_cast<const f16x2*>(tab + ((w >> 8) & 0xFFu) * 4);
+    const f16x2 c = *reinterpret_cast<const f16x2*>(tab + ((w >> 16) & 0xFFu) * 4);
+    const f16x2 d = *reinterpret_cast<const f16x2*>(tab + (w >> 24) * 4);
+    const f16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    const f16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+    return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void load_dwords(uint32_t* dst, const uint8_t* src) {
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i)
+    *reinterpret_cast<u32x4*>(dst + 4 * i) = *reinterpret_cast<const u32x4*>(src + 16 * i);
+}
+
+// ---- prologue -----------------------------------------------------------------------------
+struct PrologueArgs {
+  const void* q;
+  const uint16_t* r_hi;
+  const uint16_t* r_lo;
+  const uint16_t* s_b;  // may be NULL (no sketch)
+  _Float16* qrec;       // [B*Hq][QREC]
+};
+
+__device__ float block_absmax_128(float v, float* red) {
+  float m = fabsf(v);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  return fmaxf(red[0], red[1]);
+}
+
+template <bool F32>
+__global__ void __launch_bounds__(128) prologue_kernel(PrologueArgs a) {
+  __shared__ float qs[D];
+  __shared__ float q1s[D];
+  __shared__ float red[2];
+  const int j = threadIdx.x;
+  const int64_t head = blockIdx.x;
+  float qv;
+  if constexpr (F32) {
+    qv = reinterpret_cast<const float*>(a.q)[head * D + j];
+  } else {
+    qv = bf2f(reinterpret_cast<const uint16_t*>(a.q)[head * D + j]);
+  }
+  qs[j] = qv;
+  __syncthreads();
+  float q1 = 0.f;
+  for (int k = 0; k < D; ++k) {
+    q1 = fmaf(bf2f(a.r_hi[j * D + k]), qs[k], q1);
+    q1 = fmaf(bf2f(a.r_lo[j * D + k]), qs[k], q1);
+  }
+  q1s[j] = q1;
+  __syncthreads();
+  float q2 = 0.f;
+  if (a.s_b != nullptr)
+    for (int k = 0; k < D; ++k) q2 = fmaf(bf2f(a.s_b[j * D + k]), q1s[k], q2);
+  const float m1 = block_absmax_128(q1, red);
+  const float m2 = block_absmax_128(q2, red);
+  int e1 = 0, e2 = 0;
+  if (m1 > 0.f) frexpf(m1, &e1);
+  if (m2 > 0.f) frexpf(m2, &e2);
+  _Float16* rec = a.qrec + head * QREC;
+  rec[j] = static_cast<_Float16>(ldexpf(q1, -e1));
+  rec[D + j] = static_cast<_Float16>(ldexpf(q2, -e2));
+  if (j == 0) {
+    float* sc = reinterpret_cast<float*>(rec + 2 * D);
+    sc[0] = ldexpf(1.0f, e1);
+    sc[1] = ldexpf(1.0f, e2);
+  }
+}
+
+// ---- main kernel ----------------------------------------------------------------------------
+struct MainArgs {
+  const uint8_t* k_codes;
+  const uint8_t* k_signs;
+  const float* k_norm;
+  const float* k_rnorm;
+  const uint8_t* v_codes;
+  const float* v_norm;
+  const int32_t* seq_len;
+  const _Float16* qrec;
+  float* part;        // [B*Hq][n_slices][PREC]
+  float* scores_out;  // NULL or [B*Hq][T_cap]
+  int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices;
+  float scale_log2;   // scale * log2(e)
+  float scale;
+  float k_cent[16];
+  float v_cent[16];
+};
+
+template <int KB, bool QJL, int VB, int G>
+struct MainCfg {
+  static constexpr int TPD = 16 / G;       // score tiles packed into one accumulator set
+  static constexpr int NSETS = 4 / TPD;    // accumulator sets per 64-key block
+  static constexpr int KTAB = KB > 0 ? Tab<(KB > 0 ? KB : 1)>::BYTES : 0;
+  static constexpr int STAB = QJL ? 4096 : 0;
+  static constexpr int VTAB = Tab<VB>::BYTES;
+  static constexpr int TABLES = KTAB + STAB + VTAB;
+  static constexpr int MERGE = 4 * 16 * PREC * 4;  // per wave, per column: acc + state
+  static constexpr int LDS = TABLES > MERGE ? TABLES : MERGE;
+};
+
+template <int KB, bool QJL, int VB, int G>
+__global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
+  using C = MainCfg<KB, QJL, VB, G>;
+  constexpr int TPD = C::TPD, NSETS = C::NSETS;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint8_t* ktab = smem;
+  uint8_t* stab = smem + C::KTAB;
+  uint8_t* vtab = smem + C::KTAB + C::STAB;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, g = lane >> 4;
+  const int tcls = col / G;   // which tile of a set this lane's column belongs to
+  const int hh = col % G;     // q-head within the group
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int Hq = a.Hkv * G;
+  const int64_t bh = (int64_t)b * a.Hkv + kvh;
+  const int nblk_cap = a.T_cap / 64;
+
+  if constexpr (KB > 0) build_table<KB>(ktab, a.k_cent, tid, 256);
+  if constexpr (QJL) build_sign_table(stab, tid, 256);
+  build_table<VB>(vtab, a.v_cent, tid, 256);
+
+  // query operands: lane (col, g) holds q[hh][32 g + 8 kb + e] of every k-block kb
+  const _Float16* qr = a.qrec + ((int64_t)b * Hq + kvh * G + hh) * QREC;
+  f16x8 bq[4], bs[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    bq[kb] = *reinterpret_cast<const f16x8*>(qr + 32 * g + 8 * kb);
+    bs[kb] = *reinterpret_cast<const f16x8*>(qr + D + 32 * g + 8 * kb);
+  }
+  // the table holds centroids c; the key term is q1 . c / sqrt(d)
+  const float s1 = reinterpret_cast<const float*>(qr + 2 * D)[0] * INV_SQRT_D;
+  const float s2 = reinterpret_cast<const float*>(qr + 2 * D)[1];
+
+  int seq = a.seq_len[b];
+  seq = seq < 1 ? 1 : (seq > a.max_seq_len ? a.max_seq_len : seq);
+  const int nblk = (seq + 63) / 64;
+  const int slice = blockIdx.x * 4 + wave;
+  const int blk_begin = slice * a.blocks_per_wave;
+  const int blk_end = min(blk_begin + a.blocks_per_wave, nblk);
+
+  float m_run = NEG_BIG, mv_run = NEG_BIG, l_run = 0.f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  __syncthreads();  // tables ready
+
+  for (int blk = blk_begin; blk < blk_end; ++blk) {
+    // ---- loads ----------------------------------------------------------------------------
+    uint32_t kd[KB > 0 ? 4 * KB : 1];
+    uint32_t sd[4];
+    uint32_t vd[4 * VB];
+    if constexpr (KB > 0) load_dwords<4 * KB>(kd, a.k_codes + (bh * nblk_cap + blk) * (1024 * KB) + lane * 16 * KB);
+    if constexpr (QJL) load_dwords<4>(sd, a.k_signs + (bh * nblk_cap + blk) * 1024 + lane * 16);
+    load_dwords<4 * VB>(vd, a.v_codes + (bh * nblk_cap + blk) * (1024 * VB) + lane * 16 * VB);
+    f32x4 kn[NSETS], kr[NSETS], vn[NSETS];
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s) {
+      const int64_t tok = bh * a.T_cap + blk * 64 + 16 * (s * TPD + tcls) + 4 * g;
+      kn[s] = *reinterpret_cast<const f32x4*>(a.k_norm + tok);
+      if constexpr (QJL && KB > 0) kr[s] = *reinterpret_cast<const f32x4*>(a.k_rnorm + tok);
+      vn[s] = *reinterpret_cast<const f32x4*>(a.v_norm + tok);
+    }
+
+    // ---- score MFMAs: tile t = keys 16 t .. 16 t + 15 of the block ------------------------
+    f32x4 dc[4], ds[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      dc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ds[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (KB > 0) {
+        const uint32_t* seg = kd + KB * t;
+        dc[t] = mfma_f16(decode8<KB>(ktab, window<KB, 0>(seg)), bq[0], dc[t]);
+        dc[t] = mfma_f16(decode8<KB>(ktab, window<KB, 1>(seg)), bq[1], dc[t]);
+        dc[t] = mfma_f16(decode8<KB>(ktab, window<KB, 2>(seg)), bq[2], dc[t]);
+        dc[t] = mfma_f16(decode8<KB>(ktab, window<KB, 3>(seg)), bq[3], dc[t]);
+      }
+      if constexpr (QJL) {
+        const uint32_t* seg = sd + t;
+        ds[t] = mfma_f16(decode8<1>(stab, window<1, 0>(seg)), bs[0], ds[t]);
+        ds[t] = mfma_f16(decode8<1>(stab, window<1, 1>(seg)), bs[1], ds[t]);
+        ds[t] = mfma_f16(decode8<1>(stab, window<1, 2>(seg)), bs[2], ds[t]);
+        ds[t] = mfma_f16(decode8<1>(stab, window<1, 3>(seg)), bs[3], ds[t]);
+      }
+    }
+
+    // ---- logits of this lane's keys: set s, row i -> key 16 (s TPD + tcls) + 4 g + i --------
+    float lg[NSETS][4], lgv[NSETS][4];
+    float mb = NEG_BIG, mvb = NEG_BIG;
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s) {
+      f32x4 c4 = dc[s * TPD], s4 = ds[s * TPD];
+#pragma unroll
+      for (int c = 1; c < TPD; ++c) {
+        if (tcls == c) {
+          c4 = dc[s * TPD + c];
+          s4 = ds[s * TPD + c];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = blk * 64 + 16 * (s * TPD + tcls) + 4 * g + i;
+        float est = 0.f;
+        if constexpr (KB > 0) est = c4[i] * s1;
+        if constexpr (QJL) {
+          const float rn = (KB > 0) ? kr[s][i] : 1.0f;
+          est = fmaf(rn * KAPPA, s4[i] * s2, est);
+        }
+        const float logit = kn[s][i] * est * a.scale;
+        const bool valid = key < seq;
+        if (a.scores_out != nullptr && valid)
+          a.scores_out[((int64_t)b * Hq + kvh * G + hh) * a.T_cap + key] = logit;
+        const float l2 = logit * LOG2E;
+        const float vnv = vn[s][i];
+        lg[s][i] = valid ? l2 : -INFINITY;
+        lgv[s][i] = (valid && vnv > 0.f) ? l2 + __log2f(vnv) : -INFINITY;
+        mb = fmaxf(mb, lg[s][i]);
+        mvb = fmaxf(mvb, lgv[s][i]);
+      }
+    }
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    mvb = fmaxf(mvb, __shfl_xor(mvb, 16));
+    mvb = fmaxf(mvb, __shfl_xor(mvb, 32));
+    const float m_new = fmaxf(m_run, mb), mv_new = fmaxf(mv_run, mvb);
+    const float alpha = exp2f(m_run - m_new), alphav = exp2f(mv_run - mv_new);
+    m_run = m_new;
+    mv_run = mv_new;
+    float lsum = 0.f;
+    _Float16 pw[NSETS][4];
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lsum += exp2f(lg[s][i] - m_new);
+        pw[s][i] = static_cast<_Float16>(exp2f(lgv[s][i] - mv_new));
+      }
+    l_run = fmaf(l_run, alpha, lsum);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[mt] *= alphav;
+
+    // ---- value MFMAs: k-block kb2 holds tiles 2 kb2 (elements 0..3) and 2 kb2 + 1 (4..7) ---
+    static_for<0, 2>([&](auto KB2) {
+      constexpr int kb2 = decltype(KB2)::value;
+      f16x8 bp;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int te = 2 * kb2 + (e >> 2);
+        bp[e] = (te % TPD == tcls) ? pw[te / TPD][e & 3] : static_cast<_Float16>(0.0f);
+      }
+      static_for<0, 8>([&](auto MT) {
+        constexpr int mt = decltype(MT)::value;
+        const f16x8 av = decode8<VB>(vtab, window<VB, 2 * mt + kb2>(vd));
+        acc[mt] = mfma_f16(av, bp, acc[mt]);
+      });
+    });
+  }
+
+  // ---- merge the 4 waves and the TPD column classes of each q-head in LDS ---------------------
+  const float l_col = l_run + __shfl_xor(l_run, 16);
+  const float l_tot = l_col + __shfl_xor(l_col, 32);
+  __syncthreads();  // tables dead
+  float* mrg = reinterpret_cast<float*>(smem);
+  float* rec = mrg + (wave * 16 + col) * PREC;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rec[16 * mt + 4 * g + i] = acc[mt][i];
+  if (g == 0) {
+    rec[128] = m_run;
+    rec[129] = l_tot;
+    rec[130] = mv_run;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, j = idx % D;
+    float M = NEG_BIG, MV = NEG_BIG;
+    for (int w = 0; w < 4; ++w)
+      for (int c = 0; c < TPD; ++c) {
+        const float* r = mrg + (w * 16 + c * G + h) * PREC;
+        M = fmaxf(M, r[128]);
+        MV = fmaxf(MV, r[130]);
+      }
+    float Ls = 0.f, A = 0.f;
+    for (int w = 0; w < 4; ++w)
+      for (int c = 0; c < TPD; ++c) {
+        const float* r = mrg + (w * 16 + c * G + h) * PREC;
+        Ls += r[129] * exp2f(r[128] - M);
+        A += r[j] * exp2f(r[130] - MV);
+      }
+    float* out = a.part + (((int64_t)b * Hq + kvh * G + h) * a.n_slices + blockIdx.x) * PREC;
+    out[j] = A;
+    if (j == 0) {
+      out[128] = M;
+      out[129] = Ls;
+      out[130] = MV;
+    }
+  }
+}
+
+// ---- merge over slices and unrotation ---------------------------------------------------------
+struct MergeArgs {
+  const float* part;
+  const uint16_t* r_hi;
+  const uint16_t* r_lo;
+  float* out;
+  int Hq, n_slices;
+};
+
+__global__ void __launch_bounds__(128) merge_kernel(MergeArgs a) {
+  __shared__ float os[D];
+  const int j = threadIdx.x;
+  const int64_t head = (int64_t)blockIdx.y * a.Hq + blockIdx.x;
+  const float* base = a.part + head * a.n_slices * PREC;
+  float M = NEG_BIG, MV = NEG_BIG;
+  for (int s = 0; s < a.n_slices; ++s) {
+    M = fmaxf(M, base[s * PREC + 128]);
+    MV = fmaxf(MV, base[s * PREC + 130]);
+  }
+  float L = 0.f, A = 0.f;
+  for (int s = 0; s < a.n_slices; ++s) {
+    const float* r = base + s * PREC;
+    L += r[129] * exp2f(r[128] - M);
+    A += r[j] * exp2f(r[130] - MV);
+  }
+  // value centroids enter as c / sqrt(d)
+  os[j] = L > 0.f ? (A / L) * exp2f(MV - M) * INV_SQRT_D : 0.f;
+  __syncthreads();
+  // out = R_eff^T o_rot: out_k = sum_i R_eff[i][k] o_rot_i
+  float o = 0.f;
+  for (int i = 0; i < D; ++i) {
+    o = fmaf(bf2f(a.r_hi[i * D + j]), os[i], o);
+    o = fmaf(bf2f(a.r_lo[i * D + j]), os[i], o);
+  }
+  a.out[head * D + j] = o;
+}
+
+template <int KB, bool QJL, int VB, int G>
+hipError_t launch_main(const MainArgs& a, int n_slices, int B, hipStream_t s) {
+  using C = MainCfg<KB, QJL, VB, G>;
+  auto kern = attend_kernel<KB, QJL, VB, G>;
+  if (C::LDS > 65536) {
+    static std::once_flag once;
+    std::call_once(once, [&] {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    });
+  }
+  hipLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(256), C::LDS, s, a);
+  return hipGetLastError();
+}
+
+template <int KB, bool QJL, int VB>
+hipError_t dispatch_g(const MainArgs& a, int G, int n_slices, int B, hipStream_t s) {
+  switch (G) {
+    case 4: return launch_main<KB, QJL, VB, 4>(a, n_slices, B, s);
+    case 8: return launch_main<KB, QJL, VB, 8>(a, n_slices, B, s);
+    case 16: return launch_main<KB, QJL, VB, 16>(a, n_slices, B, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int KB, bool QJL>
+hipError_t dispatch_v(const MainArgs& a, int VB, int G, int n_slices, int B, hipStream_t s) {
+  switch (VB) {
+    case 2: return dispatch_g<KB, QJL, 2>(a, G, n_slices, B, s);
+    case 3: return dispatch_g<KB, QJL, 3>(a, G, n_slices, B, s);
+    case 4: return dispatch_g<KB, QJL, 4>(a, G, n_slices, B, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool supported(const tq_config& c, int G) {
+  const bool keys = (c.k_qjl == 1 && (c.k_bits == 0 || c.k_bits == 2 || c.k_bits == 3)) ||
+                    (c.k_qjl == 0 && (c.k_bits == 2 || c.k_bits == 3));
+  return keys && c.v_bits >= 2 && c.v_bits <= 4 && (G == 4 || G == 8 || G == 16);
+}
+
+hipError_t dispatch_main(const MainArgs& a, const tq_config& c, int G, int n_slices, int B, hipStream_t s) {
+  if (c.k_qjl) {
+    switch (c.k_bits) {
+      case 0: return dispatch_v<0, true>(a, c.v_bits, G, n_slices, B, s);
+      case 2: return dispatch_v<2, true>(a, c.v_bits, G, n_slices, B, s);
+      case 3: return dispatch_v<3, true>(a, c.v_bits, G, n_slices, B, s);
+    }
+  } else {
+    switch (c.k_bits) {
+      case 2: return dispatch_v<2, false>(a, c.v_bits, G, n_slices, B, s);
+      case 3: return dispatch_v<3, false>(a, c.v_bits, G, n_slices, B, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= static_cast<int>(cache.size())) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+}  // namespace tq
+
+extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache,
+                                const void* q, tq_dtype q_dtype, int Hq, const int32_t* seq_len, int max_seq_len,
+                                float scale, float* out, float* scores_out, void* workspace,
+                                size_t* workspace_bytes, void* hip_stream) {
+  using namespace tq;
+  clear_error();
+  if (cb == nullptr || p == nullptr || cache == nullptr || q == nullptr || seq_len == nullptr || out == nullptr ||
+      workspace_bytes == nullptr)
+    return fail(TQ_ERR_INVALID, "cb, p, cache, q, seq_len, out and workspace_bytes must not be NULL");
+  int rc = check_config(cb->cfg);
+  if (rc != TQ_OK) return rc;
+  rc = check_cache(cb->cfg, *cache);
+  if (rc != TQ_OK) return rc;
+  if (Hq < 1 || Hq % cache->Hkv != 0) return fail(TQ_ERR_INVALID, "Hq must be a positive multiple of Hkv");
+  const int G = Hq / cache->Hkv;
+  if (!supported(cb->cfg, G))
+    return fail(TQ_ERR_UNSUPPORTED,
+                "attention supports keys (2|3 bits, sketch on/off) or sketch-only keys, values of 2..4 bits, "
+                "and Hq/Hkv in {4, 8, 16}");
+  if (max_seq_len < 1 || max_seq_len > cache->T_cap) return fail(TQ_ERR_INVALID, "max_seq_len must be in 1..T_cap");
+  if (q_dtype != TQ_DTYPE_BF16 && q_dtype != TQ_DTYPE_F32) return fail(TQ_ERR_UNSUPPORTED, "query dtype");
+  if (p->r_hi == nullptr || p->r_lo == nullptr || (cb->cfg.k_qjl && p->s_qjl == nullptr))
+    return fail(TQ_ERR_INVALID, "device parameter matrices missing");
+  if (!aligned(out, 4) || (scores_out && !aligned(scores_out, 4)) || !aligned(q, q_dtype == TQ_DTYPE_F32 ? 4 : 2))
+    return fail(TQ_ERR_INVALID, "misaligned q / out / scores_out");
+
+  const int B = cache->B;
+  const int nblk_max = (max_seq_len + 63) / 64;
+  const int units = B * cache->Hkv;
+  const int target_wg = 2 * device_cu_count();
+  constexpr int MIN_BLOCKS_PER_WAVE = 4;
+  int n_slices = (target_wg + units - 1) / units;
+  const int max_slices = std::max(1, (nblk_max + 4 * MIN_BLOCKS_PER_WAVE - 1) / (4 * MIN_BLOCKS_PER_WAVE));
+  n_slices = std::max(1, std::min(n_slices, max_slices));
+  const int bpw = (nblk_max + 4 * n_slices - 1) / (4 * n_slices);
+  n_slices = (nblk_max + 4 * bpw - 1) / (4 * bpw);
+
+  const size_t qrec_bytes = align256(static_cast<size_t>(B) * Hq * QREC * sizeof(_Float16));
+  const size_t part_bytes = align256(static_cast<size_t>(B) * Hq * n_slices * PREC * sizeof(float));
+  const size_t need = qrec_bytes + part_bytes;
+  if (workspace == nullptr) {
+    *workspace_bytes = need;
+    return TQ_OK;
+  }
+  if (*workspace_bytes < need) {
+    *workspace_bytes = need;
+    return fail(TQ_ERR_WORKSPACE, "workspace too small");
+  }
+  if (!aligned(workspace, 256)) return fail(TQ_ERR_INVALID, "workspace must be 256-byte aligned");
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  _Float16* qrec = reinterpret_cast<_Float16*>(workspace);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + qrec_bytes);
+  if (scale == 0.f) scale = INV_SQRT_D;
+
+  PrologueArgs pa{q, p->r_hi, p->r_lo, cb->cfg.k_qjl ? p->s_qjl : nullptr, qrec};
+  if (q_dtype == TQ_DTYPE_F32)
+    hipLaunchKernelGGL(prologue_kernel<true>, dim3(B * Hq), dim3(128), 0, s, pa);
+  else
+    hipLaunchKernelGGL(prologue_kernel<false>, dim3(B * Hq), dim3(128), 0, s, pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("prologue launch: ") + hipGetErrorString(e));
+
+  MainArgs ma{};
+  ma.k_codes = cache->k_codes;
+  ma.k_signs = cache->k_signs;
+  ma.k_norm = cache->k_norm;
+  ma.k_rnorm = cache->k_rnorm;
+  ma.v_codes = cache->v_codes;
+  ma.v_norm = cache->v_norm;
+  ma.seq_len = seq_len;
+  ma.qrec = qrec;
+  ma.part = part;
+  ma.scores_out = scores_out;
+  ma.Hkv = cache->Hkv;
+  ma.T_cap = cache->T_cap;
+  ma.max_seq_len = max_seq_len;
+  ma.blocks_per_wave = bpw;
+  ma.n_slices = n_slices;
+  ma.scale = scale;
+  ma.scale_log2 = scale * LOG2E;
+  for (int l = 0; l < 16; ++l) {
+    ma.k_cent[l] = cb->k_centroids[l];
+    ma.v_cent[l] = cb->v_centroids[l];
+  }
+  e = dispatch_main(ma, cb->cfg, G, n_slices, B, s);
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("attention launch: ") + hipGetErrorString(e));
+
+  MergeArgs mg{part, p->r_hi, p->r_lo, out, Hq, n_slices};
+  hipLaunchKernelGGL(merge_kernel, dim3(Hq, B), dim3(128), 0, s, mg);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("merge launch: ") + hipGetErrorString(e));
+  return TQ_OK;
+}

@@ -1,0 +1,201 @@
+"""GPU parity of the HIP path against the oracle (small and mid-size workloads, edge cases).
+
+Every call goes through libtq's C ABI (kv_cache_vector_tq_amd binds it with ctypes).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import tq_workloads as wl
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU machines deselect these tests
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import kv_cache_vector_tq_amd as tq  # noqa: E402
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def _setup(preset, B, Hkv, T_cap, seed=0, zero=True):
+    cb = tq.tq_build_codebook(*wl.PRESETS[preset], seed=seed)
+    dp = tq.upload_params(cb)
+    cache = tq.KVCache(cb, B, Hkv, T_cap, zero=zero)
+    return cb, dp, cache
+
+
+def _run_workload_full(w, preset):
+    """Quantize the whole workload and attend once; return everything for the comparison."""
+    K = wl.host_tensor(w, wl.TENSOR_K)
+    V = wl.host_tensor(w, wl.TENSOR_V)
+    Q = wl.host_tensor(w, wl.TENSOR_Q)
+    cb, dp, cache = _setup(preset, w.B, w.Hkv, wl.round_up(w.T, 64))
+    say(w.name, preset, "quantize", K.shape)
+    start = torch.zeros(w.B, dtype=torch.int32, device="cuda")
+    tq.tq_quantize_kv(cb, dp, cache, H.to_device(K, w.dtype), H.to_device(V, w.dtype), start)
+    seq = torch.full((w.B,), w.T, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((w.B, w.Hq, cache.T_cap), dtype=torch.float32, device="cuda")
+    say(w.name, preset, "attend")
+    out = tq.tq_attend_decode(cb, dp, cache, H.to_device(Q, w.dtype), seq, w.T, scores_out=scores)
+    torch.cuda.synchronize()
+    say(w.name, preset, "device done")
+    q_used = Q if w.dtype == "f32" else wl.round_to_bf16(Q)
+    return K, V, q_used, H.cache_host(cache), out.cpu().numpy(), scores.cpu().numpy()
+
+
+@pytest.mark.parametrize("wname,preset", [("c1_single_head_t4096", "turbo3"),
+                                          ("c2_llama8b_layer_t32k", "turbo3"),
+                                          ("c2_llama8b_layer_t32k", "turbo4")])
+def test_workload_parity(wname, preset):
+    w = wl.workload(wname)
+    K, V, Q, hc, out, scores = _run_workload_full(w, preset)
+    orc = H.make_oracle(preset)
+    stats, errs = {}, []
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            kg = H.unpack_keys(orc, hc, b, h, w.T)
+            vg = H.unpack_values(orc, hc, b, h, w.T)
+            H.compare_keys(orc, K[b, h], kg, stats)
+            H.compare_values(orc, V[b, h], vg, stats)
+            hs = slice(h * w.G, (h + 1) * w.G)
+            errs.append(H.compare_attention(orc, Q[b, hs], kg, vg, w.T, out[b, hs], scores[b, hs]))
+    H.finish_stats(stats)
+    say(wname, preset, "codes", stats, "max rel err", max(e["out"] for e in errs), max(e["score"] for e in errs))
+
+
+@pytest.mark.parametrize("preset", ["turbo3", "turbo4", "qjl1"])
+def test_ragged_appends_and_canary(preset):
+    """Bulk fill from unaligned starts, then one-token and block-crossing appends; slots never
+    written keep their canary bytes."""
+    B, Hkv, T_cap = 3, 2, 256
+    cb, dp, cache = _setup(preset, B, Hkv, T_cap, zero=False)
+    for t in cache.tensors().values():
+        if t is not None:
+            if t.dtype == torch.uint8:
+                t.fill_(0xA5)
+            else:
+                t.fill_(0.5)
+    rng = np.random.default_rng(7)
+    starts = [0, 37, 64]
+    steps = [(150, starts), (1, [s + 150 for s in starts]), (5, [s + 151 for s in starts])]
+    X = {"k": np.zeros((B, Hkv, T_cap, 128), np.float32), "v": np.zeros((B, Hkv, T_cap, 128), np.float32)}
+    written = np.zeros((B, T_cap), dtype=bool)
+    for n_new, st in steps:
+        k = wl.round_to_bf16(rng.standard_normal((B, Hkv, n_new, 128)).astype(np.float32) * 3)
+        v = wl.round_to_bf16(rng.standard_normal((B, Hkv, n_new, 128)).astype(np.float32))
+        for b in range(B):
+            X["k"][b, :, st[b]:st[b] + n_new] = k[b]
+            X["v"][b, :, st[b]:st[b] + n_new] = v[b]
+            written[b, st[b]:st[b] + n_new] = True
+        say("ragged", preset, "append", n_new, st)
+        tq.tq_quantize_kv(cb, dp, cache, H.to_device(k, "bf16"), H.to_device(v, "bf16"),
+                          torch.tensor(st, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    hc = H.cache_host(cache)
+    orc = H.make_oracle(preset)
+    canary = {name: np.full_like(a, 0xA5) for name, a in hc.items() if a is not None and a.dtype == np.uint8}
+    stats = {}
+    for b in range(B):
+        wr = np.nonzero(written[b])[0]
+        un = np.nonzero(~written[b])[0]
+        for h in range(Hkv):
+            kg = H.unpack_keys(orc, hc, b, h, T_cap)
+            vg = H.unpack_values(orc, hc, b, h, T_cap)
+            H.compare_keys(orc, X["k"][b, h, wr], {n: a[wr] for n, a in kg.items()}, stats)
+            H.compare_values(orc, X["v"][b, h, wr], {n: a[wr] for n, a in vg.items()}, stats)
+            # untouched slots
+            assert np.all(hc["k_norm"][b, h, un] == 0.5) and np.all(hc["v_norm"][b, h, un] == 0.5)
+            kc = H.unpack_keys(orc, {**hc, **canary}, b, h, T_cap)
+            vc = H.unpack_values(orc, {**hc, **canary}, b, h, T_cap)
+            if orc.k_bits:
+                np.testing.assert_array_equal(kg["idx"][un], kc["idx"][un])
+            np.testing.assert_array_equal(kg["sign"][un], kc["sign"][un])
+            np.testing.assert_array_equal(vg["idx"][un], vc["idx"][un])
+    H.finish_stats(stats)
+
+
+@pytest.mark.parametrize("preset,G", [("turbo3", 4), ("turbo4", 8), ("qjl1", 8), ("turbo3", 16)])
+def test_attention_ragged_lengths(preset, G):
+    """Different sequence lengths per batch row (1, partial blocks, several slices)."""
+    B, Hkv, T_cap = 4, 2, 2048
+    cb, dp, cache = _setup(preset, B, Hkv, T_cap)
+    rng = np.random.default_rng(11)
+    K = wl.round_to_bf16(rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32) * 2)
+    V = wl.round_to_bf16(rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32))
+    Q = wl.round_to_bf16(rng.standard_normal((B, Hkv * G, 128)).astype(np.float32))
+    start = torch.zeros(B, dtype=torch.int32, device="cuda")
+    say("ragged-attn", preset, G, "quantize")
+    tq.tq_quantize_kv(cb, dp, cache, H.to_device(K, "bf16"), H.to_device(V, "bf16"), start)
+    lens = [1, 63, 1000, 2048]
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((B, Hkv * G, T_cap), dtype=torch.float32, device="cuda")
+    say("ragged-attn", preset, G, "attend")
+    out = tq.tq_attend_decode(cb, dp, cache, H.to_device(Q, "bf16"), seq, T_cap, scores_out=scores)
+    torch.cuda.synchronize()
+    hc, out, scores = H.cache_host(cache), out.cpu().numpy(), scores.cpu().numpy()
+    orc = H.make_oracle(preset)
+    for b in range(B):
+        for h in range(Hkv):
+            kg = H.unpack_keys(orc, hc, b, h, lens[b])
+            vg = H.unpack_values(orc, hc, b, h, lens[b])
+            hs = slice(h * G, (h + 1) * G)
+            H.compare_attention(orc, Q[b, hs], kg, vg, lens[b], out[b, hs], scores[b, hs])
+            # no score is written past the sequence length
+            assert np.all(scores[b, hs, lens[b]:] == 0)
+
+
+def test_special_vectors():
+    """Zero vectors, one-hot vectors, huge and tiny magnitudes, fp32 inputs."""
+    preset = "turbo3"
+    T = 128
+    cb, dp, cache = _setup(preset, 1, 1, T)
+    rng = np.random.default_rng(5)
+    K = rng.standard_normal((1, 1, T, 128)).astype(np.float32)
+    K[0, 0, 0] = 0
+    K[0, 0, 1] = 0
+    K[0, 0, 1, 17] = 1.0
+    K[0, 0, 2] *= 1e30
+    K[0, 0, 3] *= 1e-30
+    K[0, 0, 4] = 1.0
+    V = K.copy()
+    say("special", "quantize")
+    tq.tq_quantize_kv(cb, dp, cache, H.to_device(K, "f32"), H.to_device(V, "f32"),
+                      torch.zeros(1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    hc = H.cache_host(cache)
+    orc = H.make_oracle(preset)
+    stats = {}
+    kg = H.unpack_keys(orc, hc, 0, 0, T)
+    vg = H.unpack_values(orc, hc, 0, 0, T)
+    H.compare_keys(orc, K[0, 0].astype(np.float64), kg, stats)
+    H.compare_values(orc, V[0, 0].astype(np.float64), vg, stats)
+    assert kg["n"][0] == 0 and np.all(kg["idx"][0] == 2) and kg["gamma"][0] == 0 and np.all(kg["sign"][0])
+    assert np.all(vg["idx"][0] == 4)
+
+
+def test_deterministic():
+    preset = "turbo3"
+    B, Hkv, T = 2, 2, 1024
+    rng = np.random.default_rng(1)
+    K = H.to_device(wl.round_to_bf16(rng.standard_normal((B, Hkv, T, 128)).astype(np.float32)), "bf16")
+    V = H.to_device(wl.round_to_bf16(rng.standard_normal((B, Hkv, T, 128)).astype(np.float32)), "bf16")
+    Q = H.to_device(wl.round_to_bf16(rng.standard_normal((B, Hkv * 4, 128)).astype(np.float32)), "bf16")
+    outs = []
+    for rep in range(2):
+        cb, dp, cache = _setup(preset, B, Hkv, T)
+        say("determinism", rep)
+        tq.tq_quantize_kv(cb, dp, cache, K, V, torch.zeros(B, dtype=torch.int32, device="cuda"))
+        out = tq.tq_attend_decode(cb, dp, cache, Q, torch.full((B,), T, dtype=torch.int32, device="cuda"), T)
+        torch.cuda.synchronize()
+        outs.append((H.cache_host(cache), out.cpu().numpy()))
+    for name, a in outs[0][0].items():
+        if a is not None:
+            np.testing.assert_array_equal(a, outs[1][0][name])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])

@@ -1,0 +1,152 @@
+"""CPU tests of libtq's host side: exports, parameter build parity with the oracle, sizes,
+and argument checks that fail before any launch (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_vector_tq_amd as tq
+from kv_cache_vector_tq_amd import _lib
+from oracle import layout
+from oracle.lloyd_max import codebook_f32
+from oracle.params import build_params
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tq_\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert {"tq_build_codebook", "tq_quantize_kv", "tq_attend_decode", "tq_last_error",
+            "tq_abi_version", "tq_cache_layout"} <= names
+    so = ctypes.CDLL(_lib.LIB_PATH)
+    for n in names:
+        assert hasattr(so, n), n
+
+
+def test_abi_version():
+    assert tq.tq_abi_version() == 1
+
+
+@pytest.mark.parametrize("preset", ["turbo3", "turbo4", "qjl1"])
+@pytest.mark.parametrize("seed", [0, 1, 12345])
+def test_parameter_build_matches_oracle_bit_for_bit(preset, seed):
+    kb, kq, vb = tq.PRESETS[preset]
+    cb = tq.tq_build_codebook(kb, kq, vb, seed)
+    p = build_params(seed)
+    np.testing.assert_array_equal(cb.r_hi, p["r_hi"])
+    np.testing.assert_array_equal(cb.r_lo, p["r_lo"])
+    np.testing.assert_array_equal(cb.s_qjl, p["s_b"])
+    vc, vt, vmse = codebook_f32(vb)
+    np.testing.assert_array_equal(cb.v_centroids(), vc)
+    np.testing.assert_array_equal(cb.v_thresholds(), vt)
+    assert abs(cb.cb.v_mse - vmse) < 1e-15
+    if kb:
+        kc, kt, kmse = codebook_f32(kb)
+        np.testing.assert_array_equal(cb.k_centroids(), kc)
+        np.testing.assert_array_equal(cb.k_thresholds(), kt)
+        assert abs(cb.cb.k_mse - kmse) < 1e-15
+
+
+@pytest.mark.parametrize("bad", [dict(k_bits=0, k_qjl=0, v_bits=3), dict(k_bits=5, k_qjl=1, v_bits=3),
+                                 dict(k_bits=2, k_qjl=2, v_bits=3), dict(k_bits=2, k_qjl=1, v_bits=0),
+                                 dict(k_bits=2, k_qjl=1, v_bits=5)])
+def test_bad_configs_rejected(bad):
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_build_codebook(**bad)
+    assert e.value.code == _lib.TQ_ERR_UNSUPPORTED
+
+
+def test_bad_head_dim_rejected():
+    cfg = _lib.TQConfig(64, 2, 1, 3, 0)
+    cb = _lib.TQCodebook()
+    assert _lib.lib.tq_build_codebook(ctypes.byref(cfg), ctypes.byref(cb), None, None, None) == _lib.TQ_ERR_UNSUPPORTED
+    assert b"d = 128" in _lib.lib.tq_last_error()
+    assert _lib.lib.tq_build_codebook(None, ctypes.byref(cb), None, None, None) == _lib.TQ_ERR_INVALID
+
+
+@pytest.mark.parametrize("preset", ["turbo3", "turbo4", "qjl1"])
+def test_cache_layout_sizes(preset):
+    kb, kq, vb = tq.PRESETS[preset]
+    s = tq.tq_cache_layout(kb, kq, vb, 2, 3, 256)
+    slots = 2 * 3 * 256
+    assert s["k_codes"] == slots * 128 * kb // 8
+    assert s["k_signs"] == (slots * 16 if kq else 0)
+    assert s["v_codes"] == slots * 128 * vb // 8
+    assert s["k_norm"] == s["v_norm"] == slots * 4
+    assert s["bytes_per_token"] == layout.bytes_per_token(kb, kq, vb)["total"]
+    with pytest.raises(tq.TQError):
+        tq.tq_cache_layout(kb, kq, vb, 1, 1, 100)
+
+
+class _FakeCache:
+    """Cache descriptor with fake (never dereferenced) aligned device addresses."""
+
+    def __init__(self, cb, B=1, Hkv=1, T_cap=64):
+        c = cb.cfg
+        addr = iter(range(1 << 20, 1 << 30, 1 << 16))
+        self.struct = _lib.TQKVCache(next(addr) if c.k_bits else 0, next(addr) if c.k_qjl else 0, next(addr),
+                                     next(addr) if (c.k_qjl and c.k_bits) else 0, next(addr), next(addr),
+                                     B, Hkv, T_cap)
+
+
+def _quantize_rc(cb, cache, **kw):
+    args = dict(k=1 << 12, v=1 << 13, dtype=_lib.TQ_DTYPE_BF16, B=1, Hkv=1, n_new=1, sb=128, sh=128, st=128,
+                start=1 << 14)
+    args.update(kw)
+    params = _lib.TQDevParams(1 << 15, 1 << 16, 1 << 17)
+    return _lib.lib.tq_quantize_kv(ctypes.byref(cb.cb), ctypes.byref(params), args["k"], args["v"], args["dtype"],
+                                   args["B"], args["Hkv"], args["n_new"], args["sb"], args["sh"], args["st"],
+                                   args["start"], ctypes.byref(cache.struct), None)
+
+
+@pytest.mark.parametrize("kw", [dict(k=None, v=None), dict(B=2), dict(n_new=0), dict(st=100), dict(k=(1 << 12) + 2),
+                                dict(start=None), dict(sb=-128)])
+def test_quantize_argument_checks(kw):
+    cb = tq.tq_build_codebook(2, 1, 3)
+    assert _quantize_rc(cb, _FakeCache(cb), **kw) == _lib.TQ_ERR_INVALID
+
+
+def test_quantize_rejects_bad_cache():
+    cb = tq.tq_build_codebook(2, 1, 3)
+    cache = _FakeCache(cb)
+    cache.struct.k_signs = 0
+    assert _quantize_rc(cb, cache) == _lib.TQ_ERR_INVALID
+    cache = _FakeCache(cb)
+    cache.struct.v_codes += 4
+    assert _quantize_rc(cb, cache) == _lib.TQ_ERR_INVALID
+    cache = _FakeCache(cb, T_cap=100)
+    assert _quantize_rc(cb, cache) == _lib.TQ_ERR_INVALID
+
+
+def _attend_rc(cb, cache, Hq=4, max_seq=64, ws=None, ws_bytes=None):
+    n = ctypes.c_size_t(0 if ws_bytes is None else ws_bytes)
+    params = _lib.TQDevParams(1 << 15, 1 << 16, 1 << 17)
+    rc = _lib.lib.tq_attend_decode(ctypes.byref(cb.cb), ctypes.byref(params), ctypes.byref(cache.struct), 1 << 12,
+                                   _lib.TQ_DTYPE_F32, Hq, 1 << 13, max_seq, 0.0, 1 << 14, None, ws, ctypes.byref(n),
+                                   None)
+    return rc, n.value
+
+
+def test_attend_workspace_query_and_checks():
+    cb = tq.tq_build_codebook(2, 1, 3)
+    cache = _FakeCache(cb, B=2, Hkv=2, T_cap=4096)
+    rc, need = _attend_rc(cb, cache, Hq=8, max_seq=4096)
+    assert rc == _lib.TQ_OK and need > 0
+    rc, need2 = _attend_rc(cb, cache, Hq=8, max_seq=4096, ws=1 << 20, ws_bytes=need - 1)
+    assert rc == _lib.TQ_ERR_WORKSPACE and need2 == need
+    assert _attend_rc(cb, cache, Hq=7)[0] == _lib.TQ_ERR_INVALID          # not a multiple of Hkv
+    assert _attend_rc(cb, cache, Hq=2 * 3)[0] == _lib.TQ_ERR_UNSUPPORTED  # group of 3
+    assert _attend_rc(cb, cache, Hq=8, max_seq=0)[0] == _lib.TQ_ERR_INVALID
+    assert _attend_rc(cb, cache, Hq=8, max_seq=4097)[0] == _lib.TQ_ERR_INVALID
