@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the TurboQuant compressed-KV hot path on one MI355X.
+
+Workload: a Llama-3.1-8B-shaped decode layer (batch 1, 32 q-heads / 8 kv-heads, d = 128,
+context 32768, bf16 K/V ~ N(0,1) x per-channel LogNormal(0, 0.5) scales), stacked as 32
+layers with distinct caches so that the packed caches (32 x 28.3 MB at turbo3) do not
+fit the 256 MB Infinity Cache.  One step = for every layer: quantize-on-write of the new
+token's K and V (8 + 8 vectors) into the packed cache, then decode attention of the 32
+q-heads over the 32768-key context straight from the codes.  The step is captured once
+in a HIP graph and replayed.
+
+Prints one JSON line: keys/s (value), the roofline of the dominant kernel (the main
+decode-attention kernel: algorithmic bytes per launch over its average duration, timed
+with HIP events on its stream), and the oracle's rate on the host cores (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--preset", default="turbo3", choices=["turbo3", "turbo4"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall time spent timing the oracle on the host (0 disables)")
+    ap.add_argument("--kernel-reps", type=int, default=4, help="eager passes over the layers for kernel timing")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import kv_cache_vector_tq_amd as tq
+    import tq_workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.workload("c2_llama8b_layer_t32k")
+    B, Hkv, Hq, T, G = w.B, w.Hkv, w.Hq, w.T, w.G
+    L = args.layers
+    kb, kq, vb = wl.PRESETS[args.preset]
+
+    # ---- inputs (seeded, synthetic) -------------------------------------------------------------
+    log("drawing inputs", w.name)
+    K = torch.from_numpy(wl.host_tensor(w, wl.TENSOR_K)).to(dev).to(torch.bfloat16)
+    V = torch.from_numpy(wl.host_tensor(w, wl.TENSOR_V)).to(dev).to(torch.bfloat16)
+    Qh = wl.host_tensor(w, wl.TENSOR_Q)
+    Q = torch.from_numpy(Qh).to(dev).to(torch.bfloat16)
+
+    cb = tq.tq_build_codebook(kb, kq, vb, seed=0)
+    dp = tq.upload_params(cb, dev)
+    caches = [tq.KVCache(cb, B, Hkv, T, device=dev, zero=False) for _ in range(L)]
+    bytes_per_key = caches[0].bytes_per_token
+    zero = torch.zeros(B, dtype=torch.int32, device=dev)
+
+    # ---- prefill: bulk quantize of T-1 tokens into every layer (timed per launch) ---------------
+    qs, qe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qs.record()
+    qe.record()
+    torch.cuda.synchronize()
+    tq.tq_profile_events(quant=(qs, qe))
+    bulk_ms = []
+    Kp, Vp = K[:, :, : T - 1], V[:, :, : T - 1]
+    for l in range(L):
+        tq.tq_quantize_kv(cb, dp, caches[l], Kp, Vp, zero)
+        torch.cuda.synchronize()
+        bulk_ms.append(qs.elapsed_time(qe))
+    tq.tq_profile_events()
+    n_vec = 2 * B * Hkv * (T - 1)
+    k_out = 16 * kb + (16 if kq else 0) + 4 + (4 if (kq and kb) else 0)
+    v_out = 16 * vb + 4
+    bulk_bytes = B * Hkv * (T - 1) * (256 + k_out) + B * Hkv * (T - 1) * (256 + v_out)
+    bulk_s = float(np.median(bulk_ms[1:] if L > 1 else bulk_ms)) * 1e-3
+    log(f"bulk quantize: {n_vec} vectors in {bulk_s * 1e6:.1f} us")
+
+    # ---- one decode step over all layers ----------------------------------------------------------
+    k_new = [K[:, :, T - 1:T].contiguous() for _ in range(L)]
+    v_new = [V[:, :, T - 1:T].contiguous() for _ in range(L)]
+    qs_l = [Q.clone() for _ in range(L)]
+    outs = [torch.empty((B, Hq, 128), dtype=torch.float32, device=dev) for _ in range(L)]
+    start = torch.full((B,), T - 1, dtype=torch.int32, device=dev)
+    seq = torch.full((B,), T, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.attend_workspace_bytes(cb, dp, caches[0], Hq, T), dtype=torch.uint8, device=dev)
+
+    def step():
+        for l in range(L):
+            tq.tq_quantize_kv(cb, dp, caches[l], k_new[l], v_new[l], start)
+            tq.tq_attend_decode(cb, dp, caches[l], qs_l[l], seq, T, out=outs[l], workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / args.steps
+    keys_per_step = L * B * Hkv * T
+    value = keys_per_step / (step_ms * 1e-3)
+    log(f"step {step_ms:.3f} ms ({L} layers), wall {wall:.3f} s for {args.steps} steps")
+
+    # ---- dominant kernel: main attention kernel, HIP events on its stream ------------------------
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    a1.record()
+    torch.cuda.synchronize()
+    tq.tq_profile_events(attend=(a0, a1))
+    kern_ms = []
+    for _ in range(args.kernel_reps):
+        for l in range(L):
+            tq.tq_attend_decode(cb, dp, caches[l], qs_l[l], seq, T, out=outs[l], workspace=ws)
+            torch.cuda.synchronize()
+            kern_ms.append(a0.elapsed_time(a1))
+    tq.tq_profile_events()
+    kern_s = float(np.mean(kern_ms)) * 1e-3
+    bytes_per_launch = B * Hkv * T * bytes_per_key
+    achieved = bytes_per_launch / kern_s / 1e9
+    log(f"attention kernel: {kern_s * 1e6:.2f} us per launch, {achieved:.0f} GB/s")
+
+    # ---- oracle on the host cores ----------------------------------------------------------------
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, caches[0], Qh, args.preset, args.cpu_seconds)
+
+    line = {
+        "metric": "compressed-KV decode attention keys/s + achieved HBM GB/s (% of peak) at 3/4 bit",
+        "value": value,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "preset": args.preset, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": 128, "context": T, "layers": L, "bytes_per_key": bytes_per_key,
+                   "step": "per layer: quantize-on-write of 1 new token (K+V) then decode attention"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "attend_kernel (main decode attention)", "bytes_per_launch": bytes_per_launch,
+                     "avg_launch_us": kern_s * 1e6},
+        "cpu_baseline": cpu,
+        "extra": {
+            "step_gbs": keys_per_step * bytes_per_key / (step_ms * 1e-3) / 1e9,
+            "bulk_quantize": {"vectors_per_launch": n_vec, "us_per_launch": bulk_s * 1e6,
+                              "vectors_per_s": n_vec / bulk_s, "gbs": bulk_bytes / bulk_s / 1e9,
+                              "frac": bulk_bytes / bulk_s / 1e9 / HBM_PEAK_GBS},
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, cache, Qh, preset, seconds):
+    """The oracle (fp64 NumPy) decoding one (batch row, kv-head) of one layer from its packed cache:
+    unpack the codes, then attention of the G q-heads over the full context.  Repeated for
+    about `seconds`; reported as keys/s (keys attended per second)."""
+    import tq_workloads as wl
+    from oracle.pipeline import Oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    orc = Oracle(*wl.PRESETS[preset], seed=0)
+    T, G = w.T, w.G
+    host = {n: (None if t is None else t[0, 0].cpu().numpy()) for n, t in cache.tensors().items()}
+    q = Qh[0, :G].astype(np.float64)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        k = orc.unpack_keys(host["k_codes"], host["k_signs"], host["k_norm"], host["k_rnorm"], T)
+        v = orc.unpack_values(host["v_codes"], host["v_norm"], T)
+        orc.attend(q, k, v, T=T)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": reps * T / el, "unit": "keys/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} decode passes of one (batch row, kv-head) of one layer: unpack + attention of "
+                      f"{G} q-heads over {T} keys, fp64 NumPy ({el:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

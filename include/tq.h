@@ -184,6 +184,14 @@ int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_
                      int max_seq_len, float scale, float* out, float* scores_out,
                      void* workspace, size_t* workspace_bytes, void* hip_stream);
 
+/* Diagnostic timing hook (for benchmarks): events (hipEvent_t, created by the caller) that
+ * later calls on this thread record on their stream, attend_* immediately before and after
+ * the main attention kernel of tq_attend_decode (not its query prologue or merge) and
+ * quant_* before the first and after the last kernel of tq_quantize_kv.  NULL disables a
+ * pair.  The events are only recorded; the caller reads them after synchronizing.  Returns
+ * TQ_OK. */
+int tq_profile_events(void* attend_start, void* attend_stop, void* quant_start, void* quant_stop);
+
 /* Description of the last error on this thread ("" when none). */
 const char* tq_last_error(void);
 

@@ -20,12 +20,26 @@ PRESETS = {"turbo3": (2, 1, 3), "turbo4": (3, 1, 4), "qjl1": (0, 1, 3)}
 
 __all__ = [
     "PRESETS", "Codebook", "DeviceParams", "KVCache", "TQError", "tq_build_codebook", "tq_cache_layout",
-    "tq_quantize_kv", "tq_attend_decode", "tq_abi_version", "upload_params", "attend_workspace_bytes",
+    "tq_quantize_kv", "tq_attend_decode", "tq_abi_version", "tq_profile_events", "upload_params",
+    "attend_workspace_bytes",
 ]
 
 
 def tq_abi_version() -> int:
     return lib.tq_abi_version()
+
+
+def tq_profile_events(attend=None, quant=None):
+    """Timing hook: pairs of torch.cuda.Event (start, stop) recorded around the main attention
+    kernel and around the quantize kernels by later calls on this thread; None disables."""
+    def raw(pair):
+        if pair is None:
+            return None, None
+        return tuple(ctypes.c_void_p(e.cuda_event) for e in pair)
+
+    a0, a1 = raw(attend)
+    q0, q1 = raw(quant)
+    check(lib.tq_profile_events(a0, a1, q0, q1), "tq_profile_events")
 
 
 @dataclass

@@ -85,6 +85,8 @@ def _load():
     lib.tq_attend_decode.argtypes = [P(TQCodebook), P(TQDevParams), P(TQKVCache), vp, ctypes.c_int,
                                      ctypes.c_int, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp,
                                      P(ctypes.c_size_t), vp]
+    lib.tq_profile_events.restype = ctypes.c_int
+    lib.tq_profile_events.argtypes = [vp, vp, vp, vp]
     return lib
 
 

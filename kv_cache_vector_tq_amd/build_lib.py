@@ -1,6 +1,6 @@
 """Builds libtq.so (HIP kernels for gfx950 plus the host C++ of the C ABI) in this directory.
 
-Usage: python -m kv_cache_vector_tq_amd.build_lib   (or build() from Python).
+Usage: python kv_cache_vector_tq_amd/build_lib.py  (run by path: importing the package needs the built library).
 Each source is compiled on its own (in parallel) and then linked with hipcc.
 """
 from __future__ import annotations

@@ -612,7 +612,10 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
     ma.k_cent[l] = cb->k_centroids[l];
     ma.v_cent[l] = cb->v_centroids[l];
   }
+  const ProfileEvents& pe = profile_events();
+  if (pe.attend_start && pe.attend_stop) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(pe.attend_start), s);
   e = dispatch_main(ma, cb->cfg, G, n_slices, B, s);
+  if (pe.attend_start && pe.attend_stop) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(pe.attend_stop), s);
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("attention launch: ") + hipGetErrorString(e));
 
   MergeArgs mg{part, p->r_hi, p->r_lo, out, Hq, n_slices};

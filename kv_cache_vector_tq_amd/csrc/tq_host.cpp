@@ -27,6 +27,11 @@ int fail(int code, const std::string& msg) {
 
 void clear_error() { g_last_error.clear(); }
 
+ProfileEvents& profile_events() {
+  static thread_local ProfileEvents ev;
+  return ev;
+}
+
 int check_config(const tq_config& cfg) {
   if (cfg.d != TQ_HEAD_DIM) return fail(TQ_ERR_UNSUPPORTED, "only d = 128 is supported");
   if (cfg.k_bits < 0 || cfg.k_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "k_bits must be in 0..4");
@@ -197,6 +202,15 @@ double from_bf16(uint16_t b) {
 extern "C" {
 
 int tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+int tq_profile_events(void* attend_start, void* attend_stop, void* quant_start, void* quant_stop) {
+  tq::ProfileEvents& ev = tq::profile_events();
+  ev.attend_start = attend_start;
+  ev.attend_stop = attend_stop;
+  ev.quant_start = quant_start;
+  ev.quant_stop = quant_stop;
+  return TQ_OK;
+}
 
 const char* tq_last_error(void) { return tq::g_last_error.c_str(); }
 

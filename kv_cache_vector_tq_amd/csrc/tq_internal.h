@@ -24,4 +24,13 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 // Number of compute units of the current device (cached per device id).
 int device_cu_count();
 
+// Events of the timing hook (tq_profile_events), per thread; NULL when disabled.
+struct ProfileEvents {
+  void* attend_start = nullptr;
+  void* attend_stop = nullptr;
+  void* quant_start = nullptr;
+  void* quant_stop = nullptr;
+};
+ProfileEvents& profile_events();
+
 }  // namespace tq

@@ -440,6 +440,9 @@ extern "C" int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, con
   a.T_cap = cache->T_cap;
   a.r_hi = p->r_hi;
   a.r_lo = p->r_lo;
+  const ProfileEvents& pe = profile_events();
+  const bool prof = pe.quant_start && pe.quant_stop;
+  if (prof) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(pe.quant_start), s);
   if (k) {
     QuantArgs ak = a;
     ak.x = k;
@@ -467,5 +470,6 @@ extern "C" int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, con
     hipError_t e = dispatch_values(av, cb->cfg.v_bits, f32, B, s);
     if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("value quantize launch: ") + hipGetErrorString(e));
   }
+  if (prof) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(pe.quant_stop), s);
   return TQ_OK;
 }
