@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall time spent timing the oracle on the host (0 disables)")
     ap.add_argument("--kernel-reps", type=int, default=4, help="eager passes over the layers for kernel timing")
+    ap.add_argument("--workload", default="c2_llama8b_layer_t32k",
+                    help="workload name (default: the Llama-3.1-8B decode layer); others are for exploration")
     return ap.parse_args()
 
 
@@ -62,17 +64,26 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = wl.workload("c2_llama8b_layer_t32k")
+    w = wl.workload(args.workload)
     B, Hkv, Hq, T, G = w.B, w.Hkv, w.Hq, w.T, w.G
     L = args.layers
     kb, kq, vb = wl.PRESETS[args.preset]
 
     # ---- inputs (seeded, synthetic) -------------------------------------------------------------
     log("drawing inputs", w.name)
-    K = torch.from_numpy(wl.host_tensor(w, wl.TENSOR_K)).to(dev).to(torch.bfloat16)
-    V = torch.from_numpy(wl.host_tensor(w, wl.TENSOR_V)).to(dev).to(torch.bfloat16)
+    in_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    if B * Hkv * T <= (1 << 19):
+        K = torch.from_numpy(wl.host_tensor(w, wl.TENSOR_K)).to(dev).to(in_dtype)
+        V = torch.from_numpy(wl.host_tensor(w, wl.TENSOR_V)).to(dev).to(in_dtype)
+    else:  # large contexts are drawn on the device, one (b, kv-head) slice at a time
+        K = torch.empty((B, Hkv, T, 128), dtype=in_dtype, device=dev)
+        V = torch.empty((B, Hkv, T, 128), dtype=in_dtype, device=dev)
+        for bb in range(B):
+            for hh in range(Hkv):
+                wl.device_slice(w, bb, hh, wl.TENSOR_K, out=K[bb, hh])
+                wl.device_slice(w, bb, hh, wl.TENSOR_V, out=V[bb, hh])
     Qh = wl.host_tensor(w, wl.TENSOR_Q)
-    Q = torch.from_numpy(Qh).to(dev).to(torch.bfloat16)
+    Q = torch.from_numpy(Qh).to(dev).to(in_dtype)
 
     cb = tq.tq_build_codebook(kb, kq, vb, seed=0)
     dp = tq.upload_params(cb, dev)

@@ -21,8 +21,10 @@
 //     LDS and write one partial per (q-head, slice);
 //  3. merge: log-sum-exp over slices, then the unrotation R_eff^T (fp32).
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <mutex>
 #include <type_traits>
 #include <vector>
@@ -53,21 +55,24 @@ struct Tab {
 template <int B>
 __device__ void build_table(uint8_t* tab, const float* cent, int tid, int nthreads) {
   using T = Tab<B>;
+  typedef _Float16 entry_t __attribute__((ext_vector_type(T::CPL)));
   _Float16 c16[1 << B];
 #pragma unroll
   for (int l = 0; l < (1 << B); ++l) c16[l] = static_cast<_Float16>(cent[l]);
   for (int e = tid; e < T::ENTRIES; e += nthreads) {
-    _Float16* dst = reinterpret_cast<_Float16*>(tab + e * T::EBYTES);
+    entry_t v;
 #pragma unroll
-    for (int i = 0; i < T::CPL; ++i) dst[i] = c16[(e >> (B * i)) & ((1 << B) - 1)];
+    for (int i = 0; i < T::CPL; ++i) v[i] = c16[(e >> (B * i)) & ((1 << B) - 1)];
+    *reinterpret_cast<entry_t*>(tab + e * T::EBYTES) = v;
   }
 }
 
 __device__ void build_sign_table(uint8_t* tab, int tid, int nthreads) {
   for (int e = tid; e < 256; e += nthreads) {
-    _Float16* dst = reinterpret_cast<_Float16*>(tab + e * 16);
+    f16x8 v;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = ((e >> i) & 1) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
+    for (int i = 0; i < 8; ++i) v[i] = ((e >> i) & 1) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
+    *reinterpret_cast<f16x8*>(tab + e * 16) = v;
   }
 }
 
@@ -122,62 +127,182 @@ __device__ __forceinline__ void load_dwords(uint32_t* dst, const uint8_t* src) {
     *reinterpret_cast<u32x4*>(dst + 4 * i) = *reinterpret_cast<const u32x4*>(src + 16 * i);
 }
 
-// ---- prologue -----------------------------------------------------------------------------
+// ---- prologue ------------------------------------------------------------------------------
+// One workgroup per (batch row, kv-head) computes q1 = R_eff q and q2 = S_b q1 for the G
+// (<= 16) q-heads of the group as two 16x16x32 bf16 MFMA products: the q-heads are the M
+// rows, the wave's 32 output coordinates the N columns; operands are split into exact bf16
+// terms (fp32 q and q1 into three, R_eff into hi + lo), so products are exact and sums are
+// fp32.  Two extra workgroups write R_hi^T and R_lo^T into the workspace for the
+// unrotation at the end of the main kernel.
+constexpr int QS = 132;  // LDS row stride (floats) of q1
+
 struct PrologueArgs {
   const void* q;
   const uint16_t* r_hi;
   const uint16_t* r_lo;
   const uint16_t* s_b;  // may be NULL (no sketch)
   _Float16* qrec;       // [B*Hq][QREC]
+  uint16_t* rt_hi;      // [128][128] R_hi^T
+  uint16_t* rt_lo;      // [128][128] R_lo^T
+  int G, n_groups;
 };
 
-__device__ float block_absmax_128(float v, float* red) {
-  float m = fabsf(v);
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
+}
+
+// dst = src^T for a 128x128 bf16 matrix, through an LDS tile of row stride 136 (16-byte
+// aligned rows): 16-byte loads and stores, 8 per thread, all issued before any use.
+__device__ void transpose_matrix(uint16_t* dst, const uint16_t* src, uint16_t* tile) {
+  constexpr int TS = 136;
+  u16x8 v[8];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  for (int r = 0; r < 8; ++r) v[r] = *reinterpret_cast<const u16x8*>(src + 8 * (threadIdx.x + 256 * r));
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int idx8 = threadIdx.x + 256 * r;
+    const int i = (8 * idx8) / D, k0 = (8 * idx8) % D;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[(k0 + e) * TS + i] = v[r][e];
+  }
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  return fmaxf(red[0], red[1]);
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int idx8 = threadIdx.x + 256 * r;
+    const int k = (8 * idx8) / D, i0 = (8 * idx8) % D;
+    *reinterpret_cast<u16x8*>(dst + 8 * idx8) = *reinterpret_cast<const u16x8*>(tile + k * TS + i0);
+  }
 }
 
 template <bool F32>
-__global__ void __launch_bounds__(128) prologue_kernel(PrologueArgs a) {
-  __shared__ float qs[D];
-  __shared__ float q1s[D];
-  __shared__ float red[2];
-  const int j = threadIdx.x;
-  const int64_t head = blockIdx.x;
-  float qv;
-  if constexpr (F32) {
-    qv = reinterpret_cast<const float*>(a.q)[head * D + j];
-  } else {
-    qv = bf2f(reinterpret_cast<const uint16_t*>(a.q)[head * D + j]);
+__global__ void __launch_bounds__(256) prologue_kernel(PrologueArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float psm[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, g = lane >> 4;
+  if (blockIdx.x >= a.n_groups) {  // two extra workgroups write R_hi^T and R_lo^T
+    uint16_t* tile = reinterpret_cast<uint16_t*>(psm);
+    if (blockIdx.x == a.n_groups)
+      transpose_matrix(a.rt_hi, a.r_hi, tile);
+    else
+      transpose_matrix(a.rt_lo, a.r_lo, tile);
+    return;
   }
-  qs[j] = qv;
-  __syncthreads();
-  float q1 = 0.f;
-  for (int k = 0; k < D; ++k) {
-    q1 = fmaf(bf2f(a.r_hi[j * D + k]), qs[k], q1);
-    q1 = fmaf(bf2f(a.r_lo[j * D + k]), qs[k], q1);
+  float* q1s = psm;  // [16][QS]
+  __shared__ unsigned int mx[2][16];
+  const int G = a.G;
+  const bool sketch = a.s_b != nullptr;
+  const int64_t head0 = (int64_t)blockIdx.x * G;
+
+  // operands of this wave's output rows o = 32 wave + 16 nt + col
+  bf16x8 rh[2][4], rl[2][4], sb[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int o = 32 * wave + 16 * nt + col;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      rh[nt][kb] = load_bf16x8(a.r_hi + o * D + 32 * g + 8 * kb);
+      rl[nt][kb] = load_bf16x8(a.r_lo + o * D + 32 * g + 8 * kb);
+      sb[nt][kb] = sketch ? load_bf16x8(a.s_b + o * D + 32 * g + 8 * kb) : bf16x8{};
+    }
   }
-  q1s[j] = q1;
+  if (tid < 32) mx[tid >> 4][tid & 15] = 0u;
+  // A operand: q-head h = col (rows >= G are zero)
+  const int hA = col;
+  f32x4 d1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (hA < G) {
+      if constexpr (F32) {
+        const float* src = reinterpret_cast<const float*>(a.q) + (head0 + hA) * D + 32 * g + 8 * kb;
+        *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
+        *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
+      } else {
+        const u16x8 x = *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(a.q) + (head0 + hA) * D +
+                                                        32 * g + 8 * kb);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = bf2f(x[e]);
+      }
+    }
+    bf16x8 ph, pm, pl;
+    split3_bf16(v, ph, pm, pl);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      d1[nt] = mfma_bf16(ph, rh[nt][kb], d1[nt]);
+      d1[nt] = mfma_bf16(ph, rl[nt][kb], d1[nt]);
+      d1[nt] = mfma_bf16(pm, rh[nt][kb], d1[nt]);
+      d1[nt] = mfma_bf16(pm, rl[nt][kb], d1[nt]);
+      if constexpr (F32) {
+        d1[nt] = mfma_bf16(pl, rh[nt][kb], d1[nt]);
+        d1[nt] = mfma_bf16(pl, rl[nt][kb], d1[nt]);
+      }
+    }
+  }
+  __syncthreads();  // mx cleared
+  // D layout: lane (col, g) holds q-head 4 g + i, output coordinate 32 wave + 16 nt + col
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float m = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      q1s[(4 * g + i) * QS + 32 * wave + 16 * nt + col] = d1[nt][i];
+      m = fmaxf(m, fabsf(d1[nt][i]));
+    }
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    m = fmaxf(m, __shfl_xor(m, 8));
+    if (col == 0) atomicMax(&mx[0][4 * g + i], __float_as_uint(m));
+  }
   __syncthreads();
-  float q2 = 0.f;
-  if (a.s_b != nullptr)
-    for (int k = 0; k < D; ++k) q2 = fmaf(bf2f(a.s_b[j * D + k]), q1s[k], q2);
-  const float m1 = block_absmax_128(q1, red);
-  const float m2 = block_absmax_128(q2, red);
-  int e1 = 0, e2 = 0;
-  if (m1 > 0.f) frexpf(m1, &e1);
-  if (m2 > 0.f) frexpf(m2, &e2);
-  _Float16* rec = a.qrec + head * QREC;
-  rec[j] = static_cast<_Float16>(ldexpf(q1, -e1));
-  rec[D + j] = static_cast<_Float16>(ldexpf(q2, -e2));
-  if (j == 0) {
-    float* sc = reinterpret_cast<float*>(rec + 2 * D);
-    sc[0] = ldexpf(1.0f, e1);
-    sc[1] = ldexpf(1.0f, e2);
+  f32x4 d2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (sketch) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float v[8];
+      const float* src = q1s + hA * QS + 32 * g + 8 * kb;
+      *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
+      *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
+      bf16x8 ph, pm, pl;
+      split3_bf16(v, ph, pm, pl);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        d2[nt] = mfma_bf16(ph, sb[nt][kb], d2[nt]);
+        d2[nt] = mfma_bf16(pm, sb[nt][kb], d2[nt]);
+        d2[nt] = mfma_bf16(pl, sb[nt][kb], d2[nt]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = fmaxf(fabsf(d2[0][i]), fabsf(d2[1][i]));
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      m = fmaxf(m, __shfl_xor(m, 8));
+      if (col == 0) atomicMax(&mx[1][4 * g + i], __float_as_uint(m));
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    if (h >= G) continue;
+    const float m1 = __uint_as_float(mx[0][h]), m2 = __uint_as_float(mx[1][h]);
+    int e1 = 0, e2 = 0;
+    if (m1 > 0.f) frexpf(m1, &e1);
+    if (m2 > 0.f) frexpf(m2, &e2);
+    _Float16* rec = a.qrec + (head0 + h) * QREC;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int o = 32 * wave + 16 * nt + col;
+      rec[o] = static_cast<_Float16>(ldexpf(d1[nt][i], -e1));
+      rec[D + o] = static_cast<_Float16>(ldexpf(d2[nt][i], -e2));
+    }
+    if (wave == 0 && col == 0) {
+      float* sc = reinterpret_cast<float*>(rec + 2 * D);
+      sc[0] = ldexpf(1.0f, e1);
+      sc[1] = ldexpf(1.0f, e2);
+    }
   }
 }
 
@@ -191,7 +316,9 @@ struct MainArgs {
   const float* v_norm;
   const int32_t* seq_len;
   const _Float16* qrec;
-  float* part;        // [B*Hq][n_slices][PREC]
+  const uint16_t* rt_hi;  // R_hi^T, R_lo^T (written by the prologue)
+  const uint16_t* rt_lo;
+  float* part;        // [B*Hq][n_slices][PREC]: unrotated sums, m, l, mv
   float* scores_out;  // NULL or [B*Hq][T_cap]
   int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices;
   float scale_log2;   // scale * log2(e)
@@ -208,7 +335,8 @@ struct MainCfg {
   static constexpr int STAB = QJL ? 4096 : 0;
   static constexpr int VTAB = Tab<VB>::BYTES;
   static constexpr int TABLES = KTAB + STAB + VTAB;
-  static constexpr int MERGE = 4 * 16 * PREC * 4;  // per wave, per column: acc + state
+  // per wave and column: acc + state; then the merged rotated sums [16][QS] and states
+  static constexpr int MERGE = 4 * 16 * PREC * 4 + 16 * QS * 4 + 16 * 4 * 4;
   static constexpr int LDS = TABLES > MERGE ? TABLES : MERGE;
 };
 
@@ -260,22 +388,37 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
 
   __syncthreads();  // tables ready
 
-  for (int blk = blk_begin; blk < blk_end; ++blk) {
-    // ---- loads ----------------------------------------------------------------------------
+  // Block data of one lane; the next block is loaded while the current one is processed.
+  struct Blk {
     uint32_t kd[KB > 0 ? 4 * KB : 1];
     uint32_t sd[4];
     uint32_t vd[4 * VB];
-    if constexpr (KB > 0) load_dwords<4 * KB>(kd, a.k_codes + (bh * nblk_cap + blk) * (1024 * KB) + lane * 16 * KB);
-    if constexpr (QJL) load_dwords<4>(sd, a.k_signs + (bh * nblk_cap + blk) * 1024 + lane * 16);
-    load_dwords<4 * VB>(vd, a.v_codes + (bh * nblk_cap + blk) * (1024 * VB) + lane * 16 * VB);
     f32x4 kn[NSETS], kr[NSETS], vn[NSETS];
+  };
+  auto load_block = [&](int blk, Blk& d) {
+    if constexpr (KB > 0)
+      load_dwords<4 * KB>(d.kd, a.k_codes + (bh * nblk_cap + blk) * (1024 * KB) + lane * 16 * KB);
+    if constexpr (QJL) load_dwords<4>(d.sd, a.k_signs + (bh * nblk_cap + blk) * 1024 + lane * 16);
+    load_dwords<4 * VB>(d.vd, a.v_codes + (bh * nblk_cap + blk) * (1024 * VB) + lane * 16 * VB);
 #pragma unroll
     for (int s = 0; s < NSETS; ++s) {
       const int64_t tok = bh * a.T_cap + blk * 64 + 16 * (s * TPD + tcls) + 4 * g;
-      kn[s] = *reinterpret_cast<const f32x4*>(a.k_norm + tok);
-      if constexpr (QJL && KB > 0) kr[s] = *reinterpret_cast<const f32x4*>(a.k_rnorm + tok);
-      vn[s] = *reinterpret_cast<const f32x4*>(a.v_norm + tok);
+      d.kn[s] = *reinterpret_cast<const f32x4*>(a.k_norm + tok);
+      if constexpr (QJL && KB > 0) d.kr[s] = *reinterpret_cast<const f32x4*>(a.k_rnorm + tok);
+      d.vn[s] = *reinterpret_cast<const f32x4*>(a.v_norm + tok);
     }
+  };
+  Blk cur, nxt;
+  if (blk_begin < blk_end) load_block(blk_begin, cur);
+
+  for (int blk = blk_begin; blk < blk_end; ++blk) {
+    if (blk + 1 < blk_end) load_block(blk + 1, nxt);
+    const uint32_t* kd = cur.kd;
+    const uint32_t* sd = cur.sd;
+    const uint32_t* vd = cur.vd;
+    const f32x4* kn = cur.kn;
+    const f32x4* kr = cur.kr;
+    const f32x4* vn = cur.vn;
 
     // ---- score MFMAs: tile t = keys 16 t .. 16 t + 15 of the block ------------------------
     f32x4 dc[4], ds[4];
@@ -369,13 +512,27 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
         acc[mt] = mfma_f16(av, bp, acc[mt]);
       });
     });
+    cur = nxt;
   }
 
-  // ---- merge the 4 waves and the TPD column classes of each q-head in LDS ---------------------
+  // ---- merge the 4 waves and the TPD column classes of each q-head in LDS, then unrotate ----
   const float l_col = l_run + __shfl_xor(l_run, 16);
   const float l_tot = l_col + __shfl_xor(l_col, 32);
+  // R_eff^T operands for this wave's output coordinates k = 32 wave + 16 nt + col
+  bf16x8 th[2][4], tl[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int k = 32 * wave + 16 * nt + col;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      th[nt][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_hi + k * D + 32 * g + 8 * kb));
+      tl[nt][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_lo + k * D + 32 * g + 8 * kb));
+    }
+  }
   __syncthreads();  // tables dead
   float* mrg = reinterpret_cast<float*>(smem);
+  float* amat = mrg + 4 * 16 * PREC;  // [16][QS] merged rotated sums (rows >= G zero)
+  float* st = amat + 16 * QS;         // [16][4] m, l, mv
   float* rec = mrg + (wave * 16 + col) * PREC;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
@@ -387,8 +544,12 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
     rec[130] = mv_run;
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D; idx += 256) {
+  for (int idx = tid; idx < 16 * D; idx += 256) {
     const int h = idx / D, j = idx % D;
+    if (h >= G) {
+      amat[h * QS + j] = 0.f;
+      continue;
+    }
     float M = NEG_BIG, MV = NEG_BIG;
     for (int w = 0; w < 4; ++w)
       for (int c = 0; c < TPD; ++c) {
@@ -403,55 +564,110 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
         Ls += r[129] * exp2f(r[128] - M);
         A += r[j] * exp2f(r[130] - MV);
       }
-    float* out = a.part + (((int64_t)b * Hq + kvh * G + h) * a.n_slices + blockIdx.x) * PREC;
-    out[j] = A;
+    amat[h * QS + j] = A;
     if (j == 0) {
-      out[128] = M;
-      out[129] = Ls;
-      out[130] = MV;
+      st[4 * h + 0] = M;
+      st[4 * h + 1] = Ls;
+      st[4 * h + 2] = MV;
     }
+  }
+  __syncthreads();
+  // U[h][k] = sum_j A[h][j] R_eff[j][k]: rows = q-heads, columns = this wave's k
+  f32x4 u[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    float v[8];
+    const float* src = amat + col * QS + 32 * g + 8 * kb;
+    *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
+    *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
+    bf16x8 ph, pm, pl;
+    split3_bf16(v, ph, pm, pl);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      u[nt] = mfma_bf16(ph, th[nt][kb], u[nt]);
+      u[nt] = mfma_bf16(ph, tl[nt][kb], u[nt]);
+      u[nt] = mfma_bf16(pm, th[nt][kb], u[nt]);
+      u[nt] = mfma_bf16(pm, tl[nt][kb], u[nt]);
+      u[nt] = mfma_bf16(pl, th[nt][kb], u[nt]);
+      u[nt] = mfma_bf16(pl, tl[nt][kb], u[nt]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    if (h >= G) continue;
+    float* out = a.part + (((int64_t)b * Hq + kvh * G + h) * a.n_slices + blockIdx.x) * PREC;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) out[32 * wave + 16 * nt + col] = u[nt][i];
+  }
+  if (tid < G) {
+    float* out = a.part + (((int64_t)b * Hq + kvh * G + tid) * a.n_slices + blockIdx.x) * PREC;
+    out[128] = st[4 * tid + 0];
+    out[129] = st[4 * tid + 1];
+    out[130] = st[4 * tid + 2];
   }
 }
 
-// ---- merge over slices and unrotation ---------------------------------------------------------
+// ---- merge over slices ---------------------------------------------------------------------------
+// One workgroup per (batch row, q-head): log-sum-exp weights of the slices, then the
+// weighted sum of their (already unrotated) value sums.
+constexpr int MAX_SLICES = 1024;
+
 struct MergeArgs {
   const float* part;
-  const uint16_t* r_hi;
-  const uint16_t* r_lo;
   float* out;
-  int Hq, n_slices;
+  int n_slices;
 };
 
-__global__ void __launch_bounds__(128) merge_kernel(MergeArgs a) {
-  __shared__ float os[D];
-  const int j = threadIdx.x;
-  const int64_t head = (int64_t)blockIdx.y * a.Hq + blockIdx.x;
-  const float* base = a.part + head * a.n_slices * PREC;
-  float M = NEG_BIG, MV = NEG_BIG;
-  for (int s = 0; s < a.n_slices; ++s) {
-    M = fmaxf(M, base[s * PREC + 128]);
-    MV = fmaxf(MV, base[s * PREC + 130]);
+__device__ float block_reduce(float v, float* red, bool is_max) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float w = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, w) : v + w;
   }
-  float L = 0.f, A = 0.f;
-  for (int s = 0; s < a.n_slices; ++s) {
-    const float* r = base + s * PREC;
-    L += r[129] * exp2f(r[128] - M);
-    A += r[j] * exp2f(r[130] - MV);
-  }
-  // value centroids enter as c / sqrt(d)
-  os[j] = L > 0.f ? (A / L) * exp2f(MV - M) * INV_SQRT_D : 0.f;
   __syncthreads();
-  // out = R_eff^T o_rot: out_k = sum_i R_eff[i][k] o_rot_i
-  float o = 0.f;
-  for (int i = 0; i < D; ++i) {
-    o = fmaf(bf2f(a.r_hi[i * D + j]), os[i], o);
-    o = fmaf(bf2f(a.r_lo[i * D + j]), os[i], o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
+  return r;
+}
+
+__global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
+  __shared__ float wa[MAX_SLICES];
+  __shared__ float red[4];
+  __shared__ float half_sum[D];
+  const int tid = threadIdx.x;
+  const int64_t head = blockIdx.x;
+  const float* base = a.part + head * a.n_slices * PREC;
+  float m = NEG_BIG, mv = NEG_BIG;
+  for (int s = tid; s < a.n_slices; s += 256) {
+    m = fmaxf(m, base[s * PREC + 128]);
+    mv = fmaxf(mv, base[s * PREC + 130]);
   }
-  a.out[head * D + j] = o;
+  const float M = block_reduce(m, red, true);
+  const float MV = block_reduce(mv, red, true);
+  float l = 0.f;
+  for (int s = tid; s < a.n_slices; s += 256) {
+    l += base[s * PREC + 129] * exp2f(base[s * PREC + 128] - M);
+    wa[s] = exp2f(base[s * PREC + 130] - MV);
+  }
+  const float L = block_reduce(l, red, false);  // also orders the wa writes before the reads
+  const int k = tid & (D - 1), hf = tid >> 7;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int s = hf; s < a.n_slices; s += 2) acc = fmaf(wa[s], base[s * PREC + k], acc);
+  if (hf == 1) half_sum[k] = acc;
+  __syncthreads();
+  if (hf == 0) {
+    acc += half_sum[k];
+    // value centroids enter as c / sqrt(d)
+    a.out[head * D + k] = L > 0.f ? acc / L * exp2f(MV - M) * INV_SQRT_D : 0.f;
+  }
 }
 
 template <int KB, bool QJL, int VB, int G>
-hipError_t launch_main(const MainArgs& a, int n_slices, int B, hipStream_t s) {
+hipError_t launch_main(const MainArgs& a, int n_slices, int B, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   using C = MainCfg<KB, QJL, VB, G>;
   auto kern = attend_kernel<KB, QJL, VB, G>;
   if (C::LDS > 65536) {
@@ -460,26 +676,30 @@ hipError_t launch_main(const MainArgs& a, int n_slices, int B, hipStream_t s) {
       (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     });
   }
-  hipLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(256), C::LDS, s, a);
+  if (e0 != nullptr || e1 != nullptr)
+    hipExtLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(256), C::LDS, s, e0, e1, 0, a);
+  else
+    hipLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(256), C::LDS, s, a);
   return hipGetLastError();
 }
 
 template <int KB, bool QJL, int VB>
-hipError_t dispatch_g(const MainArgs& a, int G, int n_slices, int B, hipStream_t s) {
+hipError_t dispatch_g(const MainArgs& a, int G, int n_slices, int B, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (G) {
-    case 4: return launch_main<KB, QJL, VB, 4>(a, n_slices, B, s);
-    case 8: return launch_main<KB, QJL, VB, 8>(a, n_slices, B, s);
-    case 16: return launch_main<KB, QJL, VB, 16>(a, n_slices, B, s);
+    case 4: return launch_main<KB, QJL, VB, 4>(a, n_slices, B, s, e0, e1);
+    case 8: return launch_main<KB, QJL, VB, 8>(a, n_slices, B, s, e0, e1);
+    case 16: return launch_main<KB, QJL, VB, 16>(a, n_slices, B, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
 template <int KB, bool QJL>
-hipError_t dispatch_v(const MainArgs& a, int VB, int G, int n_slices, int B, hipStream_t s) {
+hipError_t dispatch_v(const MainArgs& a, int VB, int G, int n_slices, int B, hipStream_t s, hipEvent_t e0,
+                      hipEvent_t e1) {
   switch (VB) {
-    case 2: return dispatch_g<KB, QJL, 2>(a, G, n_slices, B, s);
-    case 3: return dispatch_g<KB, QJL, 3>(a, G, n_slices, B, s);
-    case 4: return dispatch_g<KB, QJL, 4>(a, G, n_slices, B, s);
+    case 2: return dispatch_g<KB, QJL, 2>(a, G, n_slices, B, s, e0, e1);
+    case 3: return dispatch_g<KB, QJL, 3>(a, G, n_slices, B, s, e0, e1);
+    case 4: return dispatch_g<KB, QJL, 4>(a, G, n_slices, B, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }
@@ -490,23 +710,32 @@ bool supported(const tq_config& c, int G) {
   return keys && c.v_bits >= 2 && c.v_bits <= 4 && (G == 4 || G == 8 || G == 16);
 }
 
-hipError_t dispatch_main(const MainArgs& a, const tq_config& c, int G, int n_slices, int B, hipStream_t s) {
+hipError_t dispatch_main(const MainArgs& a, const tq_config& c, int G, int n_slices, int B, hipStream_t s,
+                         hipEvent_t e0, hipEvent_t e1) {
   if (c.k_qjl) {
     switch (c.k_bits) {
-      case 0: return dispatch_v<0, true>(a, c.v_bits, G, n_slices, B, s);
-      case 2: return dispatch_v<2, true>(a, c.v_bits, G, n_slices, B, s);
-      case 3: return dispatch_v<3, true>(a, c.v_bits, G, n_slices, B, s);
+      case 0: return dispatch_v<0, true>(a, c.v_bits, G, n_slices, B, s, e0, e1);
+      case 2: return dispatch_v<2, true>(a, c.v_bits, G, n_slices, B, s, e0, e1);
+      case 3: return dispatch_v<3, true>(a, c.v_bits, G, n_slices, B, s, e0, e1);
     }
   } else {
     switch (c.k_bits) {
-      case 2: return dispatch_v<2, false>(a, c.v_bits, G, n_slices, B, s);
-      case 3: return dispatch_v<3, false>(a, c.v_bits, G, n_slices, B, s);
+      case 2: return dispatch_v<2, false>(a, c.v_bits, G, n_slices, B, s, e0, e1);
+      case 3: return dispatch_v<3, false>(a, c.v_bits, G, n_slices, B, s, e0, e1);
     }
   }
   return hipErrorInvalidValue;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Integer tuning knob from the environment, clamped to [lo, hi]; dflt when unset.
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* v = getenv(name);
+  if (v == nullptr || *v == 0) return dflt;
+  const long x = strtol(v, nullptr, 10);
+  return static_cast<int>(x < lo ? lo : (x > hi ? hi : x));
+}
 
 }  // namespace
 
@@ -556,17 +785,20 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   const int B = cache->B;
   const int nblk_max = (max_seq_len + 63) / 64;
   const int units = B * cache->Hkv;
-  const int target_wg = 2 * device_cu_count();
-  constexpr int MIN_BLOCKS_PER_WAVE = 4;
+  static const int wg_per_cu = env_int("TQ_ATTN_WG_PER_CU", 2, 1, 64);
+  static const int MIN_BLOCKS_PER_WAVE = env_int("TQ_ATTN_MIN_BLOCKS", 2, 1, 1 << 20);
+  const int target_wg = wg_per_cu * device_cu_count();
   int n_slices = (target_wg + units - 1) / units;
   const int max_slices = std::max(1, (nblk_max + 4 * MIN_BLOCKS_PER_WAVE - 1) / (4 * MIN_BLOCKS_PER_WAVE));
   n_slices = std::max(1, std::min(n_slices, max_slices));
   const int bpw = (nblk_max + 4 * n_slices - 1) / (4 * n_slices);
   n_slices = (nblk_max + 4 * bpw - 1) / (4 * bpw);
+  if (n_slices > MAX_SLICES) return fail(TQ_ERR_UNSUPPORTED, "context split exceeds the merge limit");
 
   const size_t qrec_bytes = align256(static_cast<size_t>(B) * Hq * QREC * sizeof(_Float16));
+  const size_t rt_bytes = 2 * D * D * sizeof(uint16_t);
   const size_t part_bytes = align256(static_cast<size_t>(B) * Hq * n_slices * PREC * sizeof(float));
-  const size_t need = qrec_bytes + part_bytes;
+  const size_t need = qrec_bytes + rt_bytes + part_bytes;
   if (workspace == nullptr) {
     *workspace_bytes = need;
     return TQ_OK;
@@ -579,14 +811,17 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
 
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   _Float16* qrec = reinterpret_cast<_Float16*>(workspace);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + qrec_bytes);
+  uint16_t* rt = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(workspace) + qrec_bytes);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + qrec_bytes + rt_bytes);
   if (scale == 0.f) scale = INV_SQRT_D;
 
-  PrologueArgs pa{q, p->r_hi, p->r_lo, cb->cfg.k_qjl ? p->s_qjl : nullptr, qrec};
+  const int n_groups = B * cache->Hkv;
+  PrologueArgs pa{q, p->r_hi, p->r_lo, cb->cfg.k_qjl ? p->s_qjl : nullptr, qrec, rt, rt + D * D, G, n_groups};
+  const size_t plds = std::max<size_t>(16 * QS * sizeof(float), D * 136 * sizeof(uint16_t));
   if (q_dtype == TQ_DTYPE_F32)
-    hipLaunchKernelGGL(prologue_kernel<true>, dim3(B * Hq), dim3(128), 0, s, pa);
+    hipLaunchKernelGGL(prologue_kernel<true>, dim3(n_groups + 2), dim3(256), plds, s, pa);
   else
-    hipLaunchKernelGGL(prologue_kernel<false>, dim3(B * Hq), dim3(128), 0, s, pa);
+    hipLaunchKernelGGL(prologue_kernel<false>, dim3(n_groups + 2), dim3(256), plds, s, pa);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("prologue launch: ") + hipGetErrorString(e));
 
@@ -599,6 +834,8 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   ma.v_norm = cache->v_norm;
   ma.seq_len = seq_len;
   ma.qrec = qrec;
+  ma.rt_hi = rt;
+  ma.rt_lo = rt + D * D;
   ma.part = part;
   ma.scores_out = scores_out;
   ma.Hkv = cache->Hkv;
@@ -613,13 +850,16 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
     ma.v_cent[l] = cb->v_centroids[l];
   }
   const ProfileEvents& pe = profile_events();
-  if (pe.attend_start && pe.attend_stop) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(pe.attend_start), s);
-  e = dispatch_main(ma, cb->cfg, G, n_slices, B, s);
-  if (pe.attend_start && pe.attend_stop) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(pe.attend_stop), s);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (pe.attend_start && pe.attend_stop) {
+    e0 = reinterpret_cast<hipEvent_t>(pe.attend_start);
+    e1 = reinterpret_cast<hipEvent_t>(pe.attend_stop);
+  }
+  e = dispatch_main(ma, cb->cfg, G, n_slices, B, s, e0, e1);
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("attention launch: ") + hipGetErrorString(e));
 
-  MergeArgs mg{part, p->r_hi, p->r_lo, out, Hq, n_slices};
-  hipLaunchKernelGGL(merge_kernel, dim3(Hq, B), dim3(128), 0, s, mg);
+  MergeArgs mg{part, out, n_slices};
+  hipLaunchKernelGGL(merge_kernel, dim3(B * Hq), dim3(256), 0, s, mg);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("merge launch: ") + hipGetErrorString(e));
   return TQ_OK;

@@ -8,9 +8,12 @@
 //   keys with the sketch: r = y - c[code]/sqrt(d) (r = y without codes), rnorm = ||r||,
 //   sign_j = [(S_b r)_j >= 0].
 //
-// One workgroup (4 waves) owns one 64-token block of one (batch row, kv-head), so it is
-// the only writer of that block.  Wave w computes output coordinates 32w..32w+31 of all
-// 64 tokens with 16x16x32 bf16 MFMAs:
+// Work is split in tiles: one tile is the part of one 64-token block of one (batch row,
+// kv-head, tensor) that the call writes, so each block has a single writer.  Keys and
+// values go through one launch; persistent workgroups (4 waves) keep the rotation and
+// sketch operands in registers and walk the tiles.  Wave w computes output coordinates
+// 32w..32w+31 of the tile's tokens with 16x16x32 bf16 MFMAs (16-token sub-tiles that hold
+// no token of the call are skipped):
 //   * rotation: bf16 inputs are exact, R_eff = R_hi + R_lo takes two passes (fp32 inputs
 //     are split into three exact bf16 terms first), all products exact, fp32 accumulation;
 //   * sketch: r (fp32) is split into three exact bf16 terms, S_b is bf16, so u = S_b r is
@@ -18,6 +21,9 @@
 // The k dimension of every MFMA maps lane group g, element e of k-block kb to coordinate
 // 32 g + 8 kb + e on both operands, so the sum runs over all 128 coordinates.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+
+#include <algorithm>
 
 #include "tq_common.h"
 #include "tq_internal.h"
@@ -64,28 +70,41 @@ __device__ __forceinline__ void pack32(const uint8_t* c, uint32_t* w) {
   }
 }
 
+struct Smem {
+  float tile[64 * XS_F32];  // input tile, later residuals
+  uint8_t idx[64 * IDX_STRIDE];
+  uint8_t sgn[64 * IDX_STRIDE];
+  float norm[64];
+  float rnorm[64];
+};
+
+// Rotation (hi, lo) and sketch operands of one wave: lane (col, grp) holds row
+// 32 wave + 16 nt + col, columns 32 grp + 8 kb .. + 7.
+struct Operands {
+  bf16x8 rh[2][4], rl[2][4], sb[2][4];
+};
+
+// Quantizes the tokens of block blk of (b, h) that fall in [lo_slot, hi_slot).
 // KEY: key layout (and sketch when QJL); otherwise value layout.  BITS = 0 only for keys
 // that keep only the sketch.  F32: input elements are fp32 (else bf16).
 template <bool KEY, int BITS, bool QJL, bool F32>
-__global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a) {
+__device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, const Operands& op, int b, int h,
+                                              int start, int blk, int lo_slot, int hi_slot) {
   constexpr int L = 1 << (BITS > 0 ? BITS : 1);
-  __shared__ __attribute__((aligned(16))) float s_tile[64 * XS_F32];  // input tile, later residuals
-  __shared__ __attribute__((aligned(16))) uint8_t s_idx[64 * IDX_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint8_t s_sgn[64 * IDX_STRIDE];
-  __shared__ float s_norm[64];
-  __shared__ float s_rnorm[64];
-
+  float* s_tile = sm.tile;
+  uint8_t* s_idx = sm.idx;
+  uint8_t* s_sgn = sm.sgn;
+  float* s_norm = sm.norm;
+  float* s_rnorm = sm.rnorm;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int start = a.start_pos[b];
-  if (start < 0) return;
-  const int end = min(start + a.n_new, a.T_cap);  // one past the last slot written
-  const int blk = start / 64 + blockIdx.x;
   const int p0 = blk * 64;
-  if (p0 >= end) return;  // uniform over the workgroup
-  const int lo_slot = max(start, p0), hi_slot = min(end, p0 + 64);
+  // 16-token sub-tiles holding at least one token of the call
+  const int r0 = lo_slot - p0, r1 = hi_slot - p0;
+  bool mt_on[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) mt_on[mt] = (16 * mt < r1) && (16 * mt + 16 > r0);
 
   // ---- load the tile, row norms ----------------------------------------------------------
   // The norm is taken after an exact power-of-two rescaling by the row's largest magnitude,
@@ -149,18 +168,11 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   {
-    bf16x8 rh[2][4], rl[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int o = 32 * wave + 16 * nt + col;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        rh[nt][kb] = load_bf16x8(a.r_hi + o * D + 32 * grp + 8 * kb);
-        rl[nt][kb] = load_bf16x8(a.r_lo + o * D + 32 * grp + 8 * kb);
-      }
-    }
+    const auto& rh = op.rh;
+    const auto& rl = op.rl;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
+      if (!mt_on[mt]) continue;
       const int row = 16 * mt + col;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
@@ -242,15 +254,10 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a) {
       if (q == 0) s_rnorm[row] = s_norm[row] > 0.f ? sqrtf(ss) : 0.f;
     }
     // ---- sketch: u = S_b r, signs -----------------------------------------------------------
-    bf16x8 sb[2][4];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int o = 32 * wave + 16 * nt + col;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) sb[nt][kb] = load_bf16x8(a.s_b + o * D + 32 * grp + 8 * kb);
-    }
+    const auto& sb = op.sb;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
+      if (!mt_on[mt]) continue;
       f32x4 u[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       const int row = 16 * mt + col;
 #pragma unroll
@@ -358,42 +365,92 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs a) {
   }
 }
 
-template <bool KEY, int BITS, bool QJL>
-hipError_t launch_quantize(const QuantArgs& a, bool f32, int B, hipStream_t s) {
-  const dim3 grid((a.n_new + 63) / 64 + 1, a.Hkv, B);
-  if (f32)
-    hipLaunchKernelGGL((quantize_kernel<KEY, BITS, QJL, true>), grid, dim3(256), 0, s, a);
+struct QuantLaunch {
+  QuantArgs k, v;
+  int has_k, has_v;
+  int Hkv, nblk_max, n_tiles;
+};
+
+// Persistent workgroups walk tiles t = ((b * Hkv + h) * nblk_max + i) * 2 + tensor.
+template <int KB, bool QJL, int VB, bool F32>
+__global__ void __launch_bounds__(256) quantize_kernel(QuantLaunch q) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  Operands op;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int o = 32 * wave + 16 * nt + col;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      op.rh[nt][kb] = load_bf16x8(q.k.r_hi + o * D + 32 * grp + 8 * kb);
+      op.rl[nt][kb] = load_bf16x8(q.k.r_lo + o * D + 32 * grp + 8 * kb);
+      if constexpr (QJL)
+        op.sb[nt][kb] = q.has_k ? load_bf16x8(q.k.s_b + o * D + 32 * grp + 8 * kb) : bf16x8{};
+    }
+  }
+  for (int t = blockIdx.x; t < q.n_tiles; t += gridDim.x) {
+    const int tensor = t & 1;
+    const int rest = t >> 1;
+    const int i = rest % q.nblk_max;
+    const int bh = rest / q.nblk_max;
+    const int h = bh % q.Hkv, b = bh / q.Hkv;
+    if (tensor == 0 ? !q.has_k : !q.has_v) continue;
+    const QuantArgs& a = tensor == 0 ? q.k : q.v;
+    const int start = a.start_pos[b];
+    if (start < 0) continue;
+    const int end = min(start + a.n_new, a.T_cap);  // one past the last slot written
+    const int blk = start / 64 + i;
+    const int p0 = blk * 64;
+    if (p0 >= end) continue;  // uniform over the workgroup
+    const int lo_slot = max(start, p0), hi_slot = min(end, p0 + 64);
+    __syncthreads();  // the previous tile is fully stored
+    if (tensor == 0)
+      quantize_tile<true, KB, QJL, F32>(q.k, sm, op, b, h, start, blk, lo_slot, hi_slot);
+    else
+      quantize_tile<false, VB, false, F32>(q.v, sm, op, b, h, start, blk, lo_slot, hi_slot);
+  }
+}
+
+template <int KB, bool QJL, int VB>
+hipError_t launch_quantize(const QuantLaunch& q, bool f32, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  auto kern = f32 ? quantize_kernel<KB, QJL, VB, true> : quantize_kernel<KB, QJL, VB, false>;
+  if (e0 != nullptr || e1 != nullptr)
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, e0, e1, 0, q);
   else
-    hipLaunchKernelGGL((quantize_kernel<KEY, BITS, QJL, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, q);
   return hipGetLastError();
 }
 
-hipError_t dispatch_keys(const QuantArgs& a, int bits, bool qjl, bool f32, int B, hipStream_t s) {
-  if (qjl) {
-    switch (bits) {
-      case 0: return launch_quantize<true, 0, true>(a, f32, B, s);
-      case 1: return launch_quantize<true, 1, true>(a, f32, B, s);
-      case 2: return launch_quantize<true, 2, true>(a, f32, B, s);
-      case 3: return launch_quantize<true, 3, true>(a, f32, B, s);
-      case 4: return launch_quantize<true, 4, true>(a, f32, B, s);
-    }
-  } else {
-    switch (bits) {
-      case 1: return launch_quantize<true, 1, false>(a, f32, B, s);
-      case 2: return launch_quantize<true, 2, false>(a, f32, B, s);
-      case 3: return launch_quantize<true, 3, false>(a, f32, B, s);
-      case 4: return launch_quantize<true, 4, false>(a, f32, B, s);
-    }
+template <int KB, bool QJL>
+hipError_t dispatch_v(const QuantLaunch& q, int vb, bool f32, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  switch (vb) {
+    case 1: return launch_quantize<KB, QJL, 1>(q, f32, grid, s, e0, e1);
+    case 2: return launch_quantize<KB, QJL, 2>(q, f32, grid, s, e0, e1);
+    case 3: return launch_quantize<KB, QJL, 3>(q, f32, grid, s, e0, e1);
+    case 4: return launch_quantize<KB, QJL, 4>(q, f32, grid, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t dispatch_values(const QuantArgs& a, int bits, bool f32, int B, hipStream_t s) {
-  switch (bits) {
-    case 1: return launch_quantize<false, 1, false>(a, f32, B, s);
-    case 2: return launch_quantize<false, 2, false>(a, f32, B, s);
-    case 3: return launch_quantize<false, 3, false>(a, f32, B, s);
-    case 4: return launch_quantize<false, 4, false>(a, f32, B, s);
+hipError_t dispatch(const QuantLaunch& q, const tq_config& c, bool f32, int grid, hipStream_t s, hipEvent_t e0,
+                    hipEvent_t e1) {
+  if (c.k_qjl) {
+    switch (c.k_bits) {
+      case 0: return dispatch_v<0, true>(q, c.v_bits, f32, grid, s, e0, e1);
+      case 1: return dispatch_v<1, true>(q, c.v_bits, f32, grid, s, e0, e1);
+      case 2: return dispatch_v<2, true>(q, c.v_bits, f32, grid, s, e0, e1);
+      case 3: return dispatch_v<3, true>(q, c.v_bits, f32, grid, s, e0, e1);
+      case 4: return dispatch_v<4, true>(q, c.v_bits, f32, grid, s, e0, e1);
+    }
+  } else {
+    switch (c.k_bits) {
+      case 1: return dispatch_v<1, false>(q, c.v_bits, f32, grid, s, e0, e1);
+      case 2: return dispatch_v<2, false>(q, c.v_bits, f32, grid, s, e0, e1);
+      case 3: return dispatch_v<3, false>(q, c.v_bits, f32, grid, s, e0, e1);
+      case 4: return dispatch_v<4, false>(q, c.v_bits, f32, grid, s, e0, e1);
+    }
   }
   return hipErrorInvalidValue;
 }
@@ -440,36 +497,39 @@ extern "C" int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, con
   a.T_cap = cache->T_cap;
   a.r_hi = p->r_hi;
   a.r_lo = p->r_lo;
+  QuantLaunch q{};
+  q.k = a;
+  q.k.x = k;
+  q.k.s_b = p->s_qjl;
+  q.k.codes = cache->k_codes;
+  q.k.signs = cache->k_signs;
+  q.k.norm = cache->k_norm;
+  q.k.rnorm = cache->k_rnorm;
+  q.v = a;
+  q.v.x = v;
+  q.v.codes = cache->v_codes;
+  q.v.norm = cache->v_norm;
+  for (int l = 0; l < 16; ++l) {
+    q.k.centroids[l] = cb->k_centroids[l];
+    q.k.thresholds[l] = cb->k_thresholds[l];
+    q.v.centroids[l] = cb->v_centroids[l];
+    q.v.thresholds[l] = cb->v_thresholds[l];
+  }
+  q.has_k = k != nullptr;
+  q.has_v = v != nullptr;
+  q.Hkv = Hkv;
+  q.nblk_max = (n_new + 126) / 64;  // blocks a run of n_new slots can touch
+  const int64_t tiles = 2ll * B * Hkv * q.nblk_max;
+  if (tiles > (1ll << 30)) return fail(TQ_ERR_INVALID, "too many tokens in one call");
+  q.n_tiles = static_cast<int>(tiles);
+  const int grid = static_cast<int>(std::min<int64_t>(tiles, 3ll * device_cu_count()));
   const ProfileEvents& pe = profile_events();
-  const bool prof = pe.quant_start && pe.quant_stop;
-  if (prof) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(pe.quant_start), s);
-  if (k) {
-    QuantArgs ak = a;
-    ak.x = k;
-    ak.s_b = p->s_qjl;
-    ak.codes = cache->k_codes;
-    ak.signs = cache->k_signs;
-    ak.norm = cache->k_norm;
-    ak.rnorm = cache->k_rnorm;
-    for (int l = 0; l < 16; ++l) {
-      ak.centroids[l] = cb->k_centroids[l];
-      ak.thresholds[l] = cb->k_thresholds[l];
-    }
-    hipError_t e = dispatch_keys(ak, cb->cfg.k_bits, cb->cfg.k_qjl != 0, f32, B, s);
-    if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("key quantize launch: ") + hipGetErrorString(e));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (pe.quant_start && pe.quant_stop) {
+    e0 = reinterpret_cast<hipEvent_t>(pe.quant_start);
+    e1 = reinterpret_cast<hipEvent_t>(pe.quant_stop);
   }
-  if (v) {
-    QuantArgs av = a;
-    av.x = v;
-    av.codes = cache->v_codes;
-    av.norm = cache->v_norm;
-    for (int l = 0; l < 16; ++l) {
-      av.centroids[l] = cb->v_centroids[l];
-      av.thresholds[l] = cb->v_thresholds[l];
-    }
-    hipError_t e = dispatch_values(av, cb->cfg.v_bits, f32, B, s);
-    if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("value quantize launch: ") + hipGetErrorString(e));
-  }
-  if (prof) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(pe.quant_stop), s);
+  hipError_t e = dispatch(q, cb->cfg, f32, grid, s, e0, e1);
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("quantize launch: ") + hipGetErrorString(e));
   return TQ_OK;
 }
