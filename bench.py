@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--preset", default="turbo3", choices=["turbo3", "turbo4"])
+    ap.add_argument("--preset", default="turbo3", choices=["turbo3", "turbo4", "qjl1"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall time spent timing the oracle on the host (0 disables)")
     ap.add_argument("--kernel-reps", type=int, default=4, help="eager passes over the layers for kernel timing")

@@ -39,27 +39,39 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float KAPPA = 0.009791666936874390f;  // sqrt(pi/2)/128
 constexpr float NEG_BIG = -1.0e30f;
 constexpr int QREC = 288;   // f16 elements per prologue record: q1[128], q2[128], scales
-constexpr int PREC = 132;   // floats per partial record: acc[128], m, l, mv, pad
+constexpr int PREC = 132;   // floats per partial record: sums[128], m, l, scale, pad
 
-// ---- LDS code tables ----------------------------------------------------------------------
-// A lookup turns CPL codes of B bits (one KEYBITS-bit window) into CPL f16 values.
+// ---- code decoding ------------------------------------------------------------------------
+// An 8-code window of a lane's chunk becomes one f16x8 MFMA operand (element e = code at bits
+// B*e of the window) through wide LDS lookups (few LDS instructions per code):
+//   B = 1 and sign bits: an 8-bit key -> 8 values (16-byte entries, 256 entries);
+//   B = 2: an 8-bit key -> 4 codes (8-byte entries, 256 entries);
+//   B = 3: a 12-bit key -> 4 codes (8-byte entries, 4096 entries);
+//   B = 4: an 8-bit key -> 2 codes (4-byte entries, 256 entries).
+// Tables depend only on the bit width (codebooks do), so keys and values of the same width
+// share one table.
 template <int B>
-struct Tab {
-  static constexpr int CPL = (B == 1) ? 8 : (B == 4) ? 2 : 4;
-  static constexpr int KEYBITS = B * CPL;
-  static constexpr int ENTRIES = 1 << KEYBITS;
+struct Dec {
+  static constexpr int KEYBITS = (B == 3) ? 12 : 8;
+  static constexpr int CPL = (B == 1) ? 8 : (B == 4) ? 2 : 4;  // codes per lookup
   static constexpr int EBYTES = 2 * CPL;
-  static constexpr int BYTES = ENTRIES * EBYTES;
+  static constexpr int LDS_BYTES = (1 << KEYBITS) * EBYTES;
 };
+constexpr int SIGN_TABLE_BYTES = 256 * 16;
+
+__device__ __forceinline__ uint32_t pack_f16x2(_Float16 a, _Float16 b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
 
 template <int B>
-__device__ void build_table(uint8_t* tab, const float* cent, int tid, int nthreads) {
-  using T = Tab<B>;
+__device__ void build_code_table(uint8_t* tab, const float* cent, int tid) {
+  using T = Dec<B>;
   typedef _Float16 entry_t __attribute__((ext_vector_type(T::CPL)));
   _Float16 c16[1 << B];
 #pragma unroll
   for (int l = 0; l < (1 << B); ++l) c16[l] = static_cast<_Float16>(cent[l]);
-  for (int e = tid; e < T::ENTRIES; e += nthreads) {
+  for (int e = tid; e < (1 << T::KEYBITS); e += 256) {
     entry_t v;
 #pragma unroll
     for (int i = 0; i < T::CPL; ++i) v[i] = c16[(e >> (B * i)) & ((1 << B) - 1)];
@@ -67,49 +79,66 @@ __device__ void build_table(uint8_t* tab, const float* cent, int tid, int nthrea
   }
 }
 
-__device__ void build_sign_table(uint8_t* tab, int tid, int nthreads) {
-  for (int e = tid; e < 256; e += nthreads) {
-    f16x8 v;
+__device__ void build_sign_table(uint8_t* tab, int tid) {
+  f16x8 v;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = ((e >> i) & 1) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
-    *reinterpret_cast<f16x8*>(tab + e * 16) = v;
-  }
+  for (int i = 0; i < 8; ++i) v[i] = ((tid >> i) & 1) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
+  *reinterpret_cast<f16x8*>(tab + tid * 16) = v;
 }
 
-// Window W of 8*B bits (bits 8*B*W ..) of a little-endian dword array.
-template <int B, int W>
-__device__ __forceinline__ uint32_t window(const uint32_t* dw) {
-  constexpr int bit = 8 * B * W;
-  constexpr int word = bit >> 5, off = bit & 31;
-  uint32_t v = dw[word] >> off;
-  if constexpr (off + 8 * B > 32) v |= dw[word + 1] << (32 - off);
-  if constexpr (8 * B < 32) v &= (1u << (8 * B)) - 1u;
-  return v;
-}
-
-// 8 codes of a window -> f16x8 operand (element e = code at bits B*e of the window).
-template <int B>
-__device__ __forceinline__ f16x8 decode8(const uint8_t* tab, uint32_t w) {
-  if constexpr (B == 1) {
-    return *reinterpret_cast<const f16x8*>(tab + w * 16);
-  } else if constexpr (B == 2) {
-    const f16x4 a = *reinterpret_cast<const f16x4*>(tab + (w & 0xFFu) * 8);
-    const f16x4 b = *reinterpret_cast<const f16x4*>(tab + (w >> 8) * 8);
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  } else if constexpr (B == 3) {
-    const f16x4 a = *reinterpret_cast<const f16x4*>(tab + (w & 0xFFFu) * 8);
-    const f16x4 b = *reinterpret_cast<const f16x4*>(tab + (w >> 12) * 8);
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+// Bits P .. P+N-1 of the little-endian dword array dw, shifted left by S (a byte offset).
+template <int P, int N, int S>
+__device__ __forceinline__ uint32_t field(const uint32_t* dw) {
+  constexpr int w = P >> 5, o = P & 31;
+  constexpr uint32_t mask = ((1u << N) - 1u) << S;
+  if constexpr (o + N <= 32) {
+    if constexpr (o >= S)
+      return (dw[w] >> (o - S)) & mask;
+    else
+      return (dw[w] << (S - o)) & mask;
   } else {
-    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-    const f16x2 a = *reinterpret_cast<const f16x2*>(tab + (w & 0xFFu) * 4);
-    const f16x2 b = *reinterpret_cast<const f16x2*>(tab + ((w >> 8) & 0xFFu) * 4);
-    const f16x2 c = *reinterpret_cast<const f16x2*>(tab + ((w >> 16) & 0xFFu) * 4);
-    const f16x2 d = *reinterpret_cast<const f16x2*>(tab + (w >> 24) * 4);
-    const f16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
-    const f16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
-    return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_alignbit(dw[w + 1], dw[w], o - S) & mask;
   }
+}
+
+// The 8 B-bit codes starting at bit P of dw -> f16x8, via the LDS table tab.
+template <int B, int P>
+__device__ __forceinline__ f16x8 decode8(const uint32_t* dw, const uint8_t* tab) {
+  if constexpr (B == 1) {
+    return *reinterpret_cast<const f16x8*>(tab + field<P, 8, 4>(dw));
+  } else if constexpr (B == 2 || B == 3) {
+    constexpr int K = Dec<B>::KEYBITS;
+    const u32x2 a = *reinterpret_cast<const u32x2*>(tab + field<P, K, 3>(dw));
+    const u32x2 b = *reinterpret_cast<const u32x2*>(tab + field<P + K, K, 3>(dw));
+    return __builtin_bit_cast(f16x8, u32x4{a[0], a[1], b[0], b[1]});
+  } else {
+    return __builtin_bit_cast(f16x8, u32x4{*reinterpret_cast<const uint32_t*>(tab + field<P, 8, 2>(dw)),
+                                           *reinterpret_cast<const uint32_t*>(tab + field<P + 8, 8, 2>(dw)),
+                                           *reinterpret_cast<const uint32_t*>(tab + field<P + 16, 8, 2>(dw)),
+                                           *reinterpret_cast<const uint32_t*>(tab + field<P + 24, 8, 2>(dw))});
+  }
+}
+
+// 8 sign bits starting at bit P of dw -> f16x8 of +1 / -1.
+template <int P>
+__device__ __forceinline__ f16x8 decode_signs(const uint32_t* dw, const uint8_t* tab) {
+  return *reinterpret_cast<const f16x8*>(tab + field<P, 8, 4>(dw));
+}
+
+// Reductions over the 4 lanes of a column (lanes l, l^16, l^32, l^48) with the gfx950
+// row-swap instructions (VALU, no LDS round trip): each swap returns this lane's value and
+// its partner's, in some order, so max / sum of the pair is the pairwise reduction.
+__device__ __forceinline__ float col_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float col_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int I, int N, typename F>
@@ -331,23 +360,29 @@ template <int KB, bool QJL, int VB, int G>
 struct MainCfg {
   static constexpr int TPD = 16 / G;       // score tiles packed into one accumulator set
   static constexpr int NSETS = 4 / TPD;    // accumulator sets per 64-key block
-  static constexpr int KTAB = KB > 0 ? Tab<(KB > 0 ? KB : 1)>::BYTES : 0;
-  static constexpr int STAB = QJL ? 4096 : 0;
-  static constexpr int VTAB = Tab<VB>::BYTES;
+  static constexpr bool SHARED = (KB == VB);  // one table serves keys and values
+  static constexpr int KTAB = KB > 0 ? Dec<(KB > 0 ? KB : 1)>::LDS_BYTES : 0;
+  static constexpr int STAB = QJL ? SIGN_TABLE_BYTES : 0;
+  static constexpr int VTAB = SHARED ? 0 : Dec<VB>::LDS_BYTES;
   static constexpr int TABLES = KTAB + STAB + VTAB;
-  // per wave and column: acc + state; then the merged rotated sums [16][QS] and states
+  // per wave and column: acc + state; then the merged rotated sums [16][QS] and states.  The
+  // merge area reuses the table space once every wave has left the block loop.
   static constexpr int MERGE = 4 * 16 * PREC * 4 + 16 * QS * 4 + 16 * 4 * 4;
   static constexpr int LDS = TABLES > MERGE ? TABLES : MERGE;
 };
 
-template <int KB, bool QJL, int VB, int G>
-__global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
+#ifndef ATTN_MIN_WG
+#define ATTN_MIN_WG 2
+#endif
+// Streams the 64-key blocks of one slice.  SCORES: also write the logits (parity runs).
+template <int KB, bool QJL, int VB, int G, bool SCORES>
+__global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   using C = MainCfg<KB, QJL, VB, G>;
   constexpr int TPD = C::TPD, NSETS = C::NSETS;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
   uint8_t* ktab = smem;
   uint8_t* stab = smem + C::KTAB;
-  uint8_t* vtab = smem + C::KTAB + C::STAB;
+  uint8_t* vtab = C::SHARED ? smem : smem + C::KTAB + C::STAB;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, g = lane >> 4;
@@ -358,9 +393,9 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
   const int64_t bh = (int64_t)b * a.Hkv + kvh;
   const int nblk_cap = a.T_cap / 64;
 
-  if constexpr (KB > 0) build_table<KB>(ktab, a.k_cent, tid, 256);
-  if constexpr (QJL) build_sign_table(stab, tid, 256);
-  build_table<VB>(vtab, a.v_cent, tid, 256);
+  if constexpr (KB > 0) build_code_table<(KB > 0 ? KB : 1)>(ktab, a.k_cent, tid);
+  if constexpr (QJL) build_sign_table(stab, tid);
+  if constexpr (!C::SHARED) build_code_table<VB>(vtab, a.v_cent, tid);
 
   // query operands: lane (col, g) holds q[hh][32 g + 8 kb + e] of every k-block kb
   const _Float16* qr = a.qrec + ((int64_t)b * Hq + kvh * G + hh) * QREC;
@@ -370,9 +405,11 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
     bq[kb] = *reinterpret_cast<const f16x8*>(qr + 32 * g + 8 * kb);
     bs[kb] = *reinterpret_cast<const f16x8*>(qr + D + 32 * g + 8 * kb);
   }
-  // the table holds centroids c; the key term is q1 . c / sqrt(d)
-  const float s1 = reinterpret_cast<const float*>(qr + 2 * D)[0] * INV_SQRT_D;
-  const float s2 = reinterpret_cast<const float*>(qr + 2 * D)[1];
+  // logit * log2(e) = n (code_acc * c1 + rnorm * sign_acc * c2): the table holds centroids c,
+  // the key term is q1 . c / sqrt(d), the sign term carries sqrt(pi/2)/m
+  const float lscale = a.scale * LOG2E;
+  const float c1 = reinterpret_cast<const float*>(qr + 2 * D)[0] * INV_SQRT_D * lscale;
+  const float c2 = reinterpret_cast<const float*>(qr + 2 * D)[1] * KAPPA * lscale;
 
   int seq = a.seq_len[b];
   seq = seq < 1 ? 1 : (seq > a.max_seq_len ? a.max_seq_len : seq);
@@ -381,7 +418,9 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
   const int blk_begin = slice * a.blocks_per_wave;
   const int blk_end = min(blk_begin + a.blocks_per_wave, nblk);
 
-  float m_run = NEG_BIG, mv_run = NEG_BIG, l_run = 0.f;
+  // online softmax per lane column: m_run (log2 domain), l_run = sum 2^(lg - m_run);
+  // acc = sum P' V with P' = 2^(lg - m_run) nv / s_run and s_run >= every such product
+  float m_run = NEG_BIG, l_run = 0.f, s_run = 0.f;
   f32x4 acc[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -389,17 +428,23 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
   __syncthreads();  // tables ready
 
   // Block data of one lane; the next block is loaded while the current one is processed.
+  // Codes of the next block are loaded while the current one is processed; the norms of
+  // the current block are loaded at its start (they are first needed after the score MFMAs).
   struct Blk {
     uint32_t kd[KB > 0 ? 4 * KB : 1];
     uint32_t sd[4];
     uint32_t vd[4 * VB];
-    f32x4 kn[NSETS], kr[NSETS], vn[NSETS];
   };
   auto load_block = [&](int blk, Blk& d) {
     if constexpr (KB > 0)
       load_dwords<4 * KB>(d.kd, a.k_codes + (bh * nblk_cap + blk) * (1024 * KB) + lane * 16 * KB);
     if constexpr (QJL) load_dwords<4>(d.sd, a.k_signs + (bh * nblk_cap + blk) * 1024 + lane * 16);
     load_dwords<4 * VB>(d.vd, a.v_codes + (bh * nblk_cap + blk) * (1024 * VB) + lane * 16 * VB);
+  };
+  struct Norms {
+    f32x4 kn[NSETS], kr[NSETS], vn[NSETS];
+  };
+  auto load_norms = [&](int blk, Norms& d) {
 #pragma unroll
     for (int s = 0; s < NSETS; ++s) {
       const int64_t tok = bh * a.T_cap + blk * 64 + 16 * (s * TPD + tcls) + 4 * g;
@@ -412,103 +457,109 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
   if (blk_begin < blk_end) load_block(blk_begin, cur);
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
+    Norms nrm;
+    load_norms(blk, nrm);
     if (blk + 1 < blk_end) load_block(blk + 1, nxt);
-    const uint32_t* kd = cur.kd;
-    const uint32_t* sd = cur.sd;
-    const uint32_t* vd = cur.vd;
-    const f32x4* kn = cur.kn;
-    const f32x4* kr = cur.kr;
-    const f32x4* vn = cur.vn;
 
-    // ---- score MFMAs: tile t = keys 16 t .. 16 t + 15 of the block ------------------------
-    f32x4 dc[4], ds[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      dc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      ds[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---- score MFMAs: tile t = keys 16 t .. 16 t + 15 of the block; each lane keeps the
+    // tile of its column class in every set (tile s TPD + tcls of set s) ----------------------
+    f32x4 cs[NSETS], ss[NSETS];
+    static_for<0, 4>([&](auto T_) {
+      constexpr int t = decltype(T_)::value;
+      f32x4 dc = f32x4{0.f, 0.f, 0.f, 0.f}, ds = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (KB > 0) {
-        const uint32_t* seg = kd + KB * t;
-        dc[t] = mfma_f16(decode8<KB>(ktab, window<KB, 0>(seg)), bq[0], dc[t]);
-        dc[t] = mfma_f16(decode8<KB>(ktab, window<KB, 1>(seg)), bq[1], dc[t]);
-        dc[t] = mfma_f16(decode8<KB>(ktab, window<KB, 2>(seg)), bq[2], dc[t]);
-        dc[t] = mfma_f16(decode8<KB>(ktab, window<KB, 3>(seg)), bq[3], dc[t]);
+        static_for<0, 4>([&](auto KB_) {
+          constexpr int kb = decltype(KB_)::value;
+          dc = mfma_f16(decode8<KB, 32 * KB * t + 8 * KB * kb>(cur.kd, ktab), bq[kb], dc);
+        });
       }
       if constexpr (QJL) {
-        const uint32_t* seg = sd + t;
-        ds[t] = mfma_f16(decode8<1>(stab, window<1, 0>(seg)), bs[0], ds[t]);
-        ds[t] = mfma_f16(decode8<1>(stab, window<1, 1>(seg)), bs[1], ds[t]);
-        ds[t] = mfma_f16(decode8<1>(stab, window<1, 2>(seg)), bs[2], ds[t]);
-        ds[t] = mfma_f16(decode8<1>(stab, window<1, 3>(seg)), bs[3], ds[t]);
+        static_for<0, 4>([&](auto KB_) {
+          constexpr int kb = decltype(KB_)::value;
+          ds = mfma_f16(decode_signs<32 * t + 8 * kb>(cur.sd, stab), bs[kb], ds);
+        });
       }
-    }
+      constexpr int st_ = t / TPD, ct = t % TPD;
+      if constexpr (ct == 0) {
+        cs[st_] = dc;
+        ss[st_] = ds;
+      } else {
+        if (tcls == ct) {
+          cs[st_] = dc;
+          ss[st_] = ds;
+        }
+      }
+    });
 
     // ---- logits of this lane's keys: set s, row i -> key 16 (s TPD + tcls) + 4 g + i --------
-    float lg[NSETS][4], lgv[NSETS][4];
+    // lg = logit * log2(e); lgb = lg + an upper bound of log2(nv) (from the float exponent),
+    // so that 2^(lg - m) nv <= 2^(lgb - m).  One column reduction of (max lg, max lgb).
+    float lg[NSETS][4];
     float mb = NEG_BIG, mvb = NEG_BIG;
 #pragma unroll
     for (int s = 0; s < NSETS; ++s) {
-      f32x4 c4 = dc[s * TPD], s4 = ds[s * TPD];
-#pragma unroll
-      for (int c = 1; c < TPD; ++c) {
-        if (tcls == c) {
-          c4 = dc[s * TPD + c];
-          s4 = ds[s * TPD + c];
-        }
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = blk * 64 + 16 * (s * TPD + tcls) + 4 * g + i;
         float est = 0.f;
-        if constexpr (KB > 0) est = c4[i] * s1;
-        if constexpr (QJL) {
-          const float rn = (KB > 0) ? kr[s][i] : 1.0f;
-          est = fmaf(rn * KAPPA, s4[i] * s2, est);
-        }
-        const float logit = kn[s][i] * est * a.scale;
+        if constexpr (KB > 0) est = cs[s][i] * c1;
+        if constexpr (QJL) est = fmaf((KB > 0 ? nrm.kr[s][i] : 1.0f) * ss[s][i], c2, est);
+        const float l2 = nrm.kn[s][i] * est;
         const bool valid = key < seq;
-        if (a.scores_out != nullptr && valid)
-          a.scores_out[((int64_t)b * Hq + kvh * G + hh) * a.T_cap + key] = logit;
-        const float l2 = logit * LOG2E;
-        const float vnv = vn[s][i];
+        if constexpr (SCORES) {
+          if (valid) a.scores_out[((int64_t)b * Hq + kvh * G + hh) * a.T_cap + key] = l2 * (1.0f / LOG2E);
+        }
         lg[s][i] = valid ? l2 : -INFINITY;
-        lgv[s][i] = (valid && vnv > 0.f) ? l2 + __log2f(vnv) : -INFINITY;
+        const float ebound = static_cast<float>(static_cast<int>(__float_as_uint(nrm.vn[s][i]) >> 23) - 126);
         mb = fmaxf(mb, lg[s][i]);
-        mvb = fmaxf(mvb, lgv[s][i]);
+        mvb = fmaxf(mvb, lg[s][i] + ebound);
       }
     }
-    mb = fmaxf(mb, __shfl_xor(mb, 16));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    mvb = fmaxf(mvb, __shfl_xor(mvb, 16));
-    mvb = fmaxf(mvb, __shfl_xor(mvb, 32));
-    const float m_new = fmaxf(m_run, mb), mv_new = fmaxf(mv_run, mvb);
-    const float alpha = exp2f(m_run - m_new), alphav = exp2f(mv_run - mv_new);
-    m_run = m_new;
-    mv_run = mv_new;
-    float lsum = 0.f;
-    _Float16 pw[NSETS][4];
+    mb = col_max(mb);
+    mvb = col_max(mvb);
+    const float m_new = fmaxf(m_run, mb);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float s_scaled = s_run * alpha;
+    const float s_new = fmaxf(s_scaled, __builtin_amdgcn_exp2f(mvb - m_new));
+    const float inv = s_new > 0.f ? __builtin_amdgcn_rcpf(s_new) : 0.f;
+    const float f = s_new > 0.f ? s_scaled * inv : 1.0f;
+    if (__any(f != 1.0f)) {  // rescale only when some column's scale moved
 #pragma unroll
-    for (int s = 0; s < NSETS; ++s)
+      for (int mt = 0; mt < 8; ++mt) acc[mt] *= f;
+    }
+    float lsum = 0.f;
+    uint32_t pw[NSETS][2];
+#pragma unroll
+    for (int s = 0; s < NSETS; ++s) {
+      float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        lsum += exp2f(lg[s][i] - m_new);
-        pw[s][i] = static_cast<_Float16>(exp2f(lgv[s][i] - mv_new));
+        const float pr = __builtin_amdgcn_exp2f(lg[s][i] - m_new);  // 0 for keys past the sequence
+        lsum += pr;
+        x[i] = pr > 0.f ? fminf(pr * nrm.vn[s][i] * inv, 1.0f) : 0.f;
       }
+      pw[s][0] = pack_f16x2(static_cast<_Float16>(x[0]), static_cast<_Float16>(x[1]));
+      pw[s][1] = pack_f16x2(static_cast<_Float16>(x[2]), static_cast<_Float16>(x[3]));
+    }
+    m_run = m_new;
+    s_run = s_new;
     l_run = fmaf(l_run, alpha, lsum);
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[mt] *= alphav;
 
     // ---- value MFMAs: k-block kb2 holds tiles 2 kb2 (elements 0..3) and 2 kb2 + 1 (4..7) ---
     static_for<0, 2>([&](auto KB2) {
       constexpr int kb2 = decltype(KB2)::value;
-      f16x8 bp;
+      u32x4 bpw;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int te = 2 * kb2 + (e >> 2);
-        bp[e] = (te % TPD == tcls) ? pw[te / TPD][e & 3] : static_cast<_Float16>(0.0f);
+      for (int hf = 0; hf < 2; ++hf) {
+        const int te = 2 * kb2 + hf;
+        const bool mine = (te % TPD) == tcls;
+        bpw[2 * hf] = mine ? pw[te / TPD][0] : 0u;
+        bpw[2 * hf + 1] = mine ? pw[te / TPD][1] : 0u;
       }
+      const f16x8 bp = __builtin_bit_cast(f16x8, bpw);
       static_for<0, 8>([&](auto MT) {
         constexpr int mt = decltype(MT)::value;
-        const f16x8 av = decode8<VB>(vtab, window<VB, 2 * mt + kb2>(vd));
+        const f16x8 av = decode8<VB, 8 * VB * (2 * mt + kb2)>(cur.vd, vtab);
         acc[mt] = mfma_f16(av, bp, acc[mt]);
       });
     });
@@ -516,8 +567,7 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
   }
 
   // ---- merge the 4 waves and the TPD column classes of each q-head in LDS, then unrotate ----
-  const float l_col = l_run + __shfl_xor(l_run, 16);
-  const float l_tot = l_col + __shfl_xor(l_col, 32);
+  const float l_tot = col_sum(l_run);
   // R_eff^T operands for this wave's output coordinates k = 32 wave + 16 nt + col
   bf16x8 th[2][4], tl[2][4];
 #pragma unroll
@@ -529,10 +579,10 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
       tl[nt][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_lo + k * D + 32 * g + 8 * kb));
     }
   }
-  __syncthreads();  // tables dead
+  __syncthreads();  // every wave is done with the tables
   float* mrg = reinterpret_cast<float*>(smem);
   float* amat = mrg + 4 * 16 * PREC;  // [16][QS] merged rotated sums (rows >= G zero)
-  float* st = amat + 16 * QS;         // [16][4] m, l, mv
+  float* st = amat + 16 * QS;         // [16][4] m, l
   float* rec = mrg + (wave * 16 + col) * PREC;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
@@ -541,7 +591,7 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
   if (g == 0) {
     rec[128] = m_run;
     rec[129] = l_tot;
-    rec[130] = mv_run;
+    rec[130] = s_run;
   }
   __syncthreads();
   for (int idx = tid; idx < 16 * D; idx += 256) {
@@ -550,25 +600,21 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
       amat[h * QS + j] = 0.f;
       continue;
     }
-    float M = NEG_BIG, MV = NEG_BIG;
+    float M = NEG_BIG;
     for (int w = 0; w < 4; ++w)
-      for (int c = 0; c < TPD; ++c) {
-        const float* r = mrg + (w * 16 + c * G + h) * PREC;
-        M = fmaxf(M, r[128]);
-        MV = fmaxf(MV, r[130]);
-      }
+      for (int c = 0; c < TPD; ++c) M = fmaxf(M, mrg[(w * 16 + c * G + h) * PREC + 128]);
     float Ls = 0.f, A = 0.f;
     for (int w = 0; w < 4; ++w)
       for (int c = 0; c < TPD; ++c) {
         const float* r = mrg + (w * 16 + c * G + h) * PREC;
-        Ls += r[129] * exp2f(r[128] - M);
-        A += r[j] * exp2f(r[130] - MV);
+        const float e = exp2f(r[128] - M);
+        Ls += r[129] * e;
+        A += r[j] * (r[130] * e);
       }
     amat[h * QS + j] = A;
     if (j == 0) {
       st[4 * h + 0] = M;
       st[4 * h + 1] = Ls;
-      st[4 * h + 2] = MV;
     }
   }
   __syncthreads();
@@ -604,7 +650,6 @@ __global__ void __launch_bounds__(256, 2) attend_kernel(MainArgs a) {
     float* out = a.part + (((int64_t)b * Hq + kvh * G + tid) * a.n_slices + blockIdx.x) * PREC;
     out[128] = st[4 * tid + 0];
     out[129] = st[4 * tid + 1];
-    out[130] = st[4 * tid + 2];
   }
 }
 
@@ -640,17 +685,14 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   const int tid = threadIdx.x;
   const int64_t head = blockIdx.x;
   const float* base = a.part + head * a.n_slices * PREC;
-  float m = NEG_BIG, mv = NEG_BIG;
-  for (int s = tid; s < a.n_slices; s += 256) {
-    m = fmaxf(m, base[s * PREC + 128]);
-    mv = fmaxf(mv, base[s * PREC + 130]);
-  }
+  float m = NEG_BIG;
+  for (int s = tid; s < a.n_slices; s += 256) m = fmaxf(m, base[s * PREC + 128]);
   const float M = block_reduce(m, red, true);
-  const float MV = block_reduce(mv, red, true);
   float l = 0.f;
   for (int s = tid; s < a.n_slices; s += 256) {
-    l += base[s * PREC + 129] * exp2f(base[s * PREC + 128] - M);
-    wa[s] = exp2f(base[s * PREC + 130] - MV);
+    const float e = exp2f(base[s * PREC + 128] - M);
+    l += base[s * PREC + 129] * e;
+    wa[s] = e;
   }
   const float L = block_reduce(l, red, false);  // also orders the wa writes before the reads
   const int k = tid & (D - 1), hf = tid >> 7;
@@ -662,24 +704,19 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
   if (hf == 0) {
     acc += half_sum[k];
     // value centroids enter as c / sqrt(d)
-    a.out[head * D + k] = L > 0.f ? acc / L * exp2f(MV - M) * INV_SQRT_D : 0.f;
+    a.out[head * D + k] = L > 0.f ? acc / L * INV_SQRT_D : 0.f;
   }
 }
 
 template <int KB, bool QJL, int VB, int G>
 hipError_t launch_main(const MainArgs& a, int n_slices, int B, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   using C = MainCfg<KB, QJL, VB, G>;
-  auto kern = attend_kernel<KB, QJL, VB, G>;
-  if (C::LDS > 65536) {
-    static std::once_flag once;
-    std::call_once(once, [&] {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    });
-  }
+  static_assert(C::LDS <= 65536, "attention LDS budget");
+  auto kern = a.scores_out != nullptr ? attend_kernel<KB, QJL, VB, G, true> : attend_kernel<KB, QJL, VB, G, false>;
   if (e0 != nullptr || e1 != nullptr)
-    hipExtLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(256), C::LDS, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(256), 0, s, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(256), C::LDS, s, a);
+    hipLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
