@@ -10,7 +10,7 @@
 //   score_i = n_i (sum_j q1_j c[code_ij]/sqrt(d) + rnorm_i sqrt(pi/2)/m sum_j q2_j (2 sign_ij - 1));
 //   p = softmax(scale * score);  out = R_eff^T sum_i p_i nv_i cv[codev_i] / sqrt(d).
 //
-// Three launches on the caller's stream:
+// Two launches on the caller's stream:
 //  1. prologue: q1, q2 per (batch row, q-head), stored as f16 with a power-of-two scale;
 //  2. main: one workgroup of 4 waves per (batch row, kv-head, context slice); each wave
 //     streams 64-key blocks of its sub-slice.  Codes are turned into f16 MFMA operands by
@@ -18,8 +18,10 @@
 //     MFMAs (one key read serves all G q-heads of the group), the softmax weights of a
 //     score tile feed the value MFMA directly from the accumulator layout, and the value
 //     sum stays in the rotated domain.  The 4 waves merge their online-softmax states in
-//     LDS and write one partial per (q-head, slice);
-//  3. merge: log-sum-exp over slices, then the unrotation R_eff^T (fp32).
+//     LDS and write one partial per (q-head, slice).  Arrival counters then elect, per
+//     (batch row, kv-head), the last workgroup of each group of 16 slices to merge that
+//     group (log-sum-exp), and the last of those to merge the groups and apply R_eff^T
+//     (exact bf16-split MFMA, fp32 sums) - no separate merge launch.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
@@ -40,6 +42,9 @@ constexpr float KAPPA = 0.009791666936874390f;  // sqrt(pi/2)/128
 constexpr float NEG_BIG = -1.0e30f;
 constexpr int QREC = 288;   // f16 elements per prologue record: q1[128], q2[128], scales
 constexpr int PREC = 132;   // floats per partial record: sums[128], m, l, scale, pad
+constexpr int MGROUP = 16;                       // slices per first-level merge group
+constexpr int MAX_GROUPS = 32;                   // merge groups per (batch row, kv-head)
+constexpr int MAX_SLICES = MGROUP * MAX_GROUPS;  // context slices per (batch row, kv-head)
 
 // ---- code decoding ------------------------------------------------------------------------
 // An 8-code window of a lane's chunk becomes one f16x8 MFMA operand (element e = code at bits
@@ -71,6 +76,18 @@ __device__ void build_code_table(uint8_t* tab, const float* cent, int tid) {
   _Float16 c16[1 << B];
 #pragma unroll
   for (int l = 0; l < (1 << B); ++l) c16[l] = static_cast<_Float16>(cent[l]);
+  if constexpr (B == 3) {
+    // entry e = tid + 256 k (k < 16) holds codes e & 7, (e >> 3) & 7, (e >> 6) & 7, e >> 9:
+    // the first two depend only on the lane (e & 63 = tid & 63), the third is
+    // c[w + 4 (k & 1)] for the wave w = tid >> 6, the fourth c[k >> 1]
+    const int lane = tid & 63, w = tid >> 6;
+    const uint32_t lo = pack_f16x2(c16[lane & 7], c16[(lane >> 3) & 7]);
+    const _Float16 x0 = c16[w], x1 = c16[w + 4];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      *reinterpret_cast<u32x2*>(tab + (tid + 256 * k) * 8) = u32x2{lo, pack_f16x2((k & 1) ? x1 : x0, c16[k >> 1])};
+    return;
+  }
   for (int e = tid; e < (1 << T::KEYBITS); e += 256) {
     entry_t v;
 #pragma unroll
@@ -173,6 +190,8 @@ struct PrologueArgs {
   _Float16* qrec;       // [B*Hq][QREC]
   uint16_t* rt_hi;      // [128][128] R_hi^T
   uint16_t* rt_lo;      // [128][128] R_lo^T
+  unsigned* cnt_grp;    // merge counters of the main kernel, zeroed here
+  unsigned* cnt_top;
   int G, n_groups;
 };
 
@@ -218,6 +237,8 @@ __global__ void __launch_bounds__(256) prologue_kernel(PrologueArgs a) {
   }
   float* q1s = psm;  // [16][QS]
   __shared__ unsigned int mx[2][16];
+  if (tid < MAX_GROUPS) a.cnt_grp[blockIdx.x * MAX_GROUPS + tid] = 0u;
+  if (tid == MAX_GROUPS) a.cnt_top[blockIdx.x] = 0u;
   const int G = a.G;
   const bool sketch = a.s_b != nullptr;
   const int64_t head0 = (int64_t)blockIdx.x * G;
@@ -336,6 +357,75 @@ __global__ void __launch_bounds__(256) prologue_kernel(PrologueArgs a) {
 }
 
 // ---- main kernel ----------------------------------------------------------------------------
+
+// Partial results crossing workgroups are written and read with device-scope (coherent)
+// atomic accesses, which bypass the non-coherent per-XCD caching of ordinary accesses.  A
+// writer drains its stores (s_waitcnt) before the workgroup barrier that precedes its
+// arrival increment; a reader issues its loads only after its own increment has returned
+// with the final count.  No cache-wide writeback or invalidate is needed.
+__device__ __forceinline__ void st_dev2(float* p, float x, float y) {
+  const uint64_t v = static_cast<uint64_t>(__float_as_uint(x)) | (static_cast<uint64_t>(__float_as_uint(y)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 ld_dev2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
+__device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+// LDS of the epilogue (aliases the decode tables)
+struct Epi {
+  float rec[64][PREC];  // per wave and lane column: rotated sums, m, l, value scale
+  float w64[64];        // weight of each record in its q-head's merge
+  float amat[16][QS];   // merged rotated sums of the q-heads (rows >= G unused)
+  float st[16][2];      // merged max and sum of each q-head
+  int stage;
+};
+
+struct Merged {
+  f32x4 A;  // weighted sums of one 4-float chunk
+  float M, L;
+};
+
+// Log-sum-exp merge of `count` partial records (sums[128], m, l at stride PREC from hs) for
+// the 4-float chunk c of the sums.  Records are loaded 16 at a time, all loads of a batch in
+// flight together, and merged online.
+__device__ Merged merge_chunk(const float* hs, int count, int c) {
+  float M = NEG_BIG, L = 0.f;
+  f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < count; r0 += 16) {
+    float2 ml[16];
+    f32x4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (r0 + k < count) {
+        const float* rec = hs + static_cast<int64_t>(r0 + k) * PREC;
+        ml[k] = ld_dev2(rec + 128);
+        const float2 x = ld_dev2(rec + 4 * c), y = ld_dev2(rec + 4 * c + 2);
+        v[k] = f32x4{x.x, x.y, y.x, y.y};
+      } else {
+        ml[k] = make_float2(NEG_BIG, 0.f);
+        v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) Mb = fmaxf(Mb, ml[k].x);
+    const float sc = exp2f(M - Mb);
+    A *= sc;
+    L *= sc;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float e = exp2f(ml[k].x - Mb);  // 0 for empty records unless all are empty (then v = l = 0)
+      A += e * v[k];
+      L = fmaf(e, ml[k].y, L);
+    }
+    M = Mb;
+  }
+  return Merged{A, M, L};
+}
+
 struct MainArgs {
   const uint8_t* k_codes;
   const uint8_t* k_signs;
@@ -347,7 +437,11 @@ struct MainArgs {
   const _Float16* qrec;
   const uint16_t* rt_hi;  // R_hi^T, R_lo^T (written by the prologue)
   const uint16_t* rt_lo;
-  float* part;        // [B*Hq][n_slices][PREC]: unrotated sums, m, l, mv
+  float* part;        // [B*Hq][n_slices][PREC]: rotated sums, m, l of each slice
+  float* gpart;       // [B*Hq][n_groups][PREC]: the same per group of MGROUP slices
+  unsigned* cnt_grp;  // [B*Hkv][MAX_GROUPS] arrival counters (zeroed by the prologue)
+  unsigned* cnt_top;  // [B*Hkv]
+  float* out;         // [B*Hq][128]
   float* scores_out;  // NULL or [B*Hq][T_cap]
   int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices;
   float scale_log2;   // scale * log2(e)
@@ -365,9 +459,8 @@ struct MainCfg {
   static constexpr int STAB = QJL ? SIGN_TABLE_BYTES : 0;
   static constexpr int VTAB = SHARED ? 0 : Dec<VB>::LDS_BYTES;
   static constexpr int TABLES = KTAB + STAB + VTAB;
-  // per wave and column: acc + state; then the merged rotated sums [16][QS] and states.  The
-  // merge area reuses the table space once every wave has left the block loop.
-  static constexpr int MERGE = 4 * 16 * PREC * 4 + 16 * QS * 4 + 16 * 4 * 4;
+  // the epilogue reuses the table space once every wave has left the block loop
+  static constexpr int MERGE = static_cast<int>(sizeof(Epi));
   static constexpr int LDS = TABLES > MERGE ? TABLES : MERGE;
 };
 
@@ -392,10 +485,6 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   const int Hq = a.Hkv * G;
   const int64_t bh = (int64_t)b * a.Hkv + kvh;
   const int nblk_cap = a.T_cap / 64;
-
-  if constexpr (KB > 0) build_code_table<(KB > 0 ? KB : 1)>(ktab, a.k_cent, tid);
-  if constexpr (QJL) build_sign_table(stab, tid);
-  if constexpr (!C::SHARED) build_code_table<VB>(vtab, a.v_cent, tid);
 
   // query operands: lane (col, g) holds q[hh][32 g + 8 kb + e] of every k-block kb
   const _Float16* qr = a.qrec + ((int64_t)b * Hq + kvh * G + hh) * QREC;
@@ -425,11 +514,9 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  __syncthreads();  // tables ready
-
-  // Block data of one lane; the next block is loaded while the current one is processed.
-  // Codes of the next block are loaded while the current one is processed; the norms of
-  // the current block are loaded at its start (they are first needed after the score MFMAs).
+  // Block data of one lane.  Codes of the next block are loaded while the current one is
+  // processed; the norms of the current block are loaded at its start (they are first needed
+  // after the score MFMAs).
   struct Blk {
     uint32_t kd[KB > 0 ? 4 * KB : 1];
     uint32_t sd[4];
@@ -454,7 +541,12 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
     }
   };
   Blk cur, nxt;
-  if (blk_begin < blk_end) load_block(blk_begin, cur);
+  if (blk_begin < blk_end) load_block(blk_begin, cur);  // in flight while the tables are built
+
+  if constexpr (KB > 0) build_code_table<(KB > 0 ? KB : 1)>(ktab, a.k_cent, tid);
+  if constexpr (QJL) build_sign_table(stab, tid);
+  if constexpr (!C::SHARED) build_code_table<VB>(vtab, a.v_cent, tid);
+  __syncthreads();  // tables ready
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
     Norms nrm;
@@ -566,8 +658,88 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
     cur = nxt;
   }
 
-  // ---- merge the 4 waves and the TPD column classes of each q-head in LDS, then unrotate ----
+  // ---- merge the 4 waves and the TPD column classes of each q-head in LDS ----------------------
   const float l_tot = col_sum(l_run);
+  __syncthreads();  // every wave is done with the tables
+  Epi* ep = reinterpret_cast<Epi*>(smem);
+  {
+    float* rec = ep->rec[wave * 16 + col];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rec[16 * mt + 4 * g + i] = acc[mt][i];
+    if (g == 0) {
+      rec[128] = m_run;
+      rec[129] = l_tot;
+      rec[130] = s_run;
+    }
+  }
+  __syncthreads();
+  // record r = 16 w + c G + h belongs to q-head h; wave 0 finds each head's maximum and the
+  // record weights over the lanes with the same h (xor offsets that keep r mod G)
+  if (tid < 64) {
+    const float* rec = ep->rec[tid];
+    const float m = rec[128];
+    float M = m;
+#pragma unroll
+    for (int o = G; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float e = exp2f(m - M);
+    ep->w64[tid] = rec[130] * e;
+    float l = rec[129] * e;
+#pragma unroll
+    for (int o = G; o < 64; o <<= 1) l += __shfl_xor(l, o);
+    if (tid < G) st_dev2(a.part + ((bh * G + tid) * a.n_slices + blockIdx.x) * PREC + 128, M, l);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D / 2; idx += 256) {
+    const int h = idx / (D / 2), j = 2 * (idx % (D / 2));
+    float A0 = 0.f, A1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int c = 0; c < TPD; ++c) {
+        const int r = 16 * w + c * G + h;
+        A0 = fmaf(ep->rec[r][j], ep->w64[r], A0);
+        A1 = fmaf(ep->rec[r][j + 1], ep->w64[r], A1);
+      }
+    st_dev2(a.part + ((bh * G + h) * a.n_slices + blockIdx.x) * PREC + j, A0, A1);
+  }
+
+  // ---- merge over the slices: the last workgroup of each group of 16 slices merges the
+  // group, the last group merger merges the groups and applies R_eff^T ---------------------
+  const int ns = a.n_slices;
+  const int ngrp = (ns + MGROUP - 1) / MGROUP;
+  const int grp = blockIdx.x / MGROUP;
+  drain_stores();
+  __syncthreads();
+  if (tid == 0) {
+    int stage = 0;
+    if (ngrp == 1) {
+      stage = atomicAdd(a.cnt_top + bh, 1u) == static_cast<unsigned>(ns - 1) ? 2 : 0;
+    } else {
+      const int gsize = min(MGROUP, ns - MGROUP * grp);
+      stage = atomicAdd(a.cnt_grp + bh * MAX_GROUPS + grp, 1u) == static_cast<unsigned>(gsize - 1) ? 1 : 0;
+    }
+    ep->stage = stage;
+  }
+  __syncthreads();
+  if (ep->stage == 0) return;
+  if (ep->stage == 1) {
+    const int gsize = min(MGROUP, ns - MGROUP * grp);
+    for (int idx = tid; idx < G * 32; idx += 256) {
+      const int h = idx >> 5, c = idx & 31;
+      const Merged r = merge_chunk(a.part + ((bh * G + h) * ns + MGROUP * grp) * PREC, gsize, c);
+      float* dst = a.gpart + ((bh * G + h) * ngrp + grp) * PREC;
+      st_dev2(dst + 4 * c, r.A[0], r.A[1]);
+      st_dev2(dst + 4 * c + 2, r.A[2], r.A[3]);
+      if (c == 0) st_dev2(dst + 128, r.M, r.L);
+    }
+    drain_stores();
+    __syncthreads();
+    if (tid == 0) ep->stage = atomicAdd(a.cnt_top + bh, 1u) == static_cast<unsigned>(ngrp - 1) ? 2 : 0;
+    __syncthreads();
+    if (ep->stage != 2) return;
+  }
   // R_eff^T operands for this wave's output coordinates k = 32 wave + 16 nt + col
   bf16x8 th[2][4], tl[2][4];
 #pragma unroll
@@ -579,51 +751,26 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
       tl[nt][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_lo + k * D + 32 * g + 8 * kb));
     }
   }
-  __syncthreads();  // every wave is done with the tables
-  float* mrg = reinterpret_cast<float*>(smem);
-  float* amat = mrg + 4 * 16 * PREC;  // [16][QS] merged rotated sums (rows >= G zero)
-  float* st = amat + 16 * QS;         // [16][4] m, l
-  float* rec = mrg + (wave * 16 + col) * PREC;
-#pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rec[16 * mt + 4 * g + i] = acc[mt][i];
-  if (g == 0) {
-    rec[128] = m_run;
-    rec[129] = l_tot;
-    rec[130] = s_run;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < 16 * D; idx += 256) {
-    const int h = idx / D, j = idx % D;
-    if (h >= G) {
-      amat[h * QS + j] = 0.f;
-      continue;
-    }
-    float M = NEG_BIG;
-    for (int w = 0; w < 4; ++w)
-      for (int c = 0; c < TPD; ++c) M = fmaxf(M, mrg[(w * 16 + c * G + h) * PREC + 128]);
-    float Ls = 0.f, A = 0.f;
-    for (int w = 0; w < 4; ++w)
-      for (int c = 0; c < TPD; ++c) {
-        const float* r = mrg + (w * 16 + c * G + h) * PREC;
-        const float e = exp2f(r[128] - M);
-        Ls += r[129] * e;
-        A += r[j] * (r[130] * e);
+  {
+    const float* src = ngrp == 1 ? a.part : a.gpart;
+    const int count = ngrp == 1 ? ns : ngrp;
+    for (int idx = tid; idx < G * 32; idx += 256) {
+      const int h = idx >> 5, c = idx & 31;
+      const Merged r = merge_chunk(src + (bh * G + h) * count * PREC, count, c);
+      *reinterpret_cast<f32x4*>(&ep->amat[h][4 * c]) = r.A;
+      if (c == 0) {
+        ep->st[h][0] = r.M;
+        ep->st[h][1] = r.L;
       }
-    amat[h * QS + j] = A;
-    if (j == 0) {
-      st[4 * h + 0] = M;
-      st[4 * h + 1] = Ls;
     }
+    __syncthreads();
   }
-  __syncthreads();
-  // U[h][k] = sum_j A[h][j] R_eff[j][k]: rows = q-heads, columns = this wave's k
+  // U[h][k] = sum_j A[h][j] R_eff[j][k]: rows = q-heads (rows >= G are not used), columns = k
   f32x4 u[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     float v[8];
-    const float* src = amat + col * QS + 32 * g + 8 * kb;
+    const float* src = &ep->amat[col][32 * g + 8 * kb];
     *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
     *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
     bf16x8 ph, pm, pl;
@@ -642,69 +789,12 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * g + i;
     if (h >= G) continue;
-    float* out = a.part + (((int64_t)b * Hq + kvh * G + h) * a.n_slices + blockIdx.x) * PREC;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) out[32 * wave + 16 * nt + col] = u[nt][i];
-  }
-  if (tid < G) {
-    float* out = a.part + (((int64_t)b * Hq + kvh * G + tid) * a.n_slices + blockIdx.x) * PREC;
-    out[128] = st[4 * tid + 0];
-    out[129] = st[4 * tid + 1];
-  }
-}
-
-// ---- merge over slices ---------------------------------------------------------------------------
-// One workgroup per (batch row, q-head): log-sum-exp weights of the slices, then the
-// weighted sum of their (already unrotated) value sums.
-constexpr int MAX_SLICES = 1024;
-
-struct MergeArgs {
-  const float* part;
-  float* out;
-  int n_slices;
-};
-
-__device__ float block_reduce(float v, float* red, bool is_max) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float w = __shfl_xor(v, o);
-    v = is_max ? fmaxf(v, w) : v + w;
-  }
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = red[0];
-  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
-  return r;
-}
-
-__global__ void __launch_bounds__(256) merge_kernel(MergeArgs a) {
-  __shared__ float wa[MAX_SLICES];
-  __shared__ float red[4];
-  __shared__ float half_sum[D];
-  const int tid = threadIdx.x;
-  const int64_t head = blockIdx.x;
-  const float* base = a.part + head * a.n_slices * PREC;
-  float m = NEG_BIG;
-  for (int s = tid; s < a.n_slices; s += 256) m = fmaxf(m, base[s * PREC + 128]);
-  const float M = block_reduce(m, red, true);
-  float l = 0.f;
-  for (int s = tid; s < a.n_slices; s += 256) {
-    const float e = exp2f(base[s * PREC + 128] - M);
-    l += base[s * PREC + 129] * e;
-    wa[s] = e;
-  }
-  const float L = block_reduce(l, red, false);  // also orders the wa writes before the reads
-  const int k = tid & (D - 1), hf = tid >> 7;
-  float acc = 0.f;
-#pragma unroll 8
-  for (int s = hf; s < a.n_slices; s += 2) acc = fmaf(wa[s], base[s * PREC + k], acc);
-  if (hf == 1) half_sum[k] = acc;
-  __syncthreads();
-  if (hf == 0) {
-    acc += half_sum[k];
+    const float L = ep->st[h][1];
     // value centroids enter as c / sqrt(d)
-    a.out[head * D + k] = L > 0.f ? acc / L * INV_SQRT_D : 0.f;
+    const float f = L > 0.f ? INV_SQRT_D / L : 0.f;
+    float* o = a.out + (bh * G + h) * D;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) o[32 * wave + 16 * nt + col] = u[nt][i] * f;
   }
 }
 
@@ -827,15 +917,18 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   const int target_wg = wg_per_cu * device_cu_count();
   int n_slices = (target_wg + units - 1) / units;
   const int max_slices = std::max(1, (nblk_max + 4 * MIN_BLOCKS_PER_WAVE - 1) / (4 * MIN_BLOCKS_PER_WAVE));
-  n_slices = std::max(1, std::min(n_slices, max_slices));
+  n_slices = std::max(1, std::min({n_slices, max_slices, MAX_SLICES}));
   const int bpw = (nblk_max + 4 * n_slices - 1) / (4 * n_slices);
   n_slices = (nblk_max + 4 * bpw - 1) / (4 * bpw);
-  if (n_slices > MAX_SLICES) return fail(TQ_ERR_UNSUPPORTED, "context split exceeds the merge limit");
 
   const size_t qrec_bytes = align256(static_cast<size_t>(B) * Hq * QREC * sizeof(_Float16));
   const size_t rt_bytes = 2 * D * D * sizeof(uint16_t);
+  const int n_mgroups = (n_slices + MGROUP - 1) / MGROUP;
+  const size_t cnt_bytes = align256(static_cast<size_t>(B) * cache->Hkv * (MAX_GROUPS + 1) * sizeof(unsigned));
   const size_t part_bytes = align256(static_cast<size_t>(B) * Hq * n_slices * PREC * sizeof(float));
-  const size_t need = qrec_bytes + rt_bytes + part_bytes;
+  const size_t gpart_bytes =
+      n_mgroups > 1 ? align256(static_cast<size_t>(B) * Hq * n_mgroups * PREC * sizeof(float)) : 0;
+  const size_t need = qrec_bytes + rt_bytes + cnt_bytes + part_bytes + gpart_bytes;
   if (workspace == nullptr) {
     *workspace_bytes = need;
     return TQ_OK;
@@ -849,11 +942,17 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   _Float16* qrec = reinterpret_cast<_Float16*>(workspace);
   uint16_t* rt = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(workspace) + qrec_bytes);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + qrec_bytes + rt_bytes);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  unsigned* cnt_grp = reinterpret_cast<unsigned*>(ws + qrec_bytes + rt_bytes);
+  unsigned* cnt_top = cnt_grp + static_cast<size_t>(B) * cache->Hkv * MAX_GROUPS;
+  float* part = reinterpret_cast<float*>(ws + qrec_bytes + rt_bytes + cnt_bytes);
+  float* gpart = n_mgroups > 1 ? reinterpret_cast<float*>(ws + qrec_bytes + rt_bytes + cnt_bytes + part_bytes)
+                               : nullptr;
   if (scale == 0.f) scale = INV_SQRT_D;
 
   const int n_groups = B * cache->Hkv;
-  PrologueArgs pa{q, p->r_hi, p->r_lo, cb->cfg.k_qjl ? p->s_qjl : nullptr, qrec, rt, rt + D * D, G, n_groups};
+  PrologueArgs pa{q, p->r_hi, p->r_lo, cb->cfg.k_qjl ? p->s_qjl : nullptr, qrec, rt, rt + D * D, cnt_grp, cnt_top,
+                  G, n_groups};
   const size_t plds = std::max<size_t>(16 * QS * sizeof(float), D * 136 * sizeof(uint16_t));
   if (q_dtype == TQ_DTYPE_F32)
     hipLaunchKernelGGL(prologue_kernel<true>, dim3(n_groups + 2), dim3(256), plds, s, pa);
@@ -874,6 +973,10 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   ma.rt_hi = rt;
   ma.rt_lo = rt + D * D;
   ma.part = part;
+  ma.gpart = gpart;
+  ma.cnt_grp = cnt_grp;
+  ma.cnt_top = cnt_top;
+  ma.out = out;
   ma.scores_out = scores_out;
   ma.Hkv = cache->Hkv;
   ma.T_cap = cache->T_cap;
@@ -894,10 +997,5 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   }
   e = dispatch_main(ma, cb->cfg, G, n_slices, B, s, e0, e1);
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("attention launch: ") + hipGetErrorString(e));
-
-  MergeArgs mg{part, out, n_slices};
-  hipLaunchKernelGGL(merge_kernel, dim3(B * Hq), dim3(256), 0, s, mg);
-  e = hipGetLastError();
-  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("merge launch: ") + hipGetErrorString(e));
   return TQ_OK;
 }

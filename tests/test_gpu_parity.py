@@ -151,6 +151,39 @@ def test_attention_ragged_lengths(preset, G):
             assert np.all(scores[b, hs, lens[b]:] == 0)
 
 
+@pytest.mark.parametrize("B,G,T_cap,lens", [(2, 8, 10240, [10240, 3001]), (1, 4, 262144, [262144 - 37])])
+def test_attention_merge_levels(B, G, T_cap, lens):
+    """Context splits over several merge groups: 20 slices (groups of 16 and 4, the second row
+    leaving most slices empty) and the maximum of 512 slices (32 groups).  A second call with
+    the same workspace must give identical outputs (the arrival counters are reset per call)."""
+    preset, Hkv = "turbo3", 1
+    cb, dp, cache = _setup(preset, B, Hkv, T_cap)
+    rng = np.random.default_rng(13)
+    K = wl.round_to_bf16(rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32) * 2)
+    V = wl.round_to_bf16(rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32))
+    Q = wl.round_to_bf16(rng.standard_normal((B, Hkv * G, 128)).astype(np.float32))
+    say("merge-levels", B, G, T_cap, "quantize")
+    tq.tq_quantize_kv(cb, dp, cache, H.to_device(K, "bf16"), H.to_device(V, "bf16"),
+                      torch.zeros(B, dtype=torch.int32, device="cuda"))
+    del K, V
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((B, Hkv * G, T_cap), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tq.attend_workspace_bytes(cb, dp, cache, Hkv * G, T_cap), dtype=torch.uint8, device="cuda")
+    qd = H.to_device(Q, "bf16")
+    say("merge-levels", B, G, T_cap, "attend x2")
+    out1 = tq.tq_attend_decode(cb, dp, cache, qd, seq, T_cap, scores_out=scores, workspace=ws).clone()
+    out2 = tq.tq_attend_decode(cb, dp, cache, qd, seq, T_cap, workspace=ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out1.cpu().numpy(), out2.cpu().numpy())
+    hc, out, scores = H.cache_host(cache), out1.cpu().numpy(), scores.cpu().numpy()
+    orc = H.make_oracle(preset)
+    for b in range(B):
+        kg = H.unpack_keys(orc, hc, b, 0, lens[b])
+        vg = H.unpack_values(orc, hc, b, 0, lens[b])
+        e = H.compare_attention(orc, Q[b], kg, vg, lens[b], out[b], scores[b])
+        say("merge-levels", b, lens[b], e)
+
+
 def test_special_vectors():
     """Zero vectors, one-hot vectors, huge and tiny magnitudes, fp32 inputs."""
     preset = "turbo3"
