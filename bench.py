@@ -42,7 +42,43 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=4, help="eager passes over the layers for kernel timing")
     ap.add_argument("--workload", default="c2_llama8b_layer_t32k",
                     help="workload name (default: the Llama-3.1-8B decode layer); others are for exploration")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (calibrates the HBM byte counters) and exit")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attend_kernel.json")
+ATTEND_SOURCE = os.path.join(ROOT, "kv_cache_vector_tq_amd", "csrc", "tq_attend.hip")
+
+
+def measured_traffic(workload: str, preset: str):
+    """HBM bytes per launch of the attention kernel from the committed counter summary (FETCH_SIZE
+    and WRITE_SIZE, each scaled by the same counter's reading for a copy of known size), or None
+    when there is none for this workload or the kernel source changed since it was taken."""
+    import hashlib
+
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        digest = hashlib.sha256(open(ATTEND_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    for e in rec.get("entries", []):
+        if e.get("workload") == workload and e.get("preset") == preset and e.get("source_sha256") == digest:
+            return float(e["hbm_bytes_per_launch"])
+    return None
+
+
+def copy_probe(mib: int):
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
 
 
 def log(*a):
@@ -56,6 +92,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
 
     import torch
 
@@ -118,7 +158,7 @@ def main():
     outs = [torch.empty((B, Hq, 128), dtype=torch.float32, device=dev) for _ in range(L)]
     start = torch.full((B,), T - 1, dtype=torch.int32, device=dev)
     seq = torch.full((B,), T, dtype=torch.int32, device=dev)
-    ws = torch.empty(tq.attend_workspace_bytes(cb, dp, caches[0], Hq, T), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(tq.attend_workspace_bytes(cb, dp, caches[0], Hq, T), dtype=torch.uint8, device=dev)
 
     def step():
         for l in range(L):
@@ -187,7 +227,7 @@ def main():
                    "head_dim": 128, "context": T, "layers": L, "bytes_per_key": bytes_per_key,
                    "step": "per layer: quantize-on-write of 1 new token (K+V) then decode attention"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name, args.preset),
                      "kernel": "attend_kernel (main decode attention)", "bytes_per_launch": bytes_per_launch,
                      "avg_launch_us": kern_s * 1e6},
         "cpu_baseline": cpu,

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 1
+#define TQ_ABI_VERSION 2
 #define TQ_HEAD_DIM 128
 #define TQ_BLOCK_TOKENS 64
 
@@ -76,13 +76,33 @@ typedef struct tq_codebook {
   double v_mse;
 } tq_codebook;
 
-/* Device copies of the bf16 matrices written by tq_build_codebook (row-major d x d,
- * bf16 bit patterns).  The rotation applied is R_eff = r_hi + r_lo (y = R_eff x); the
- * sketch is s_qjl (u = s_qjl r).  s_qjl may be NULL when keys carry no sketch. */
+/* Parameter matrices, row-major d x d, bf16 bit patterns, all derived from cfg->seed:
+ *   r_hi, r_lo    the rotation R_eff = r_hi + r_lo (y = R_eff x);
+ *   s_qjl         the sketch S_b (u = S_b r);
+ *   rt_hi, rt_lo  r_hi and r_lo transposed (the unrotation R_eff^T of attention outputs);
+ *   m_hi, m_lo    M = S_b R_eff (exact product, then m_hi = bf16(M), m_lo = bf16(M - m_hi)):
+ *                 a query's sketch coordinates S_b (R_eff q) in one product.
+ * tq_host_params: caller-allocated host buffers of 16384 uint16 each (any may be NULL to
+ * skip it).  tq_dev_params: device copies (16-byte aligned).  s_qjl, m_hi and m_lo may be NULL
+ * when keys carry no sketch; rt_hi, rt_lo, m_hi and m_lo are read only by tq_attend_decode. */
+typedef struct tq_host_params {
+  uint16_t* r_hi;
+  uint16_t* r_lo;
+  uint16_t* s_qjl;
+  uint16_t* rt_hi;
+  uint16_t* rt_lo;
+  uint16_t* m_hi;
+  uint16_t* m_lo;
+} tq_host_params;
+
 typedef struct tq_dev_params {
   const uint16_t* r_hi;
   const uint16_t* r_lo;
   const uint16_t* s_qjl;
+  const uint16_t* rt_hi;
+  const uint16_t* rt_lo;
+  const uint16_t* m_hi;
+  const uint16_t* m_lo;
 } tq_dev_params;
 
 /* Packed cache of B batch rows x Hkv kv-heads x T_cap token slots (T_cap a multiple of 64).
@@ -127,17 +147,15 @@ typedef struct tq_cache_sizes {
 } tq_cache_sizes;
 
 /* One-time parameter build, host only, deterministic in cfg->seed.
- * Fills *cb with the key and value codebooks (Lloyd-Max fixed point for N(0,1)).  Writes
- * the bf16 bit patterns of R_hi, R_lo and S_b (row-major 128 x 128, caller-allocated host
- * buffers of 16384 uint16 each; any of the three may be NULL to skip it):
+ * Fills *cb with the key and value codebooks (Lloyd-Max fixed point for N(0,1)) and, when
+ * out is not NULL, the parameter matrices of tq_host_params:
  *   G = 128x128 N(0,1) from SplitMix64 started at state 2*seed (Box-Muller, row-major);
  *   R = Q diag(sign U_ii) from the Householder QR G = Q U (a Haar rotation);
  *   R_hi = bf16(R), R_lo = bf16(R - R_hi), bf16() = round to fp32 then to bf16, ties to even;
  *   S_b = bf16(S), S = 128x128 N(0,1) from the stream started at 2*seed + 1.
  * Errors: TQ_ERR_INVALID (NULL cfg/cb), TQ_ERR_UNSUPPORTED (d != 128, k_bits outside 0..4,
  * v_bits outside 1..4, k_qjl not 0/1, or k_bits == 0 with k_qjl == 0). */
-int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, uint16_t* r_hi, uint16_t* r_lo,
-                      uint16_t* s_qjl);
+int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, tq_host_params* out);
 
 /* Sizes of the cache arrays for B x Hkv x T_cap slots (T_cap a positive multiple of 64).
  * Errors: TQ_ERR_INVALID (bad sizes / NULL), TQ_ERR_UNSUPPORTED (bad config). */
@@ -164,7 +182,7 @@ int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, const void* k,
 
 /* One decode step of attention for all (batch row, q-head) straight from the packed cache.
  * q: device [B][Hq][128] in q_dtype.  q-head h reads kv-head h / (Hq / Hkv); Hq / Hkv must
- *   be 1, 2, 4, 8 or 16.
+ *   be 4, 8 or 16.
  * seq_len: device int32 [B], keys 0 .. seq_len[b]-1 are attended (1 <= seq_len[b] <= max_seq_len;
  *   values outside that range are clamped into it on the device).
  * max_seq_len: host bound on seq_len (<= T_cap); sizes the split of the context.
@@ -175,7 +193,10 @@ int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, const void* k,
  *   out = R_eff^T sum_i p_i nv_i cv[codev_i]/sqrt(d)   (fp32 [B][Hq][128]).
  * scores_out: NULL or device fp32 [B][Hq][T_cap]; receives scale * score_i for i < seq_len[b].
  * workspace: device scratch of *workspace_bytes bytes (256-byte aligned).  Call with
- *   workspace == NULL to get the required size in *workspace_bytes (returns TQ_OK).
+ *   workspace == NULL to get the required size in *workspace_bytes (returns TQ_OK).  It must
+ *   be zero-filled before its first use (it holds arrival counters); every call leaves the
+ *   counters zero again, so a workspace is reused without clearing.  Calls that share a
+ *   workspace must not run concurrently (same stream, or ordered).
  * Errors: TQ_ERR_INVALID (NULL arguments, Hq not a multiple of Hkv, max_seq_len outside
  *   1..T_cap), TQ_ERR_UNSUPPORTED (group size or config), TQ_ERR_WORKSPACE (too small;
  *   required size written to *workspace_bytes), TQ_ERR_DEVICE (launch failure). */
@@ -186,7 +207,8 @@ int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_
 
 /* Diagnostic timing hook (for benchmarks): events (hipEvent_t, created by the caller) that
  * later calls on this thread record on their stream, attend_* immediately before and after
- * the main attention kernel of tq_attend_decode (not its query prologue or merge) and
+ * the attention kernel of tq_attend_decode (its only launch: query rotation, scores, softmax,
+ * value sums, merge over context slices and unrotation) and
  * quant_* before the first and after the last kernel of tq_quantize_kv.  NULL disables a
  * pair.  The events are only recorded; the caller reads them after synchronizing.  Returns
  * TQ_OK. */

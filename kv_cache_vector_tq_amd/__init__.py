@@ -13,8 +13,8 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import _lib
-from ._lib import (BLOCK_TOKENS, HEAD_DIM, TQ_DTYPE_BF16, TQ_DTYPE_F32, TQCacheSizes, TQCodebook,
-                   TQConfig, TQDevParams, TQError, TQKVCache, check, lib)
+from ._lib import (BLOCK_TOKENS, HEAD_DIM, PARAM_NAMES, TQ_DTYPE_BF16, TQ_DTYPE_F32, TQCacheSizes, TQCodebook,
+                   TQConfig, TQDevParams, TQError, TQHostParams, TQKVCache, check, lib)
 
 PRESETS = {"turbo3": (2, 1, 3), "turbo4": (3, 1, 4), "qjl1": (0, 1, 3)}
 
@@ -44,11 +44,16 @@ def tq_profile_events(attend=None, quant=None):
 
 @dataclass
 class Codebook:
-    """Host result of tq_build_codebook: the C struct plus the bf16 bit patterns of R_hi, R_lo, S_b."""
+    """Host result of tq_build_codebook: the C struct plus the bf16 bit patterns of the parameter
+    matrices (R_hi, R_lo, S_b, R_hi^T, R_lo^T, M_hi, M_lo; 128 x 128 uint16 each)."""
     cb: TQCodebook
     r_hi: np.ndarray
     r_lo: np.ndarray
     s_qjl: np.ndarray
+    rt_hi: np.ndarray
+    rt_lo: np.ndarray
+    m_hi: np.ndarray
+    m_lo: np.ndarray
 
     @property
     def cfg(self) -> TQConfig:
@@ -74,14 +79,10 @@ def _config(k_bits, k_qjl, v_bits, seed) -> TQConfig:
 def tq_build_codebook(k_bits: int, k_qjl: int, v_bits: int, seed: int = 0) -> Codebook:
     cfg = _config(k_bits, k_qjl, v_bits, seed)
     cb = TQCodebook()
-    n = HEAD_DIM * HEAD_DIM
-    r_hi = np.zeros(n, dtype=np.uint16)
-    r_lo = np.zeros(n, dtype=np.uint16)
-    s_b = np.zeros(n, dtype=np.uint16)
-    check(lib.tq_build_codebook(ctypes.byref(cfg), ctypes.byref(cb), r_hi.ctypes.data, r_lo.ctypes.data,
-                                s_b.ctypes.data), "tq_build_codebook")
-    return Codebook(cb, r_hi.reshape(HEAD_DIM, HEAD_DIM), r_lo.reshape(HEAD_DIM, HEAD_DIM),
-                    s_b.reshape(HEAD_DIM, HEAD_DIM))
+    mats = {n: np.zeros((HEAD_DIM, HEAD_DIM), dtype=np.uint16) for n in PARAM_NAMES}
+    hp = TQHostParams(*(mats[n].ctypes.data for n in PARAM_NAMES))
+    check(lib.tq_build_codebook(ctypes.byref(cfg), ctypes.byref(cb), ctypes.byref(hp)), "tq_build_codebook")
+    return Codebook(cb, **mats)
 
 
 def tq_cache_layout(k_bits: int, k_qjl: int, v_bits: int, B: int, Hkv: int, T_cap: int) -> dict:
@@ -92,7 +93,7 @@ def tq_cache_layout(k_bits: int, k_qjl: int, v_bits: int, B: int, Hkv: int, T_ca
 
 
 class DeviceParams:
-    """Device copies (torch int16 storage) of R_hi, R_lo and S_b."""
+    """Device copies (torch int16 storage) of the parameter matrices."""
 
     def __init__(self, codebook: Codebook, device):
         import torch
@@ -100,10 +101,10 @@ class DeviceParams:
         def up(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
 
-        self.r_hi = up(codebook.r_hi)
-        self.r_lo = up(codebook.r_lo)
-        self.s_qjl = up(codebook.s_qjl)
-        self.struct = TQDevParams(self.r_hi.data_ptr(), self.r_lo.data_ptr(), self.s_qjl.data_ptr())
+        self.mats = {n: up(getattr(codebook, n)) for n in PARAM_NAMES}
+        for n, t in self.mats.items():
+            setattr(self, n, t)
+        self.struct = TQDevParams(*(self.mats[n].data_ptr() for n in PARAM_NAMES))
 
 
 def upload_params(codebook: Codebook, device="cuda") -> DeviceParams:
@@ -175,6 +176,7 @@ def tq_quantize_kv(codebook: Codebook, params: DeviceParams, cache: KVCache, k, 
 
 def attend_workspace_bytes(codebook: Codebook, params: DeviceParams, cache: KVCache, Hq: int,
                            max_seq_len: int) -> int:
+    """Bytes of attention workspace; allocate it zero-filled (torch.zeros) and reuse it."""
     n = ctypes.c_size_t(0)
     # a workspace query needs no device data; dummy non-NULL pointers satisfy the argument check
     check(lib.tq_attend_decode(ctypes.byref(codebook.cb), ctypes.byref(params.struct), ctypes.byref(cache.struct),
@@ -198,7 +200,8 @@ def tq_attend_decode(codebook: Codebook, params: DeviceParams, cache: KVCache, q
         out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     need = attend_workspace_bytes(codebook, params, cache, Hq, max_seq_len)
     if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zero-filled once: the kernel keeps its arrival counters there and leaves them zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     n = ctypes.c_size_t(workspace.numel())
     check(lib.tq_attend_decode(ctypes.byref(codebook.cb), ctypes.byref(params.struct), ctypes.byref(cache.struct),
                                q.data_ptr(), _dtype_code(q), Hq, seq_len.data_ptr(), max_seq_len, float(scale),

@@ -42,7 +42,14 @@ class TQCodebook(ctypes.Structure):
 
 
 class TQDevParams(ctypes.Structure):
-    _fields_ = [("r_hi", ctypes.c_void_p), ("r_lo", ctypes.c_void_p), ("s_qjl", ctypes.c_void_p)]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("r_hi", "r_lo", "s_qjl", "rt_hi", "rt_lo", "m_hi", "m_lo")]
+
+
+class TQHostParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("r_hi", "r_lo", "s_qjl", "rt_hi", "rt_lo", "m_hi", "m_lo")]
+
+
+PARAM_NAMES = ("r_hi", "r_lo", "s_qjl", "rt_hi", "rt_lo", "m_hi", "m_lo")
 
 
 class TQKVCache(ctypes.Structure):
@@ -74,7 +81,7 @@ def _load():
     lib.tq_last_error.restype = ctypes.c_char_p
     lib.tq_last_error.argtypes = []
     lib.tq_build_codebook.restype = ctypes.c_int
-    lib.tq_build_codebook.argtypes = [P(TQConfig), P(TQCodebook), vp, vp, vp]
+    lib.tq_build_codebook.argtypes = [P(TQConfig), P(TQCodebook), P(TQHostParams)]
     lib.tq_cache_layout.restype = ctypes.c_int
     lib.tq_cache_layout.argtypes = [P(TQConfig), ctypes.c_int, ctypes.c_int, ctypes.c_int, P(TQCacheSizes)]
     lib.tq_quantize_kv.restype = ctypes.c_int

@@ -10,10 +10,11 @@
 //   score_i = n_i (sum_j q1_j c[code_ij]/sqrt(d) + rnorm_i sqrt(pi/2)/m sum_j q2_j (2 sign_ij - 1));
 //   p = softmax(scale * score);  out = R_eff^T sum_i p_i nv_i cv[codev_i] / sqrt(d).
 //
-// Two launches on the caller's stream:
-//  1. prologue: q1, q2 per (batch row, q-head), stored as f16 with a power-of-two scale;
-//  2. main: one workgroup of 4 waves per (batch row, kv-head, context slice); each wave
-//     streams 64-key blocks of its sub-slice.  Codes are turned into f16 MFMA operands by
+// One launch on the caller's stream: one workgroup of 4 waves per (batch row, kv-head,
+// context slice).  The workgroup first computes q1, q2 of its G q-heads (MFMA, staged in LDS
+// and turned into f16 operands with a power-of-two scale) while the decode tables are built
+// and its first code block is in flight; then each wave streams the 64-key blocks of its
+// sub-slice.  Codes are turned into f16 MFMA operands by
 //     table lookups in LDS (4 or 8 codes per lookup); keys sit on the M side of the score
 //     MFMAs (one key read serves all G q-heads of the group), the softmax weights of a
 //     score tile feed the value MFMA directly from the accumulator layout, and the value
@@ -40,7 +41,6 @@ namespace {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float KAPPA = 0.009791666936874390f;  // sqrt(pi/2)/128
 constexpr float NEG_BIG = -1.0e30f;
-constexpr int QREC = 288;   // f16 elements per prologue record: q1[128], q2[128], scales
 constexpr int PREC = 132;   // floats per partial record: sums[128], m, l, scale, pad
 constexpr int MGROUP = 16;                       // slices per first-level merge group
 constexpr int MAX_GROUPS = 32;                   // merge groups per (batch row, kv-head)
@@ -173,187 +173,130 @@ __device__ __forceinline__ void load_dwords(uint32_t* dst, const uint8_t* src) {
     *reinterpret_cast<u32x4*>(dst + 4 * i) = *reinterpret_cast<const u32x4*>(src + 16 * i);
 }
 
-// ---- prologue ------------------------------------------------------------------------------
-// One workgroup per (batch row, kv-head) computes q1 = R_eff q and q2 = S_b q1 for the G
-// (<= 16) q-heads of the group as two 16x16x32 bf16 MFMA products: the q-heads are the M
-// rows, the wave's 32 output coordinates the N columns; operands are split into exact bf16
-// terms (fp32 q and q1 into three, R_eff into hi + lo), so products are exact and sums are
-// fp32.  Two extra workgroups write R_hi^T and R_lo^T into the workspace for the
-// unrotation at the end of the main kernel.
-constexpr int QS = 132;  // LDS row stride (floats) of q1
+// ---- query rotation ---------------------------------------------------------------------------
+// At its start every workgroup computes, for the G (<= 16) q-heads of its kv-head,
+// q1 = R_eff q and q2 = S_b q1 = M q (M = S_b R_eff, given as the bf16 pair m_hi + m_lo) as
+// 16x16x32 bf16 MFMA products: the q-heads are the M rows, the wave's 32 output coordinates
+// the N columns.  A bf16 query is exact in one bf16 term and an fp32 query is split into
+// three, so the products are exact and the sums fp32.  The results are staged in LDS with
+// each head's largest magnitude, from which the f16 MFMA operands of the score products get
+// a power-of-two scale.
+constexpr int QS = 132;  // LDS row stride (floats) of q1 and q2
 
-struct PrologueArgs {
-  const void* q;
-  const uint16_t* r_hi;
-  const uint16_t* r_lo;
-  const uint16_t* s_b;  // may be NULL (no sketch)
-  _Float16* qrec;       // [B*Hq][QREC]
-  uint16_t* rt_hi;      // [128][128] R_hi^T
-  uint16_t* rt_lo;      // [128][128] R_lo^T
-  unsigned* cnt_grp;    // merge counters of the main kernel, zeroed here
-  unsigned* cnt_top;
-  int G, n_groups;
+struct QStage {
+  float q1[16][QS];
+  float q2[16][QS];
+  unsigned mx[2][16];  // largest |q1|, |q2| of each head (fp32 bit patterns)
 };
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
 }
 
-// dst = src^T for a 128x128 bf16 matrix, through an LDS tile of row stride 136 (16-byte
-// aligned rows): 16-byte loads and stores, 8 per thread, all issued before any use.
-__device__ void transpose_matrix(uint16_t* dst, const uint16_t* src, uint16_t* tile) {
-  constexpr int TS = 136;
-  u16x8 v[8];
+// Operands of one lane: rows o = 32 wave + 16 nt + col of R_hi, R_lo, M_hi, M_lo (k-slots
+// 32 g + 8 kb + e) and the raw words of the query of head col at the same coordinates
+// (8 x 16 bytes for fp32, the first 4 x 16 bytes for bf16).  Everything is loaded in one
+// batch; the query is converted only when first used.
+template <bool QJL>
+struct QOperands {
+  bf16x8 rh[2][4], rl[2][4], mh[QJL ? 2 : 1][4], ml[QJL ? 2 : 1][4];
+  u32x4 raw[8];
+  bool valid;  // col < G
+};
+
+template <bool QJL>
+__device__ __forceinline__ void load_query_operands(QOperands<QJL>& o, const void* q, bool q_f32, int64_t head0,
+                                                    int G, const uint16_t* r_hi, const uint16_t* r_lo,
+                                                    const uint16_t* m_hi, const uint16_t* m_lo, int wave, int col,
+                                                    int g) {
 #pragma unroll
-  for (int r = 0; r < 8; ++r) v[r] = *reinterpret_cast<const u16x8*>(src + 8 * (threadIdx.x + 256 * r));
+  for (int nt = 0; nt < 2; ++nt) {
+    const int row = 32 * wave + 16 * nt + col;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int idx8 = threadIdx.x + 256 * r;
-    const int i = (8 * idx8) / D, k0 = (8 * idx8) % D;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tile[(k0 + e) * TS + i] = v[r][e];
+    for (int kb = 0; kb < 4; ++kb) {
+      o.rh[nt][kb] = load_bf16x8(r_hi + row * D + 32 * g + 8 * kb);
+      o.rl[nt][kb] = load_bf16x8(r_lo + row * D + 32 * g + 8 * kb);
+      if constexpr (QJL) {
+        o.mh[nt][kb] = load_bf16x8(m_hi + row * D + 32 * g + 8 * kb);
+        o.ml[nt][kb] = load_bf16x8(m_lo + row * D + 32 * g + 8 * kb);
+      }
+    }
   }
-  __syncthreads();
+  // unconditional loads from clamped, in-bounds addresses (no branch that would force an
+  // early wait); lanes of rows >= G and the unused chunks of a bf16 query are masked on use
+  const int esz = q_f32 ? 4 : 2;
+  o.valid = col < G;
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(q) + ((head0 + (o.valid ? col : 0)) * D + 32 * g) * esz;
+  const int last = q_f32 ? 7 : 3;  // last 16-byte chunk of this lane's 32 coordinates
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int idx8 = threadIdx.x + 256 * r;
-    const int k = (8 * idx8) / D, i0 = (8 * idx8) % D;
-    *reinterpret_cast<u16x8*>(dst + 8 * idx8) = *reinterpret_cast<const u16x8*>(tile + k * TS + i0);
+  for (int i = 0; i < 8; ++i) o.raw[i] = *reinterpret_cast<const u32x4*>(base + 16 * min(i, last));
+}
+
+// Largest |v| over the 16 lanes of a row group, folded into *dst (LDS) by the group's lane 0.
+__device__ __forceinline__ void row_absmax(float v, unsigned* dst, int col) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  if (col == 0) atomicMax(dst, __float_as_uint(v));
+}
+
+// Accumulates the products of one k-block for both output tiles: q1 += a (r_hi + r_lo),
+// q2 += a (m_hi + m_lo).
+template <bool QJL>
+__device__ __forceinline__ void rotate_step(const QOperands<QJL>& o, int kb, bf16x8 a, f32x4* d1, f32x4* d2) {
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    d1[nt] = mfma_bf16(a, o.rh[nt][kb], d1[nt]);
+    d1[nt] = mfma_bf16(a, o.rl[nt][kb], d1[nt]);
+    if constexpr (QJL) {
+      d2[nt] = mfma_bf16(a, o.mh[nt][kb], d2[nt]);
+      d2[nt] = mfma_bf16(a, o.ml[nt][kb], d2[nt]);
+    }
   }
 }
 
-template <bool F32>
-__global__ void __launch_bounds__(256) prologue_kernel(PrologueArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float psm[];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 15, g = lane >> 4;
-  if (blockIdx.x >= a.n_groups) {  // two extra workgroups write R_hi^T and R_lo^T
-    uint16_t* tile = reinterpret_cast<uint16_t*>(psm);
-    if (blockIdx.x == a.n_groups)
-      transpose_matrix(a.rt_hi, a.r_hi, tile);
-    else
-      transpose_matrix(a.rt_lo, a.r_lo, tile);
-    return;
-  }
-  float* q1s = psm;  // [16][QS]
-  __shared__ unsigned int mx[2][16];
-  if (tid < MAX_GROUPS) a.cnt_grp[blockIdx.x * MAX_GROUPS + tid] = 0u;
-  if (tid == MAX_GROUPS) a.cnt_top[blockIdx.x] = 0u;
-  const int G = a.G;
-  const bool sketch = a.s_b != nullptr;
-  const int64_t head0 = (int64_t)blockIdx.x * G;
-
-  // operands of this wave's output rows o = 32 wave + 16 nt + col
-  bf16x8 rh[2][4], rl[2][4], sb[2][4];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int o = 32 * wave + 16 * nt + col;
+// q1 and q2 into qs (rows >= G hold zeros).  qs->mx must be zero before the first barrier
+// inside; ends with a barrier.
+template <bool QJL>
+__device__ void rotate_queries(const QOperands<QJL>& o, bool q_f32, QStage* qs, int wave, int col, int g) {
+  f32x4 d1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 d2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  if (q_f32) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      rh[nt][kb] = load_bf16x8(a.r_hi + o * D + 32 * g + 8 * kb);
-      rl[nt][kb] = load_bf16x8(a.r_lo + o * D + 32 * g + 8 * kb);
-      sb[nt][kb] = sketch ? load_bf16x8(a.s_b + o * D + 32 * g + 8 * kb) : bf16x8{};
-    }
-  }
-  if (tid < 32) mx[tid >> 4][tid & 15] = 0u;
-  // A operand: q-head h = col (rows >= G are zero)
-  const int hA = col;
-  f32x4 d1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      float x[8];
+      const u32x4 lo = o.raw[2 * kb], hi = o.raw[2 * kb + 1];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (hA < G) {
-      if constexpr (F32) {
-        const float* src = reinterpret_cast<const float*>(a.q) + (head0 + hA) * D + 32 * g + 8 * kb;
-        *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
-        *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
-      } else {
-        const u16x8 x = *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(a.q) + (head0 + hA) * D +
-                                                        32 * g + 8 * kb);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = bf2f(x[e]);
+      for (int e = 0; e < 4; ++e) {
+        x[e] = o.valid ? __uint_as_float(lo[e]) : 0.f;
+        x[4 + e] = o.valid ? __uint_as_float(hi[e]) : 0.f;
       }
+      bf16x8 ph, pm, pl;
+      split3_bf16(x, ph, pm, pl);
+      rotate_step<QJL>(o, kb, ph, d1, d2);
+      rotate_step<QJL>(o, kb, pm, d1, d2);
+      rotate_step<QJL>(o, kb, pl, d1, d2);
     }
-    bf16x8 ph, pm, pl;
-    split3_bf16(v, ph, pm, pl);
+  } else {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      d1[nt] = mfma_bf16(ph, rh[nt][kb], d1[nt]);
-      d1[nt] = mfma_bf16(ph, rl[nt][kb], d1[nt]);
-      d1[nt] = mfma_bf16(pm, rh[nt][kb], d1[nt]);
-      d1[nt] = mfma_bf16(pm, rl[nt][kb], d1[nt]);
-      if constexpr (F32) {
-        d1[nt] = mfma_bf16(pl, rh[nt][kb], d1[nt]);
-        d1[nt] = mfma_bf16(pl, rl[nt][kb], d1[nt]);
-      }
-    }
+    for (int kb = 0; kb < 4; ++kb)
+      rotate_step<QJL>(o, kb, o.valid ? __builtin_bit_cast(bf16x8, o.raw[kb]) : zero, d1, d2);
   }
   __syncthreads();  // mx cleared
-  // D layout: lane (col, g) holds q-head 4 g + i, output coordinate 32 wave + 16 nt + col
+  // D layout: lane (col, g) holds head 4 g + i, output coordinate 32 wave + 16 nt + col
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float m = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      q1s[(4 * g + i) * QS + 32 * wave + 16 * nt + col] = d1[nt][i];
-      m = fmaxf(m, fabsf(d1[nt][i]));
+      qs->q1[4 * g + i][32 * wave + 16 * nt + col] = d1[nt][i];
+      if constexpr (QJL) qs->q2[4 * g + i][32 * wave + 16 * nt + col] = d2[nt][i];
     }
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    m = fmaxf(m, __shfl_xor(m, 8));
-    if (col == 0) atomicMax(&mx[0][4 * g + i], __float_as_uint(m));
+    row_absmax(fmaxf(fabsf(d1[0][i]), fabsf(d1[1][i])), &qs->mx[0][4 * g + i], col);
+    if constexpr (QJL) row_absmax(fmaxf(fabsf(d2[0][i]), fabsf(d2[1][i])), &qs->mx[1][4 * g + i], col);
   }
   __syncthreads();
-  f32x4 d2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  if (sketch) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float v[8];
-      const float* src = q1s + hA * QS + 32 * g + 8 * kb;
-      *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
-      *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
-      bf16x8 ph, pm, pl;
-      split3_bf16(v, ph, pm, pl);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        d2[nt] = mfma_bf16(ph, sb[nt][kb], d2[nt]);
-        d2[nt] = mfma_bf16(pm, sb[nt][kb], d2[nt]);
-        d2[nt] = mfma_bf16(pl, sb[nt][kb], d2[nt]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float m = fmaxf(fabsf(d2[0][i]), fabsf(d2[1][i]));
-      m = fmaxf(m, __shfl_xor(m, 1));
-      m = fmaxf(m, __shfl_xor(m, 2));
-      m = fmaxf(m, __shfl_xor(m, 4));
-      m = fmaxf(m, __shfl_xor(m, 8));
-      if (col == 0) atomicMax(&mx[1][4 * g + i], __float_as_uint(m));
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * g + i;
-    if (h >= G) continue;
-    const float m1 = __uint_as_float(mx[0][h]), m2 = __uint_as_float(mx[1][h]);
-    int e1 = 0, e2 = 0;
-    if (m1 > 0.f) frexpf(m1, &e1);
-    if (m2 > 0.f) frexpf(m2, &e2);
-    _Float16* rec = a.qrec + (head0 + h) * QREC;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int o = 32 * wave + 16 * nt + col;
-      rec[o] = static_cast<_Float16>(ldexpf(d1[nt][i], -e1));
-      rec[D + o] = static_cast<_Float16>(ldexpf(d2[nt][i], -e2));
-    }
-    if (wave == 0 && col == 0) {
-      float* sc = reinterpret_cast<float*>(rec + 2 * D);
-      sc[0] = ldexpf(1.0f, e1);
-      sc[1] = ldexpf(1.0f, e2);
-    }
-  }
 }
 
 // ---- main kernel ----------------------------------------------------------------------------
@@ -434,16 +377,20 @@ struct MainArgs {
   const uint8_t* v_codes;
   const float* v_norm;
   const int32_t* seq_len;
-  const _Float16* qrec;
-  const uint16_t* rt_hi;  // R_hi^T, R_lo^T (written by the prologue)
+  const void* q;          // [B*Hq][128] bf16 or fp32 (q_f32)
+  const uint16_t* r_hi;   // R_hi, R_lo, M_hi, M_lo (M_* NULL without a sketch)
+  const uint16_t* r_lo;
+  const uint16_t* m_hi;
+  const uint16_t* m_lo;
+  const uint16_t* rt_hi;  // R_hi^T, R_lo^T
   const uint16_t* rt_lo;
   float* part;        // [B*Hq][n_slices][PREC]: rotated sums, m, l of each slice
   float* gpart;       // [B*Hq][n_groups][PREC]: the same per group of MGROUP slices
-  unsigned* cnt_grp;  // [B*Hkv][MAX_GROUPS] arrival counters (zeroed by the prologue)
+  unsigned* cnt_grp;  // [B*Hkv][MAX_GROUPS] arrival counters (zero between calls)
   unsigned* cnt_top;  // [B*Hkv]
   float* out;         // [B*Hq][128]
   float* scores_out;  // NULL or [B*Hq][T_cap]
-  int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices;
+  int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices, q_f32;
   float scale_log2;   // scale * log2(e)
   float scale;
   float k_cent[16];
@@ -459,9 +406,11 @@ struct MainCfg {
   static constexpr int STAB = QJL ? SIGN_TABLE_BYTES : 0;
   static constexpr int VTAB = SHARED ? 0 : Dec<VB>::LDS_BYTES;
   static constexpr int TABLES = KTAB + STAB + VTAB;
-  // the epilogue reuses the table space once every wave has left the block loop
+  static constexpr int QSTAGE = TABLES;  // QStage follows the tables
+  static constexpr int FRONT = TABLES + static_cast<int>(sizeof(QStage));
+  // the epilogue reuses the space once every wave has left the block loop
   static constexpr int MERGE = static_cast<int>(sizeof(Epi));
-  static constexpr int LDS = TABLES > MERGE ? TABLES : MERGE;
+  static constexpr int LDS = FRONT > MERGE ? FRONT : MERGE;
 };
 
 #ifndef ATTN_MIN_WG
@@ -485,20 +434,6 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   const int Hq = a.Hkv * G;
   const int64_t bh = (int64_t)b * a.Hkv + kvh;
   const int nblk_cap = a.T_cap / 64;
-
-  // query operands: lane (col, g) holds q[hh][32 g + 8 kb + e] of every k-block kb
-  const _Float16* qr = a.qrec + ((int64_t)b * Hq + kvh * G + hh) * QREC;
-  f16x8 bq[4], bs[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    bq[kb] = *reinterpret_cast<const f16x8*>(qr + 32 * g + 8 * kb);
-    bs[kb] = *reinterpret_cast<const f16x8*>(qr + D + 32 * g + 8 * kb);
-  }
-  // logit * log2(e) = n (code_acc * c1 + rnorm * sign_acc * c2): the table holds centroids c,
-  // the key term is q1 . c / sqrt(d), the sign term carries sqrt(pi/2)/m
-  const float lscale = a.scale * LOG2E;
-  const float c1 = reinterpret_cast<const float*>(qr + 2 * D)[0] * INV_SQRT_D * lscale;
-  const float c2 = reinterpret_cast<const float*>(qr + 2 * D)[1] * KAPPA * lscale;
 
   int seq = a.seq_len[b];
   seq = seq < 1 ? 1 : (seq > a.max_seq_len ? a.max_seq_len : seq);
@@ -540,13 +475,56 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
       d.vn[s] = *reinterpret_cast<const f32x4*>(a.v_norm + tok);
     }
   };
+  QStage* qs = reinterpret_cast<QStage*>(smem + C::QSTAGE);
+  if (tid < 32) qs->mx[tid >> 4][tid & 15] = 0u;
+  QOperands<QJL> qo;
+  load_query_operands<QJL>(qo, a.q, a.q_f32 != 0, (int64_t)b * Hq + kvh * G, G, a.r_hi, a.r_lo, a.m_hi, a.m_lo,
+                           wave, col, g);
   Blk cur, nxt;
   if (blk_begin < blk_end) load_block(blk_begin, cur);  // in flight while the tables are built
 
   if constexpr (KB > 0) build_code_table<(KB > 0 ? KB : 1)>(ktab, a.k_cent, tid);
   if constexpr (QJL) build_sign_table(stab, tid);
   if constexpr (!C::SHARED) build_code_table<VB>(vtab, a.v_cent, tid);
-  __syncthreads();  // tables ready
+  rotate_queries<QJL>(qo, a.q_f32 != 0, qs, wave, col, g);  // its barriers also publish the tables
+
+  // score operands: lane (col, g) holds q[hh][32 g + 8 kb + e] of every k-block kb, in f16
+  // scaled by a power of two.  logit * log2(e) = n (code_acc * c1 + rnorm * sign_acc * c2):
+  // the table holds centroids c, the key term is q1 . c / sqrt(d), the sign term carries
+  // sqrt(pi/2)/m.
+  f16x8 bq[4], bs[4];
+  float c1, c2;
+  {
+    int e1 = 0, e2 = 0;
+    const float m1 = __uint_as_float(qs->mx[0][hh]), m2 = __uint_as_float(qs->mx[1][hh]);
+    if (m1 > 0.f) frexpf(m1, &e1);
+    if (QJL && m2 > 0.f) frexpf(m2, &e2);
+    const float s1 = ldexpf(1.0f, -e1), s2 = ldexpf(1.0f, -e2);  // exact powers of two
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&qs->q1[hh][32 * g + 8 * kb]);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&qs->q1[hh][32 * g + 8 * kb + 4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bq[kb][e] = static_cast<_Float16>(a0[e] * s1);
+        bq[kb][4 + e] = static_cast<_Float16>(a1[e] * s1);
+      }
+      if constexpr (QJL) {
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&qs->q2[hh][32 * g + 8 * kb]);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&qs->q2[hh][32 * g + 8 * kb + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bs[kb][e] = static_cast<_Float16>(b0[e] * s2);
+          bs[kb][4 + e] = static_cast<_Float16>(b1[e] * s2);
+        }
+      } else {
+        bs[kb] = f16x8{};
+      }
+    }
+    const float lscale = a.scale * LOG2E;
+    c1 = ldexpf(1.0f, e1) * INV_SQRT_D * lscale;
+    c2 = ldexpf(1.0f, e2) * KAPPA * lscale;
+  }
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
     Norms nrm;
@@ -713,12 +691,13 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   drain_stores();
   __syncthreads();
   if (tid == 0) {
+    // the last arrival resets its counter, so counters are zero again after every call
     int stage = 0;
-    if (ngrp == 1) {
-      stage = atomicAdd(a.cnt_top + bh, 1u) == static_cast<unsigned>(ns - 1) ? 2 : 0;
-    } else {
-      const int gsize = min(MGROUP, ns - MGROUP * grp);
-      stage = atomicAdd(a.cnt_grp + bh * MAX_GROUPS + grp, 1u) == static_cast<unsigned>(gsize - 1) ? 1 : 0;
+    unsigned* cnt = ngrp == 1 ? a.cnt_top + bh : a.cnt_grp + bh * MAX_GROUPS + grp;
+    const unsigned last = ngrp == 1 ? ns - 1 : min(MGROUP, ns - MGROUP * grp) - 1;
+    if (atomicAdd(cnt, 1u) == last) {
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      stage = ngrp == 1 ? 2 : 1;
     }
     ep->stage = stage;
   }
@@ -736,7 +715,13 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
     }
     drain_stores();
     __syncthreads();
-    if (tid == 0) ep->stage = atomicAdd(a.cnt_top + bh, 1u) == static_cast<unsigned>(ngrp - 1) ? 2 : 0;
+    if (tid == 0) {
+      ep->stage = 0;
+      if (atomicAdd(a.cnt_top + bh, 1u) == static_cast<unsigned>(ngrp - 1)) {
+        __hip_atomic_store(a.cnt_top + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ep->stage = 2;
+      }
+    }
     __syncthreads();
     if (ep->stage != 2) return;
   }
@@ -904,7 +889,8 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
                 "and Hq/Hkv in {4, 8, 16}");
   if (max_seq_len < 1 || max_seq_len > cache->T_cap) return fail(TQ_ERR_INVALID, "max_seq_len must be in 1..T_cap");
   if (q_dtype != TQ_DTYPE_BF16 && q_dtype != TQ_DTYPE_F32) return fail(TQ_ERR_UNSUPPORTED, "query dtype");
-  if (p->r_hi == nullptr || p->r_lo == nullptr || (cb->cfg.k_qjl && p->s_qjl == nullptr))
+  if (p->r_hi == nullptr || p->r_lo == nullptr || p->rt_hi == nullptr || p->rt_lo == nullptr ||
+      (cb->cfg.k_qjl && (p->m_hi == nullptr || p->m_lo == nullptr)))
     return fail(TQ_ERR_INVALID, "device parameter matrices missing");
   if (!aligned(out, 4) || (scores_out && !aligned(scores_out, 4)) || !aligned(q, q_dtype == TQ_DTYPE_F32 ? 4 : 2))
     return fail(TQ_ERR_INVALID, "misaligned q / out / scores_out");
@@ -921,14 +907,12 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   const int bpw = (nblk_max + 4 * n_slices - 1) / (4 * n_slices);
   n_slices = (nblk_max + 4 * bpw - 1) / (4 * bpw);
 
-  const size_t qrec_bytes = align256(static_cast<size_t>(B) * Hq * QREC * sizeof(_Float16));
-  const size_t rt_bytes = 2 * D * D * sizeof(uint16_t);
   const int n_mgroups = (n_slices + MGROUP - 1) / MGROUP;
   const size_t cnt_bytes = align256(static_cast<size_t>(B) * cache->Hkv * (MAX_GROUPS + 1) * sizeof(unsigned));
   const size_t part_bytes = align256(static_cast<size_t>(B) * Hq * n_slices * PREC * sizeof(float));
   const size_t gpart_bytes =
       n_mgroups > 1 ? align256(static_cast<size_t>(B) * Hq * n_mgroups * PREC * sizeof(float)) : 0;
-  const size_t need = qrec_bytes + rt_bytes + cnt_bytes + part_bytes + gpart_bytes;
+  const size_t need = cnt_bytes + part_bytes + gpart_bytes;
   if (workspace == nullptr) {
     *workspace_bytes = need;
     return TQ_OK;
@@ -940,26 +924,13 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   if (!aligned(workspace, 256)) return fail(TQ_ERR_INVALID, "workspace must be 256-byte aligned");
 
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  _Float16* qrec = reinterpret_cast<_Float16*>(workspace);
-  uint16_t* rt = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(workspace) + qrec_bytes);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  unsigned* cnt_grp = reinterpret_cast<unsigned*>(ws + qrec_bytes + rt_bytes);
+  unsigned* cnt_grp = reinterpret_cast<unsigned*>(ws);
   unsigned* cnt_top = cnt_grp + static_cast<size_t>(B) * cache->Hkv * MAX_GROUPS;
-  float* part = reinterpret_cast<float*>(ws + qrec_bytes + rt_bytes + cnt_bytes);
-  float* gpart = n_mgroups > 1 ? reinterpret_cast<float*>(ws + qrec_bytes + rt_bytes + cnt_bytes + part_bytes)
+  float* part = reinterpret_cast<float*>(ws + cnt_bytes);
+  float* gpart = n_mgroups > 1 ? reinterpret_cast<float*>(ws + cnt_bytes + part_bytes)
                                : nullptr;
   if (scale == 0.f) scale = INV_SQRT_D;
-
-  const int n_groups = B * cache->Hkv;
-  PrologueArgs pa{q, p->r_hi, p->r_lo, cb->cfg.k_qjl ? p->s_qjl : nullptr, qrec, rt, rt + D * D, cnt_grp, cnt_top,
-                  G, n_groups};
-  const size_t plds = std::max<size_t>(16 * QS * sizeof(float), D * 136 * sizeof(uint16_t));
-  if (q_dtype == TQ_DTYPE_F32)
-    hipLaunchKernelGGL(prologue_kernel<true>, dim3(n_groups + 2), dim3(256), plds, s, pa);
-  else
-    hipLaunchKernelGGL(prologue_kernel<false>, dim3(n_groups + 2), dim3(256), plds, s, pa);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("prologue launch: ") + hipGetErrorString(e));
 
   MainArgs ma{};
   ma.k_codes = cache->k_codes;
@@ -969,9 +940,14 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   ma.v_codes = cache->v_codes;
   ma.v_norm = cache->v_norm;
   ma.seq_len = seq_len;
-  ma.qrec = qrec;
-  ma.rt_hi = rt;
-  ma.rt_lo = rt + D * D;
+  ma.q = q;
+  ma.q_f32 = q_dtype == TQ_DTYPE_F32 ? 1 : 0;
+  ma.r_hi = p->r_hi;
+  ma.r_lo = p->r_lo;
+  ma.m_hi = cb->cfg.k_qjl ? p->m_hi : nullptr;
+  ma.m_lo = cb->cfg.k_qjl ? p->m_lo : nullptr;
+  ma.rt_hi = p->rt_hi;
+  ma.rt_lo = p->rt_lo;
   ma.part = part;
   ma.gpart = gpart;
   ma.cnt_grp = cnt_grp;
@@ -995,7 +971,7 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
     e0 = reinterpret_cast<hipEvent_t>(pe.attend_start);
     e1 = reinterpret_cast<hipEvent_t>(pe.attend_stop);
   }
-  e = dispatch_main(ma, cb->cfg, G, n_slices, B, s, e0, e1);
+  const hipError_t e = dispatch_main(ma, cb->cfg, G, n_slices, B, s, e0, e1);
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("attention launch: ") + hipGetErrorString(e));
   return TQ_OK;
 }

@@ -214,8 +214,7 @@ int tq_profile_events(void* attend_start, void* attend_stop, void* quant_start, 
 
 const char* tq_last_error(void) { return tq::g_last_error.c_str(); }
 
-int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, uint16_t* r_hi, uint16_t* r_lo,
-                      uint16_t* s_qjl) {
+int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, tq_host_params* out) {
   tq::clear_error();
   if (cfg == nullptr || cb == nullptr) return tq::fail(TQ_ERR_INVALID, "cfg and cb must not be NULL");
   int rc = tq::check_config(*cfg);
@@ -234,21 +233,37 @@ int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, uint16_t* r_hi, uin
   for (int l = 0; l + 1 < (1 << cfg->v_bits); ++l) cb->v_thresholds[l] = static_cast<float>(t[l]);
   cb->v_mse = mse;
 
+  if (out == nullptr) return TQ_OK;
   const int d = cfg->d;
-  if (r_hi != nullptr || r_lo != nullptr) {
-    std::vector<double> G(static_cast<size_t>(d) * d), R(static_cast<size_t>(d) * d);
-    gaussian_fill(2ull * cfg->seed, G.data(), d * d);
-    haar_rotation(G.data(), R.data(), d);
-    for (int i = 0; i < d * d; ++i) {
-      const uint16_t hi = to_bf16(R[i]);
-      if (r_hi) r_hi[i] = hi;
-      if (r_lo) r_lo[i] = to_bf16(R[i] - from_bf16(hi));
+  const size_t n = static_cast<size_t>(d) * d;
+  std::vector<double> G(n), R(n), Reff(n), S(n), Sb(n);
+  gaussian_fill(2ull * cfg->seed, G.data(), d * d);
+  haar_rotation(G.data(), R.data(), d);
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j) {
+      const double r = R[static_cast<size_t>(i) * d + j];
+      const uint16_t hi = to_bf16(r), lo = to_bf16(r - from_bf16(hi));
+      Reff[static_cast<size_t>(i) * d + j] = from_bf16(hi) + from_bf16(lo);
+      if (out->r_hi) out->r_hi[i * d + j] = hi;
+      if (out->r_lo) out->r_lo[i * d + j] = lo;
+      if (out->rt_hi) out->rt_hi[j * d + i] = hi;
+      if (out->rt_lo) out->rt_lo[j * d + i] = lo;
     }
+  gaussian_fill(2ull * cfg->seed + 1ull, S.data(), d * d);
+  for (size_t i = 0; i < n; ++i) {
+    const uint16_t b = to_bf16(S[i]);
+    Sb[i] = from_bf16(b);
+    if (out->s_qjl) out->s_qjl[i] = b;
   }
-  if (s_qjl != nullptr) {
-    std::vector<double> S(static_cast<size_t>(d) * d);
-    gaussian_fill(2ull * cfg->seed + 1ull, S.data(), d * d);
-    for (int i = 0; i < d * d; ++i) s_qjl[i] = to_bf16(S[i]);
+  if (out->m_hi || out->m_lo) {
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j) {
+        double m = 0.0;  // M = S_b R_eff, every product exact in fp64 (8 x 16 significant bits)
+        for (int k = 0; k < d; ++k) m += Sb[static_cast<size_t>(i) * d + k] * Reff[static_cast<size_t>(k) * d + j];
+        const uint16_t hi = to_bf16(m);
+        if (out->m_hi) out->m_hi[i * d + j] = hi;
+        if (out->m_lo) out->m_lo[i * d + j] = to_bf16(m - from_bf16(hi));
+      }
   }
   return TQ_OK;
 }

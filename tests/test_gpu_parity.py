@@ -168,7 +168,7 @@ def test_attention_merge_levels(B, G, T_cap, lens):
     del K, V
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     scores = torch.zeros((B, Hkv * G, T_cap), dtype=torch.float32, device="cuda")
-    ws = torch.empty(tq.attend_workspace_bytes(cb, dp, cache, Hkv * G, T_cap), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(tq.attend_workspace_bytes(cb, dp, cache, Hkv * G, T_cap), dtype=torch.uint8, device="cuda")
     qd = H.to_device(Q, "bf16")
     say("merge-levels", B, G, T_cap, "attend x2")
     out1 = tq.tq_attend_decode(cb, dp, cache, qd, seq, T_cap, scores_out=scores, workspace=ws).clone()

@@ -11,7 +11,7 @@ import kv_cache_vector_tq_amd as tq
 from kv_cache_vector_tq_amd import _lib
 from oracle import layout
 from oracle.lloyd_max import codebook_f32
-from oracle.params import build_params
+from oracle.params import bf16_bits, bf16_value, build_params
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert tq.tq_abi_version() == 1
+    assert tq.tq_abi_version() == 2
 
 
 @pytest.mark.parametrize("preset", ["turbo3", "turbo4", "qjl1"])
@@ -47,7 +47,15 @@ def test_parameter_build_matches_oracle_bit_for_bit(preset, seed):
     p = build_params(seed)
     np.testing.assert_array_equal(cb.r_hi, p["r_hi"])
     np.testing.assert_array_equal(cb.r_lo, p["r_lo"])
+    np.testing.assert_array_equal(cb.rt_hi, p["r_hi"].T)
+    np.testing.assert_array_equal(cb.rt_lo, p["r_lo"].T)
     np.testing.assert_array_equal(cb.s_qjl, p["s_b"])
+    # M = S_b R_eff as a bf16 pair: hi is M rounded to bf16, and hi + lo is within 2^-16 |M|
+    # (two bf16 terms of 8 significant bits each)
+    M = p["S_b"] @ p["R_eff"]
+    np.testing.assert_array_equal(cb.m_hi, bf16_bits(M))
+    pair = bf16_value(cb.m_hi) + bf16_value(cb.m_lo)
+    assert np.all(np.abs(pair - M) <= 2.0 ** -16 * np.abs(M) + 1e-30)
     vc, vt, vmse = codebook_f32(vb)
     np.testing.assert_array_equal(cb.v_centroids(), vc)
     np.testing.assert_array_equal(cb.v_thresholds(), vt)
@@ -71,9 +79,9 @@ def test_bad_configs_rejected(bad):
 def test_bad_head_dim_rejected():
     cfg = _lib.TQConfig(64, 2, 1, 3, 0)
     cb = _lib.TQCodebook()
-    assert _lib.lib.tq_build_codebook(ctypes.byref(cfg), ctypes.byref(cb), None, None, None) == _lib.TQ_ERR_UNSUPPORTED
+    assert _lib.lib.tq_build_codebook(ctypes.byref(cfg), ctypes.byref(cb), None) == _lib.TQ_ERR_UNSUPPORTED
     assert b"d = 128" in _lib.lib.tq_last_error()
-    assert _lib.lib.tq_build_codebook(None, ctypes.byref(cb), None, None, None) == _lib.TQ_ERR_INVALID
+    assert _lib.lib.tq_build_codebook(None, ctypes.byref(cb), None) == _lib.TQ_ERR_INVALID
 
 
 @pytest.mark.parametrize("preset", ["turbo3", "turbo4", "qjl1"])
@@ -105,7 +113,7 @@ def _quantize_rc(cb, cache, **kw):
     args = dict(k=1 << 12, v=1 << 13, dtype=_lib.TQ_DTYPE_BF16, B=1, Hkv=1, n_new=1, sb=128, sh=128, st=128,
                 start=1 << 14)
     args.update(kw)
-    params = _lib.TQDevParams(1 << 15, 1 << 16, 1 << 17)
+    params = _lib.TQDevParams(1 << 15, 1 << 16, 1 << 17, 1 << 18, 1 << 19, 1 << 20, 1 << 21)
     return _lib.lib.tq_quantize_kv(ctypes.byref(cb.cb), ctypes.byref(params), args["k"], args["v"], args["dtype"],
                                    args["B"], args["Hkv"], args["n_new"], args["sb"], args["sh"], args["st"],
                                    args["start"], ctypes.byref(cache.struct), None)
@@ -130,9 +138,10 @@ def test_quantize_rejects_bad_cache():
     assert _quantize_rc(cb, cache) == _lib.TQ_ERR_INVALID
 
 
-def _attend_rc(cb, cache, Hq=4, max_seq=64, ws=None, ws_bytes=None):
+def _attend_rc(cb, cache, Hq=4, max_seq=64, ws=None, ws_bytes=None, params=None):
     n = ctypes.c_size_t(0 if ws_bytes is None else ws_bytes)
-    params = _lib.TQDevParams(1 << 15, 1 << 16, 1 << 17)
+    if params is None:
+        params = _lib.TQDevParams(1 << 15, 1 << 16, 1 << 17, 1 << 18, 1 << 19, 1 << 20, 1 << 21)
     rc = _lib.lib.tq_attend_decode(ctypes.byref(cb.cb), ctypes.byref(params), ctypes.byref(cache.struct), 1 << 12,
                                    _lib.TQ_DTYPE_F32, Hq, 1 << 13, max_seq, 0.0, 1 << 14, None, ws, ctypes.byref(n),
                                    None)
@@ -150,3 +159,6 @@ def test_attend_workspace_query_and_checks():
     assert _attend_rc(cb, cache, Hq=2 * 3)[0] == _lib.TQ_ERR_UNSUPPORTED  # group of 3
     assert _attend_rc(cb, cache, Hq=8, max_seq=0)[0] == _lib.TQ_ERR_INVALID
     assert _attend_rc(cb, cache, Hq=8, max_seq=4097)[0] == _lib.TQ_ERR_INVALID
+    # the transposed rotation halves are required
+    no_rt = _lib.TQDevParams(1 << 15, 1 << 16, 1 << 17, None, 1 << 19, 1 << 20, 1 << 21)
+    assert _attend_rc(cb, cache, Hq=8, max_seq=4096, params=no_rt)[0] == _lib.TQ_ERR_INVALID
