@@ -36,21 +36,25 @@ __device__ __forceinline__ float bf2f(uint16_t b) {
   return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
 }
 
-// Exact split of 8 fp32 values into three bf16 terms: x = hi + mid + lo.  Each stage
-// rounds to 8 significant bits and its remainder is exact in fp32 (Sterbenz), so the
-// last remainder has at most 8 significant bits and fits bf16 exactly.
+// Exact split of 8 fp32 values into three bf16 terms: x = hi + mid + lo.  hi is x truncated
+// to its top 16 bits (a bf16 value); the remainder x - hi is exact in fp32 and has at most
+// 16 significant bits; mid is that remainder truncated the same way, and the last remainder
+// has at most 8 significant bits, so it is a bf16 value too.  Each pair of terms is packed
+// from the high halves of two fp32 words with one byte permute.
 __device__ __forceinline__ void split3_bf16(const float* v, bf16x8& hi, bf16x8& mid, bf16x8& lo) {
-  u16x8 h, m, l;
+  u32x4 h, m, l;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = v[e];
-    const uint16_t bh = f2bf(x);
-    const float r1 = x - bf2f(bh);
-    const uint16_t bm = f2bf(r1);
-    const float r2 = r1 - bf2f(bm);
-    h[e] = bh;
-    m[e] = bm;
-    l[e] = f2bf(r2);
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t x0 = __float_as_uint(v[2 * p]), x1 = __float_as_uint(v[2 * p + 1]);
+    const float r0 = v[2 * p] - __uint_as_float(x0 & 0xFFFF0000u);
+    const float r1 = v[2 * p + 1] - __uint_as_float(x1 & 0xFFFF0000u);
+    const uint32_t y0 = __float_as_uint(r0), y1 = __float_as_uint(r1);
+    const float s0 = r0 - __uint_as_float(y0 & 0xFFFF0000u);
+    const float s1 = r1 - __uint_as_float(y1 & 0xFFFF0000u);
+    // bytes 2, 3 of the second operand, then bytes 2, 3 of the first: {a.hi16, b.hi16}
+    h[p] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+    m[p] = __builtin_amdgcn_perm(y1, y0, 0x07060302u);
+    l[p] = __builtin_amdgcn_perm(__float_as_uint(s1), __float_as_uint(s0), 0x07060302u);
   }
   hi = __builtin_bit_cast(bf16x8, h);
   mid = __builtin_bit_cast(bf16x8, m);

@@ -76,6 +76,7 @@ struct Smem {
   uint8_t sgn[64 * IDX_STRIDE];
   float norm[64];
   float rnorm[64];
+  float zs[64];  // sqrt(d) / norm (0 for a zero row)
 };
 
 // Rotation (hi, lo) and sketch operands of one wave: lane (col, grp) holds row
@@ -157,7 +158,11 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
     }
     ss += __shfl_xor(ss, 1);
     ss += __shfl_xor(ss, 2);
-    if (q == 0) s_norm[row] = mx > 0.f ? ldexpf(sqrtf(ss), ex) : 0.f;
+    if (q == 0) {
+      const float n = mx > 0.f ? ldexpf(sqrtf(ss), ex) : 0.f;
+      s_norm[row] = n;
+      sm.zs[row] = n > 0.f ? SQRT_D / n : 0.f;
+    }
   }
   __syncthreads();
 
@@ -209,16 +214,15 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   // ---- scale, scalar code, residual -------------------------------------------------------
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
+    // z = sqrt(d) y = acc sqrt(d) / n for the lane's rows 16 mt + 4 grp + i
+    const f32x4 zsv = *reinterpret_cast<const f32x4*>(sm.zs + 16 * mt + 4 * grp);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * mt + 4 * grp + i;
-      const float n = s_norm[row];
-      const float inv = n > 0.f ? 1.0f / n : 0.f;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int o = 32 * wave + 16 * nt + col;
-        const float y = acc[mt][nt][i] * inv;
-        const float z = y * SQRT_D;
+        const float z = acc[mt][nt][i] * zsv[i];
         float c = 0.f;
         if constexpr (BITS > 0) {
           int idx = 0;
@@ -232,8 +236,9 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
           s_idx[row * IDX_STRIDE + o] = static_cast<uint8_t>(idx);
         }
         if constexpr (KEY && QJL) {
-          float r = (BITS > 0) ? (y - c * INV_SQRT_D) : y;
-          if (!(n > 0.f)) r = 0.f;
+          // r = y - c / sqrt(d) = (z - c) / sqrt(d)
+          float r = ((BITS > 0) ? (z - c) : z) * INV_SQRT_D;
+          if (!(zsv[i] > 0.f)) r = 0.f;
           s_tile[row * XS_F32 + o] = r;
         }
       }
@@ -248,7 +253,10 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
       const float* src = s_tile + row * XS_F32 + 32 * q;
       float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) ss += src[j] * src[j];
+      for (int j = 0; j < 32; j += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(src + j);
+        ss = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], ss))));
+      }
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
       if (q == 0) s_rnorm[row] = s_norm[row] > 0.f ? sqrtf(ss) : 0.f;
@@ -522,7 +530,9 @@ extern "C" int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, con
   const int64_t tiles = 2ll * B * Hkv * q.nblk_max;
   if (tiles > (1ll << 30)) return fail(TQ_ERR_INVALID, "too many tokens in one call");
   q.n_tiles = static_cast<int>(tiles);
-  const int grid = static_cast<int>(std::min<int64_t>(tiles, 3ll * device_cu_count()));
+  // two workgroups per CU are resident (register budget); a larger persistent grid only adds a
+  // late-starting tail
+  const int grid = static_cast<int>(std::min<int64_t>(tiles, 2ll * device_cu_count()));
   const ProfileEvents& pe = profile_events();
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (pe.quant_start && pe.quant_stop) {
