@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--kernel-reps", type=int, default=4, help="eager passes over the layers for kernel timing")
     ap.add_argument("--workload", default="c2_llama8b_layer_t32k",
                     help="workload name (default: the Llama-3.1-8B decode layer); others are for exploration")
+    ap.add_argument("--other-workloads", type=int, default=1,
+                    help="also time the attention kernel and bulk quantize on the other HBM-sized workloads (0: off)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (calibrates the HBM byte counters) and exit")
     return ap.parse_args()
@@ -66,6 +68,110 @@ def measured_traffic(workload: str, preset: str):
         if e.get("workload") == workload and e.get("preset") == preset and e.get("source_sha256") == digest:
             return float(e["hbm_bytes_per_launch"])
     return None
+
+
+OTHER_WORKLOADS = [("c3_batch16_t128k", "turbo3"), ("c4_llama70b_layer_b8_t128k", "qjl1"),
+                   ("c5_moe_attn_t1m", "turbo3"), ("c5_moe_attn_t1m", "turbo4")]
+
+
+def draw_kv(w, dev):
+    """K and V of a workload on the device (bf16/fp32), drawn from the seeded generators."""
+    import torch
+
+    import tq_workloads as wl
+
+    in_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    if w.B * w.Hkv * w.T <= (1 << 19):
+        K = torch.from_numpy(wl.host_tensor(w, wl.TENSOR_K)).to(dev).to(in_dtype)
+        V = torch.from_numpy(wl.host_tensor(w, wl.TENSOR_V)).to(dev).to(in_dtype)
+    else:  # large contexts are drawn on the device, one (b, kv-head) slice at a time
+        K = torch.empty((w.B, w.Hkv, w.T, 128), dtype=in_dtype, device=dev)
+        V = torch.empty((w.B, w.Hkv, w.T, 128), dtype=in_dtype, device=dev)
+        for bb in range(w.B):
+            for hh in range(w.Hkv):
+                wl.device_slice(w, bb, hh, wl.TENSOR_K, out=K[bb, hh])
+                wl.device_slice(w, bb, hh, wl.TENSOR_V, out=V[bb, hh])
+    return K, V
+
+
+def bulk_bytes(B, Hkv, n, kb, kq, vb):
+    k_out = 16 * kb + (16 if kq else 0) + 4 + (4 if (kq and kb) else 0)
+    v_out = 16 * vb + 4
+    return B * Hkv * n * (256 + k_out) + B * Hkv * n * (256 + v_out)
+
+
+def time_workload(name, preset, dev, reps=5):
+    """Attention kernel (HIP events on its stream) and bulk quantize of the full context for one
+    workload: one cache, inputs resident in HBM."""
+    import torch
+
+    import kv_cache_vector_tq_amd as tq
+    import tq_workloads as wl
+
+    w = wl.workload(name)
+    kb, kq, vb = wl.PRESETS[preset]
+    K, V = draw_kv(w, dev)
+    Q = torch.from_numpy(wl.host_tensor(w, wl.TENSOR_Q)).to(dev).to(K.dtype)
+    cb = tq.tq_build_codebook(kb, kq, vb, seed=0)
+    dp = tq.upload_params(cb, dev)
+    cache = tq.KVCache(cb, w.B, w.Hkv, w.T, device=dev, zero=False)
+    zero = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    q_ms = []
+    tq.tq_profile_events(quant=(e0, e1))
+    for _ in range(3):
+        tq.tq_quantize_kv(cb, dp, cache, K, V, zero)
+        torch.cuda.synchronize()
+        q_ms.append(e0.elapsed_time(e1))
+    tq.tq_profile_events()
+    del K, V
+    seq = torch.full((w.B,), w.T, dtype=torch.int32, device=dev)
+    ws = torch.zeros(tq.attend_workspace_bytes(cb, dp, cache, w.Hq, w.T), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device=dev)
+    tq.tq_attend_decode(cb, dp, cache, Q, seq, w.T, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    a_ms = []
+    tq.tq_profile_events(attend=(e0, e1))
+    for _ in range(reps):
+        tq.tq_attend_decode(cb, dp, cache, Q, seq, w.T, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        a_ms.append(e0.elapsed_time(e1))
+    tq.tq_profile_events()
+    a_s = float(np.median(a_ms)) * 1e-3
+    q_s = float(np.median(q_ms[1:])) * 1e-3
+    att_bytes = w.B * w.Hkv * w.T * cache.bytes_per_token
+    qb = bulk_bytes(w.B, w.Hkv, w.T, kb, kq, vb)
+    n_vec = 2 * w.B * w.Hkv * w.T
+    res = {"workload": w.name, "preset": preset,
+           "attend": {"us": a_s * 1e6, "keys_per_s": w.B * w.Hkv * w.T / a_s, "gbs": att_bytes / a_s / 1e9,
+                      "frac": att_bytes / a_s / 1e9 / HBM_PEAK_GBS, "bytes": att_bytes},
+           "bulk_quantize": {"us": q_s * 1e6, "vectors_per_s": n_vec / q_s, "gbs": qb / q_s / 1e9,
+                             "frac": qb / q_s / 1e9 / HBM_PEAK_GBS, "vectors": n_vec}}
+    del cache, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def stream_read_gbs(dev, mib=2048):
+    """Read bandwidth of the box measured with a device-wide reduction over a large buffer."""
+    import torch
+
+    x = torch.ones(mib << 18, dtype=torch.int32, device=dev)
+    x.sum()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(5):
+        x.sum()
+    t1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * x.numel() * 4 / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del x
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def copy_probe(mib: int):
@@ -111,19 +217,9 @@ def main():
 
     # ---- inputs (seeded, synthetic) -------------------------------------------------------------
     log("drawing inputs", w.name)
-    in_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    if B * Hkv * T <= (1 << 19):
-        K = torch.from_numpy(wl.host_tensor(w, wl.TENSOR_K)).to(dev).to(in_dtype)
-        V = torch.from_numpy(wl.host_tensor(w, wl.TENSOR_V)).to(dev).to(in_dtype)
-    else:  # large contexts are drawn on the device, one (b, kv-head) slice at a time
-        K = torch.empty((B, Hkv, T, 128), dtype=in_dtype, device=dev)
-        V = torch.empty((B, Hkv, T, 128), dtype=in_dtype, device=dev)
-        for bb in range(B):
-            for hh in range(Hkv):
-                wl.device_slice(w, bb, hh, wl.TENSOR_K, out=K[bb, hh])
-                wl.device_slice(w, bb, hh, wl.TENSOR_V, out=V[bb, hh])
+    K, V = draw_kv(w, dev)
     Qh = wl.host_tensor(w, wl.TENSOR_Q)
-    Q = torch.from_numpy(Qh).to(dev).to(in_dtype)
+    Q = torch.from_numpy(Qh).to(dev).to(K.dtype)
 
     cb = tq.tq_build_codebook(kb, kq, vb, seed=0)
     dp = tq.upload_params(cb, dev)
@@ -145,9 +241,7 @@ def main():
         bulk_ms.append(qs.elapsed_time(qe))
     tq.tq_profile_events()
     n_vec = 2 * B * Hkv * (T - 1)
-    k_out = 16 * kb + (16 if kq else 0) + 4 + (4 if (kq and kb) else 0)
-    v_out = 16 * vb + 4
-    bulk_bytes = B * Hkv * (T - 1) * (256 + k_out) + B * Hkv * (T - 1) * (256 + v_out)
+    bulk_b = bulk_bytes(B, Hkv, T - 1, kb, kq, vb)
     bulk_s = float(np.median(bulk_ms[1:] if L > 1 else bulk_ms)) * 1e-3
     log(f"bulk quantize: {n_vec} vectors in {bulk_s * 1e6:.1f} us")
 
@@ -205,10 +299,25 @@ def main():
     achieved = bytes_per_launch / kern_s / 1e9
     log(f"attention kernel: {kern_s * 1e6:.2f} us per launch, {achieved:.0f} GB/s")
 
+    # host copy of one (batch row, kv-head) of layer 0 for the oracle on the host cores
+    host = {n: (None if t is None else t[0, 0].cpu().numpy()) for n, t in caches[0].tensors().items()}
+
+    # ---- the other HBM-sized workloads (one cache each; the step's caches are freed first) -------
+    others = []
+    if args.other_workloads:
+        del caches, k_new, v_new, K, V, ws, outs, qs_l, graph
+        torch.cuda.empty_cache()
+        for name, preset in OTHER_WORKLOADS:
+            log("timing", name, preset)
+            others.append(time_workload(name, preset, dev))
+            log(json.dumps(others[-1]))
+    read_gbs = stream_read_gbs(dev)
+    log(f"stream read ceiling {read_gbs:.0f} GB/s")
+
     # ---- oracle on the host cores ----------------------------------------------------------------
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, caches[0], Qh, args.preset, args.cpu_seconds)
+        cpu = cpu_baseline(w, host, Qh, args.preset, args.cpu_seconds)
 
     line = {
         "metric": "compressed-KV decode attention keys/s + achieved HBM GB/s (% of peak) at 3/4 bit",
@@ -232,16 +341,19 @@ def main():
                      "avg_launch_us": kern_s * 1e6},
         "cpu_baseline": cpu,
         "extra": {
+            "attend_frac_of_measured_read": achieved / read_gbs,
+            "measured_read_gbs": read_gbs,
+            "workloads": others,
             "step_gbs": keys_per_step * bytes_per_key / (step_ms * 1e-3) / 1e9,
             "bulk_quantize": {"vectors_per_launch": n_vec, "us_per_launch": bulk_s * 1e6,
-                              "vectors_per_s": n_vec / bulk_s, "gbs": bulk_bytes / bulk_s / 1e9,
-                              "frac": bulk_bytes / bulk_s / 1e9 / HBM_PEAK_GBS},
+                              "vectors_per_s": n_vec / bulk_s, "gbs": bulk_b / bulk_s / 1e9,
+                              "frac": bulk_b / bulk_s / 1e9 / HBM_PEAK_GBS},
         },
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, cache, Qh, preset, seconds):
+def cpu_baseline(w, host, Qh, preset, seconds):
     """The oracle (fp64 NumPy) decoding one (batch row, kv-head) of one layer from its packed cache:
     unpack the codes, then attention of the G q-heads over the full context.  Repeated for
     about `seconds`; reported as keys/s (keys attended per second)."""
@@ -255,7 +367,6 @@ def cpu_baseline(w, cache, Qh, preset, seconds):
         threads = 1
     orc = Oracle(*wl.PRESETS[preset], seed=0)
     T, G = w.T, w.G
-    host = {n: (None if t is None else t[0, 0].cpu().numpy()) for n, t in cache.tensors().items()}
     q = Qh[0, :G].astype(np.float64)
     reps = 0
     t0 = time.perf_counter()
@@ -267,9 +378,23 @@ def cpu_baseline(w, cache, Qh, preset, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    # quantize-on-write: the oracle quantizing the first 2048 keys and values of the same slice
+    xk = wl.host_slice(w, 0, 0, wl.TENSOR_K, n=2048).astype(np.float64)
+    xv = wl.host_slice(w, 0, 0, wl.TENSOR_V, n=2048).astype(np.float64)
+    qreps = 0
+    q0 = time.perf_counter()
+    while True:
+        orc.quantize_keys(xk)
+        orc.quantize_values(xv)
+        qreps += 1
+        qel = time.perf_counter() - q0
+        if qel >= seconds / 4:
+            break
     return {"value": reps * T / el, "unit": "keys/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} decode passes of one (batch row, kv-head) of one layer: unpack + attention of "
-                      f"{G} q-heads over {T} keys, fp64 NumPy ({el:.1f} s)"}
+                      f"{G} q-heads over {T} keys, fp64 NumPy ({el:.1f} s)",
+            "quantize_vectors_per_s": qreps * 4096 / qel,
+            "quantize_sample": f"{qreps} x (2048 keys + 2048 values) of the same slice ({qel:.1f} s)"}
 
 
 if __name__ == "__main__":

@@ -207,8 +207,8 @@ int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_
 
 /* Diagnostic timing hook (for benchmarks): events (hipEvent_t, created by the caller) that
  * later calls on this thread record on their stream, attend_* immediately before and after
- * the attention kernel of tq_attend_decode (its only launch: query rotation, scores, softmax,
- * value sums, merge over context slices and unrotation) and
+ * the main attention kernel of tq_attend_decode (scores, softmax, value sums, merge over
+ * context slices and unrotation; not its query prologue) and
  * quant_* before the first and after the last kernel of tq_quantize_kv.  NULL disables a
  * pair.  The events are only recorded; the caller reads them after synchronizing.  Returns
  * TQ_OK. */

@@ -10,19 +10,19 @@
 //   score_i = n_i (sum_j q1_j c[code_ij]/sqrt(d) + rnorm_i sqrt(pi/2)/m sum_j q2_j (2 sign_ij - 1));
 //   p = softmax(scale * score);  out = R_eff^T sum_i p_i nv_i cv[codev_i] / sqrt(d).
 //
-// One launch on the caller's stream: one workgroup of 4 waves per (batch row, kv-head,
-// context slice).  The workgroup first computes q1, q2 of its G q-heads (MFMA, staged in LDS
-// and turned into f16 operands with a power-of-two scale) while the decode tables are built
-// and its first code block is in flight; then each wave streams the 64-key blocks of its
-// sub-slice.  Codes are turned into f16 MFMA operands by
+// Two launches on the caller's stream:
+//  1. query prologue, one single-wave workgroup per (batch row, kv-head, 32 output
+//     coordinates): q1, q2 of the G q-heads (MFMA), stored as fp32 records;
+//  2. main: one workgroup of 4 waves per (batch row, kv-head, context slice); each wave
+//     streams the 64-key blocks of its sub-slice.  Codes are turned into f16 MFMA operands by
 //     table lookups in LDS (4 or 8 codes per lookup); keys sit on the M side of the score
 //     MFMAs (one key read serves all G q-heads of the group), the softmax weights of a
 //     score tile feed the value MFMA directly from the accumulator layout, and the value
 //     sum stays in the rotated domain.  The 4 waves merge their online-softmax states in
 //     LDS and write one partial per (q-head, slice).  Arrival counters then elect, per
 //     (batch row, kv-head), the last workgroup of each group of 16 slices to merge that
-//     group (log-sum-exp), and the last of those to merge the groups and apply R_eff^T
-//     (exact bf16-split MFMA, fp32 sums) - no separate merge launch.
+//     group (log-sum-exp) and apply R_eff^T to it (exact bf16-split MFMA, fp32 sums), and
+//     the last of those to merge the unrotated group results - no separate merge launch.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
@@ -183,12 +183,6 @@ __device__ __forceinline__ void load_dwords(uint32_t* dst, const uint8_t* src) {
 // a power-of-two scale.
 constexpr int QS = 132;  // LDS row stride (floats) of q1 and q2
 
-struct QStage {
-  float q1[16][QS];
-  float q2[16][QS];
-  unsigned mx[2][16];  // largest |q1|, |q2| of each head (fp32 bit patterns)
-};
-
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
 }
@@ -232,15 +226,6 @@ __device__ __forceinline__ void load_query_operands(QOperands<QJL>& o, const voi
   for (int i = 0; i < 8; ++i) o.raw[i] = *reinterpret_cast<const u32x4*>(base + 16 * min(i, last));
 }
 
-// Largest |v| over the 16 lanes of a row group, folded into *dst (LDS) by the group's lane 0.
-__device__ __forceinline__ void row_absmax(float v, unsigned* dst, int col) {
-  v = fmaxf(v, __shfl_xor(v, 1));
-  v = fmaxf(v, __shfl_xor(v, 2));
-  v = fmaxf(v, __shfl_xor(v, 4));
-  v = fmaxf(v, __shfl_xor(v, 8));
-  if (col == 0) atomicMax(dst, __float_as_uint(v));
-}
-
 // Accumulates the products of one k-block for both output tiles: q1 += a (r_hi + r_lo),
 // q2 += a (m_hi + m_lo).
 template <bool QJL>
@@ -256,12 +241,9 @@ __device__ __forceinline__ void rotate_step(const QOperands<QJL>& o, int kb, bf1
   }
 }
 
-// q1 and q2 into qs (rows >= G hold zeros).  qs->mx must be zero before the first barrier
-// inside; ends with a barrier.
+// d1 += q (R_hi + R_lo), d2 += q (M_hi + M_lo) for the lane's output tiles (all k-blocks).
 template <bool QJL>
-__device__ void rotate_queries(const QOperands<QJL>& o, bool q_f32, QStage* qs, int wave, int col, int g) {
-  f32x4 d1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  f32x4 d2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+__device__ __forceinline__ void rotate_products(const QOperands<QJL>& o, bool q_f32, f32x4* d1, f32x4* d2) {
   const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   if (q_f32) {
 #pragma unroll
@@ -284,19 +266,45 @@ __device__ void rotate_queries(const QOperands<QJL>& o, bool q_f32, QStage* qs, 
     for (int kb = 0; kb < 4; ++kb)
       rotate_step<QJL>(o, kb, o.valid ? __builtin_bit_cast(bf16x8, o.raw[kb]) : zero, d1, d2);
   }
-  __syncthreads();  // mx cleared
+}
+
+// Query prologue: one single-wave workgroup per (batch row, kv-head, 32 output coordinates)
+// writes q1 and q2 (fp32) of the G q-heads into a record per q-head: q1[128], q2[128].
+constexpr int QREC = 2 * D;  // floats per record
+
+struct PrologueArgs {
+  const void* q;  // [B*Hq][128] bf16 or fp32 (q_f32)
+  const uint16_t* r_hi;
+  const uint16_t* r_lo;
+  const uint16_t* m_hi;  // NULL without a sketch
+  const uint16_t* m_lo;
+  float* qrec;  // [B*Hq][QREC]
+  int G, q_f32;
+};
+
+template <bool QJL>
+__global__ void __launch_bounds__(64) prologue_kernel(PrologueArgs a) {
+  const int lane = threadIdx.x, wave = blockIdx.y;  // output coordinates 32 wave .. 32 wave + 31
+  const int col = lane & 15, g = lane >> 4;
+  const int G = a.G;
+  const int64_t head0 = static_cast<int64_t>(blockIdx.x) * G;
+  QOperands<QJL> qo;
+  load_query_operands<QJL>(qo, a.q, a.q_f32 != 0, head0, G, a.r_hi, a.r_lo, a.m_hi, a.m_lo, wave, col, g);
+  f32x4 d1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 d2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  rotate_products<QJL>(qo, a.q_f32 != 0, d1, d2);
   // D layout: lane (col, g) holds head 4 g + i, output coordinate 32 wave + 16 nt + col
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    if (h >= G) continue;
+    float* rec = a.qrec + (head0 + h) * QREC;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      qs->q1[4 * g + i][32 * wave + 16 * nt + col] = d1[nt][i];
-      if constexpr (QJL) qs->q2[4 * g + i][32 * wave + 16 * nt + col] = d2[nt][i];
+      rec[32 * wave + 16 * nt + col] = d1[nt][i];
+      rec[D + 32 * wave + 16 * nt + col] = QJL ? d2[nt][i] : 0.f;
     }
-    row_absmax(fmaxf(fabsf(d1[0][i]), fabsf(d1[1][i])), &qs->mx[0][4 * g + i], col);
-    if constexpr (QJL) row_absmax(fmaxf(fabsf(d2[0][i]), fabsf(d2[1][i])), &qs->mx[1][4 * g + i], col);
   }
-  __syncthreads();
 }
 
 // ---- main kernel ----------------------------------------------------------------------------
@@ -377,11 +385,7 @@ struct MainArgs {
   const uint8_t* v_codes;
   const float* v_norm;
   const int32_t* seq_len;
-  const void* q;          // [B*Hq][128] bf16 or fp32 (q_f32)
-  const uint16_t* r_hi;   // R_hi, R_lo, M_hi, M_lo (M_* NULL without a sketch)
-  const uint16_t* r_lo;
-  const uint16_t* m_hi;
-  const uint16_t* m_lo;
+  const float* qrec;      // [B*Hq][QREC] query records of the prologue
   const uint16_t* rt_hi;  // R_hi^T, R_lo^T
   const uint16_t* rt_lo;
   float* part;        // [B*Hq][n_slices][PREC]: rotated sums, m, l of each slice
@@ -390,7 +394,7 @@ struct MainArgs {
   unsigned* cnt_top;  // [B*Hkv]
   float* out;         // [B*Hq][128]
   float* scores_out;  // NULL or [B*Hq][T_cap]
-  int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices, q_f32;
+  int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices;
   float scale_log2;   // scale * log2(e)
   float scale;
   float k_cent[16];
@@ -406,11 +410,9 @@ struct MainCfg {
   static constexpr int STAB = QJL ? SIGN_TABLE_BYTES : 0;
   static constexpr int VTAB = SHARED ? 0 : Dec<VB>::LDS_BYTES;
   static constexpr int TABLES = KTAB + STAB + VTAB;
-  static constexpr int QSTAGE = TABLES;  // QStage follows the tables
-  static constexpr int FRONT = TABLES + static_cast<int>(sizeof(QStage));
-  // the epilogue reuses the space once every wave has left the block loop
+  // the epilogue reuses the table space once every wave has left the block loop
   static constexpr int MERGE = static_cast<int>(sizeof(Epi));
-  static constexpr int LDS = FRONT > MERGE ? FRONT : MERGE;
+  static constexpr int LDS = TABLES > MERGE ? TABLES : MERGE;
 };
 
 #ifndef ATTN_MIN_WG
@@ -475,56 +477,55 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
       d.vn[s] = *reinterpret_cast<const f32x4*>(a.v_norm + tok);
     }
   };
-  QStage* qs = reinterpret_cast<QStage*>(smem + C::QSTAGE);
-  if (tid < 32) qs->mx[tid >> 4][tid & 15] = 0u;
-  QOperands<QJL> qo;
-  load_query_operands<QJL>(qo, a.q, a.q_f32 != 0, (int64_t)b * Hq + kvh * G, G, a.r_hi, a.r_lo, a.m_hi, a.m_lo,
-                           wave, col, g);
+  // score operands from the prologue's record of head hh: lane (col, g) holds
+  // q[hh][32 g + 8 kb + e] of every k-block kb in f16, scaled by 2^-e with e the exponent of
+  // the vector's largest magnitude (the 4 lanes of a column hold the 128 coordinates).
+  // logit * log2(e) = n (code_acc * c1 + rnorm * sign_acc * c2): the table holds centroids c,
+  // the key term is q1 . c / sqrt(d), the sign term carries sqrt(pi/2)/m.
+  const float* qr = a.qrec + ((int64_t)b * Hq + kvh * G + hh) * QREC;
+  f32x4 qv1[8], qv2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    qv1[i] = *reinterpret_cast<const f32x4*>(qr + 32 * g + 4 * i);
+    qv2[i] = QJL ? *reinterpret_cast<const f32x4*>(qr + D + 32 * g + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   Blk cur, nxt;
   if (blk_begin < blk_end) load_block(blk_begin, cur);  // in flight while the tables are built
 
   if constexpr (KB > 0) build_code_table<(KB > 0 ? KB : 1)>(ktab, a.k_cent, tid);
   if constexpr (QJL) build_sign_table(stab, tid);
   if constexpr (!C::SHARED) build_code_table<VB>(vtab, a.v_cent, tid);
-  rotate_queries<QJL>(qo, a.q_f32 != 0, qs, wave, col, g);  // its barriers also publish the tables
-
-  // score operands: lane (col, g) holds q[hh][32 g + 8 kb + e] of every k-block kb, in f16
-  // scaled by a power of two.  logit * log2(e) = n (code_acc * c1 + rnorm * sign_acc * c2):
-  // the table holds centroids c, the key term is q1 . c / sqrt(d), the sign term carries
-  // sqrt(pi/2)/m.
   f16x8 bq[4], bs[4];
   float c1, c2;
   {
-    int e1 = 0, e2 = 0;
-    const float m1 = __uint_as_float(qs->mx[0][hh]), m2 = __uint_as_float(qs->mx[1][hh]);
-    if (m1 > 0.f) frexpf(m1, &e1);
-    if (QJL && m2 > 0.f) frexpf(m2, &e2);
-    const float s1 = ldexpf(1.0f, -e1), s2 = ldexpf(1.0f, -e2);  // exact powers of two
+    float m1 = 0.f, m2 = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&qs->q1[hh][32 * g + 8 * kb]);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&qs->q1[hh][32 * g + 8 * kb + 4]);
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        bq[kb][e] = static_cast<_Float16>(a0[e] * s1);
-        bq[kb][4 + e] = static_cast<_Float16>(a1[e] * s1);
+        m1 = fmaxf(m1, fabsf(qv1[i][e]));
+        m2 = fmaxf(m2, fabsf(qv2[i][e]));
       }
-      if constexpr (QJL) {
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&qs->q2[hh][32 * g + 8 * kb]);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&qs->q2[hh][32 * g + 8 * kb + 4]);
+    m1 = col_max(m1);
+    m2 = col_max(m2);
+    int e1 = 0, e2 = 0;
+    if (m1 > 0.f) frexpf(m1, &e1);
+    if (m2 > 0.f) frexpf(m2, &e2);
+    const float s1 = ldexpf(1.0f, -e1), s2 = ldexpf(1.0f, -e2);  // exact powers of two
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bs[kb][e] = static_cast<_Float16>(b0[e] * s2);
-          bs[kb][4 + e] = static_cast<_Float16>(b1[e] * s2);
-        }
-      } else {
-        bs[kb] = f16x8{};
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bq[kb][e] = static_cast<_Float16>(qv1[2 * kb][e] * s1);
+        bq[kb][4 + e] = static_cast<_Float16>(qv1[2 * kb + 1][e] * s1);
+        bs[kb][e] = static_cast<_Float16>(qv2[2 * kb][e] * s2);
+        bs[kb][4 + e] = static_cast<_Float16>(qv2[2 * kb + 1][e] * s2);
       }
-    }
     const float lscale = a.scale * LOG2E;
     c1 = ldexpf(1.0f, e1) * INV_SQRT_D * lscale;
     c2 = ldexpf(1.0f, e2) * KAPPA * lscale;
   }
+  __syncthreads();  // tables ready
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
     Norms nrm;
@@ -684,7 +685,7 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   }
 
   // ---- merge over the slices: the last workgroup of each group of 16 slices merges the
-  // group, the last group merger merges the groups and applies R_eff^T ---------------------
+  // group and applies R_eff^T, the last group merger merges the groups ---------------------
   const int ns = a.n_slices;
   const int ngrp = (ns + MGROUP - 1) / MGROUP;
   const int grp = blockIdx.x / MGROUP;
@@ -703,29 +704,9 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   }
   __syncthreads();
   if (ep->stage == 0) return;
-  if (ep->stage == 1) {
-    const int gsize = min(MGROUP, ns - MGROUP * grp);
-    for (int idx = tid; idx < G * 32; idx += 256) {
-      const int h = idx >> 5, c = idx & 31;
-      const Merged r = merge_chunk(a.part + ((bh * G + h) * ns + MGROUP * grp) * PREC, gsize, c);
-      float* dst = a.gpart + ((bh * G + h) * ngrp + grp) * PREC;
-      st_dev2(dst + 4 * c, r.A[0], r.A[1]);
-      st_dev2(dst + 4 * c + 2, r.A[2], r.A[3]);
-      if (c == 0) st_dev2(dst + 128, r.M, r.L);
-    }
-    drain_stores();
-    __syncthreads();
-    if (tid == 0) {
-      ep->stage = 0;
-      if (atomicAdd(a.cnt_top + bh, 1u) == static_cast<unsigned>(ngrp - 1)) {
-        __hip_atomic_store(a.cnt_top + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ep->stage = 2;
-      }
-    }
-    __syncthreads();
-    if (ep->stage != 2) return;
-  }
-  // R_eff^T operands for this wave's output coordinates k = 32 wave + 16 nt + col
+  // This workgroup merges: it applies R_eff^T to what it merged (the unrotation is linear, so
+  // merging unrotated group results is the same as unrotating the merge).  Operands for this
+  // wave's output coordinates k = 32 wave + 16 nt + col, loaded before the merge's loads.
   bf16x8 th[2][4], tl[2][4];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -736,12 +717,13 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
       tl[nt][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_lo + k * D + 32 * g + 8 * kb));
     }
   }
+  // merge the slices of this group (or all slices with a single group) into ep->amat, ep->st
   {
-    const float* src = ngrp == 1 ? a.part : a.gpart;
-    const int count = ngrp == 1 ? ns : ngrp;
+    const int first = ngrp == 1 ? 0 : MGROUP * grp;
+    const int count = ngrp == 1 ? ns : min(MGROUP, ns - MGROUP * grp);
     for (int idx = tid; idx < G * 32; idx += 256) {
       const int h = idx >> 5, c = idx & 31;
-      const Merged r = merge_chunk(src + (bh * G + h) * count * PREC, count, c);
+      const Merged r = merge_chunk(a.part + ((bh * G + h) * ns + first) * PREC, count, c);
       *reinterpret_cast<f32x4*>(&ep->amat[h][4 * c]) = r.A;
       if (c == 0) {
         ep->st[h][0] = r.M;
@@ -770,16 +752,50 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
       u[nt] = mfma_bf16(pl, tl[nt][kb], u[nt]);
     }
   }
+  if (ngrp == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * g + i;
+      if (h >= G) continue;
+      const float L = ep->st[h][1];
+      // value centroids enter as c / sqrt(d)
+      const float f = L > 0.f ? INV_SQRT_D / L : 0.f;
+      float* o = a.out + (bh * G + h) * D;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) o[32 * wave + 16 * nt + col] = u[nt][i] * f;
+    }
+    return;
+  }
+  // publish the group's unrotated record, then the last group merges the groups
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * g + i;
     if (h >= G) continue;
-    const float L = ep->st[h][1];
-    // value centroids enter as c / sqrt(d)
-    const float f = L > 0.f ? INV_SQRT_D / L : 0.f;
-    float* o = a.out + (bh * G + h) * D;
+    float* dst = a.gpart + ((bh * G + h) * ngrp + grp) * PREC;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) o[32 * wave + 16 * nt + col] = u[nt][i] * f;
+    for (int nt = 0; nt < 2; ++nt)
+      __hip_atomic_store(dst + 32 * wave + 16 * nt + col, u[nt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (tid < G) st_dev2(a.gpart + ((bh * G + tid) * ngrp + grp) * PREC + 128, ep->st[tid][0], ep->st[tid][1]);
+  drain_stores();
+  __syncthreads();
+  if (tid == 0) {
+    ep->stage = 0;
+    if (atomicAdd(a.cnt_top + bh, 1u) == static_cast<unsigned>(ngrp - 1)) {
+      __hip_atomic_store(a.cnt_top + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ep->stage = 2;
+    }
+  }
+  __syncthreads();
+  if (ep->stage != 2) return;
+  for (int idx = tid; idx < G * 32; idx += 256) {
+    const int h = idx >> 5, c = idx & 31;
+    const Merged r = merge_chunk(a.gpart + (bh * G + h) * ngrp * PREC, ngrp, c);
+    // value centroids enter as c / sqrt(d)
+    const float f = r.L > 0.f ? INV_SQRT_D / r.L : 0.f;
+    float* o = a.out + (bh * G + h) * D + 4 * c;  // out is only 4-byte aligned
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = r.A[e] * f;
   }
 }
 
@@ -898,9 +914,14 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   const int B = cache->B;
   const int nblk_max = (max_seq_len + 63) / 64;
   const int units = B * cache->Hkv;
-  static const int wg_per_cu = env_int("TQ_ATTN_WG_PER_CU", 2, 1, 64);
+  // Two workgroups per CU hide latency best when every wave still streams many blocks; when
+  // the context is short, one per CU halves the partial results the merge has to combine.
+  static const int wg_per_cu_env = env_int("TQ_ATTN_WG_PER_CU", 0, 0, 64);
   static const int MIN_BLOCKS_PER_WAVE = env_int("TQ_ATTN_MIN_BLOCKS", 2, 1, 1 << 20);
-  const int target_wg = wg_per_cu * device_cu_count();
+  const int cus = device_cu_count();
+  const int64_t total_blocks = static_cast<int64_t>(units) * nblk_max;
+  const int wg_per_cu = wg_per_cu_env > 0 ? wg_per_cu_env : (total_blocks >= 8ll * 8 * cus ? 2 : 1);
+  const int target_wg = wg_per_cu * cus;
   int n_slices = (target_wg + units - 1) / units;
   const int max_slices = std::max(1, (nblk_max + 4 * MIN_BLOCKS_PER_WAVE - 1) / (4 * MIN_BLOCKS_PER_WAVE));
   n_slices = std::max(1, std::min({n_slices, max_slices, MAX_SLICES}));
@@ -912,7 +933,8 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   const size_t part_bytes = align256(static_cast<size_t>(B) * Hq * n_slices * PREC * sizeof(float));
   const size_t gpart_bytes =
       n_mgroups > 1 ? align256(static_cast<size_t>(B) * Hq * n_mgroups * PREC * sizeof(float)) : 0;
-  const size_t need = cnt_bytes + part_bytes + gpart_bytes;
+  const size_t qrec_bytes = align256(static_cast<size_t>(B) * Hq * QREC * sizeof(float));
+  const size_t need = qrec_bytes + cnt_bytes + part_bytes + gpart_bytes;
   if (workspace == nullptr) {
     *workspace_bytes = need;
     return TQ_OK;
@@ -924,13 +946,23 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   if (!aligned(workspace, 256)) return fail(TQ_ERR_INVALID, "workspace must be 256-byte aligned");
 
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace) + qrec_bytes;  // after the query records
+  float* qrec = reinterpret_cast<float*>(workspace);
   unsigned* cnt_grp = reinterpret_cast<unsigned*>(ws);
   unsigned* cnt_top = cnt_grp + static_cast<size_t>(B) * cache->Hkv * MAX_GROUPS;
   float* part = reinterpret_cast<float*>(ws + cnt_bytes);
   float* gpart = n_mgroups > 1 ? reinterpret_cast<float*>(ws + cnt_bytes + part_bytes)
                                : nullptr;
   if (scale == 0.f) scale = INV_SQRT_D;
+
+  PrologueArgs pa{q, p->r_hi, p->r_lo, cb->cfg.k_qjl ? p->m_hi : nullptr, cb->cfg.k_qjl ? p->m_lo : nullptr, qrec, G,
+                  q_dtype == TQ_DTYPE_F32 ? 1 : 0};
+  if (cb->cfg.k_qjl)
+    hipLaunchKernelGGL(prologue_kernel<true>, dim3(B * cache->Hkv, 4), dim3(64), 0, s, pa);
+  else
+    hipLaunchKernelGGL(prologue_kernel<false>, dim3(B * cache->Hkv, 4), dim3(64), 0, s, pa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("query prologue launch: ") + hipGetErrorString(e));
 
   MainArgs ma{};
   ma.k_codes = cache->k_codes;
@@ -940,12 +972,7 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   ma.v_codes = cache->v_codes;
   ma.v_norm = cache->v_norm;
   ma.seq_len = seq_len;
-  ma.q = q;
-  ma.q_f32 = q_dtype == TQ_DTYPE_F32 ? 1 : 0;
-  ma.r_hi = p->r_hi;
-  ma.r_lo = p->r_lo;
-  ma.m_hi = cb->cfg.k_qjl ? p->m_hi : nullptr;
-  ma.m_lo = cb->cfg.k_qjl ? p->m_lo : nullptr;
+  ma.qrec = qrec;
   ma.rt_hi = p->rt_hi;
   ma.rt_lo = p->rt_lo;
   ma.part = part;
@@ -971,7 +998,7 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
     e0 = reinterpret_cast<hipEvent_t>(pe.attend_start);
     e1 = reinterpret_cast<hipEvent_t>(pe.attend_stop);
   }
-  const hipError_t e = dispatch_main(ma, cb->cfg, G, n_slices, B, s, e0, e1);
+  e = dispatch_main(ma, cb->cfg, G, n_slices, B, s, e0, e1);
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("attention launch: ") + hipGetErrorString(e));
   return TQ_OK;
 }

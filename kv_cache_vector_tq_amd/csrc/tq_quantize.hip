@@ -106,6 +106,18 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   bool mt_on[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) mt_on[mt] = (16 * mt < r1) && (16 * mt + 16 > r0);
+  const int64_t bh = (int64_t)b * a.Hkv + h;
+  const int nblk = a.T_cap / 64;
+  // Value words hold codes of 4 tokens: a tile that does not cover the whole block reads the
+  // words it will modify now, so the read-modify-write at the end costs no extra round trip.
+  const bool partial = lo_slot > p0 || hi_slot < p0 + 64;  // uniform over the workgroup
+  uint32_t prev[KEY ? 1 : (BITS > 0 ? BITS : 1)];
+  if constexpr (!KEY) {
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(a.codes + (bh * nblk + blk) * (1024 * BITS) +
+                                                           (tid >> 2) * 16 * BITS + (tid & 3) * 4 * BITS);
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) prev[i] = partial ? pw[i] : 0u;
+  }
 
   // ---- load the tile, row norms ----------------------------------------------------------
   // The norm is taken after an exact power-of-two rescaling by the row's largest magnitude,
@@ -114,30 +126,40 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
     const int row = tid >> 2, q = tid & 3;
     const int slot = p0 + row;
     const bool valid = slot >= lo_slot && slot < hi_slot;
+    // all loads first, from a clamped (always written) row, so that they are in flight together;
+    // rows outside [lo_slot, hi_slot) are masked afterwards
+    constexpr int NW = F32 ? 8 : 4;  // 16-byte words of this thread's 32 elements
+    u32x4 w[NW];
+    {
+      const int srow = min(max(slot, lo_slot), hi_slot - 1);
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(a.x) +
+                           ((int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)(srow - start) * a.st + 32 * q) *
+                               (F32 ? 4 : 2);
+#pragma unroll
+      for (int i = 0; i < NW; ++i) w[i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
+#pragma unroll
+      for (int i = 0; i < NW; ++i)
+        if (!valid) w[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     float v[32];
     if constexpr (F32) {
-      const float* src = reinterpret_cast<const float*>(a.x) + (int64_t)b * a.sb + (int64_t)h * a.sh +
-                         (int64_t)(slot - start) * a.st + 32 * q;
       float* dst = s_tile + row * XS_F32 + 32 * q;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (valid) x = *reinterpret_cast<const f32x4*>(src + 4 * i);
-        *reinterpret_cast<f32x4*>(dst + 4 * i) = x;
+        *reinterpret_cast<u32x4*>(dst + 4 * i) = w[i];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * i + e] = x[e];
+        for (int e = 0; e < 4; ++e) v[4 * i + e] = __uint_as_float(w[i][e]);
       }
     } else {
-      const uint16_t* src = reinterpret_cast<const uint16_t*>(a.x) + (int64_t)b * a.sb + (int64_t)h * a.sh +
-                            (int64_t)(slot - start) * a.st + 32 * q;
       uint16_t* dst = reinterpret_cast<uint16_t*>(s_tile) + row * XS_BF16 + 32 * q;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        u16x8 x = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        if (valid) x = *reinterpret_cast<const u16x8*>(src + 8 * i);
-        *reinterpret_cast<u16x8*>(dst + 8 * i) = x;
+        *reinterpret_cast<u32x4*>(dst + 8 * i) = w[i];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[8 * i + e] = bf2f(x[e]);
+        for (int e = 0; e < 4; ++e) {
+          v[8 * i + 2 * e] = __uint_as_float(w[i][e] << 16);
+          v[8 * i + 2 * e + 1] = __uint_as_float(w[i][e] & 0xFFFF0000u);
+        }
       }
     }
     float mx = 0.f;
@@ -295,8 +317,6 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   }
 
   // ---- pack and store ------------------------------------------------------------------------
-  const int64_t bh = (int64_t)b * a.Hkv + h;
-  const int nblk = a.T_cap / 64;
   {
     const int Lc = tid >> 2, part = tid & 3;
     const int c = Lc & 15, g = Lc >> 4;
@@ -359,7 +379,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
         if (m[i] == 0xFFFFFFFFu) {
           dst[i] = w[i];
         } else if (m[i] != 0u) {
-          dst[i] = (dst[i] & ~m[i]) | w[i];
+          dst[i] = (prev[i] & ~m[i]) | w[i];
         }
       }
     }
