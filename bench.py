@@ -156,16 +156,18 @@ def time_workload(name, preset, dev, reps=5):
 
 
 def stream_read_gbs(dev, mib=2048):
-    """Read bandwidth of the box measured with a device-wide reduction over a large buffer."""
+    """Read bandwidth of the box: row sums over a 2 GiB fp32 buffer (a streaming read that
+    writes almost nothing), 5 passes timed with events."""
     import torch
 
-    x = torch.ones(mib << 18, dtype=torch.int32, device=dev)
-    x.sum()
+    x = torch.ones(mib << 18, dtype=torch.float32, device=dev)
+    xv = x.view(4096, -1)
+    xv.sum(dim=1)
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(5):
-        x.sum()
+        xv.sum(dim=1)
     t1.record()
     torch.cuda.synchronize()
     gbs = 5 * x.numel() * 4 / (t0.elapsed_time(t1) * 1e-3) / 1e9
