@@ -20,7 +20,7 @@
 //     score tile feed the value MFMA directly from the accumulator layout, and the value
 //     sum stays in the rotated domain.  The 4 waves merge their online-softmax states in
 //     LDS and write one partial per (q-head, slice).  Arrival counters then elect, per
-//     (batch row, kv-head), the last workgroup of each group of 16 slices to merge that
+//     (batch row, kv-head), the last workgroup of each group of slices to merge that
 //     group (log-sum-exp) and apply R_eff^T to it (exact bf16-split MFMA, fp32 sums), and
 //     the last of those to merge the unrotated group results - no separate merge launch.
 #include <hip/hip_runtime.h>
@@ -389,12 +389,12 @@ struct MainArgs {
   const uint16_t* rt_hi;  // R_hi^T, R_lo^T
   const uint16_t* rt_lo;
   float* part;        // [B*Hq][n_slices][PREC]: rotated sums, m, l of each slice
-  float* gpart;       // [B*Hq][n_groups][PREC]: the same per group of MGROUP slices
+  float* gpart;       // [B*Hq][n_groups][PREC]: the same per group of mgroup slices
   unsigned* cnt_grp;  // [B*Hkv][MAX_GROUPS] arrival counters (zero between calls)
   unsigned* cnt_top;  // [B*Hkv]
   float* out;         // [B*Hq][128]
   float* scores_out;  // NULL or [B*Hq][T_cap]
-  int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices;
+  int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices, mgroup;
   float scale_log2;   // scale * log2(e)
   float scale;
   float k_cent[16];
@@ -687,15 +687,16 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   // ---- merge over the slices: the last workgroup of each group of 16 slices merges the
   // group and applies R_eff^T, the last group merger merges the groups ---------------------
   const int ns = a.n_slices;
-  const int ngrp = (ns + MGROUP - 1) / MGROUP;
-  const int grp = blockIdx.x / MGROUP;
+  const int mgroup = a.mgroup;
+  const int ngrp = (ns + mgroup - 1) / mgroup;
+  const int grp = blockIdx.x / mgroup;
   drain_stores();
   __syncthreads();
   if (tid == 0) {
     // the last arrival resets its counter, so counters are zero again after every call
     int stage = 0;
     unsigned* cnt = ngrp == 1 ? a.cnt_top + bh : a.cnt_grp + bh * MAX_GROUPS + grp;
-    const unsigned last = ngrp == 1 ? ns - 1 : min(MGROUP, ns - MGROUP * grp) - 1;
+    const unsigned last = ngrp == 1 ? ns - 1 : min(mgroup, ns - mgroup * grp) - 1;
     if (atomicAdd(cnt, 1u) == last) {
       __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       stage = ngrp == 1 ? 2 : 1;
@@ -719,8 +720,8 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   }
   // merge the slices of this group (or all slices with a single group) into ep->amat, ep->st
   {
-    const int first = ngrp == 1 ? 0 : MGROUP * grp;
-    const int count = ngrp == 1 ? ns : min(MGROUP, ns - MGROUP * grp);
+    const int first = ngrp == 1 ? 0 : mgroup * grp;
+    const int count = ngrp == 1 ? ns : min(mgroup, ns - mgroup * grp);
     for (int idx = tid; idx < G * 32; idx += 256) {
       const int h = idx >> 5, c = idx & 31;
       const Merged r = merge_chunk(a.part + ((bh * G + h) * ns + first) * PREC, count, c);
@@ -928,7 +929,9 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   const int bpw = (nblk_max + 4 * n_slices - 1) / (4 * n_slices);
   n_slices = (nblk_max + 4 * bpw - 1) / (4 * bpw);
 
-  const int n_mgroups = (n_slices + MGROUP - 1) / MGROUP;
+  // groups of 16 slices (one load batch per merger); a single group needs no second level
+  const int mgroup = MGROUP;
+  const int n_mgroups = (n_slices + mgroup - 1) / mgroup;
   const size_t cnt_bytes = align256(static_cast<size_t>(B) * cache->Hkv * (MAX_GROUPS + 1) * sizeof(unsigned));
   const size_t part_bytes = align256(static_cast<size_t>(B) * Hq * n_slices * PREC * sizeof(float));
   const size_t gpart_bytes =
@@ -986,6 +989,7 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   ma.max_seq_len = max_seq_len;
   ma.blocks_per_wave = bpw;
   ma.n_slices = n_slices;
+  ma.mgroup = mgroup;
   ma.scale = scale;
   ma.scale_log2 = scale * LOG2E;
   for (int l = 0; l < 16; ++l) {

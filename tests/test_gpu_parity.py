@@ -151,11 +151,13 @@ def test_attention_ragged_lengths(preset, G):
             assert np.all(scores[b, hs, lens[b]:] == 0)
 
 
-@pytest.mark.parametrize("B,G,T_cap,lens", [(2, 8, 10240, [10240, 3001]), (1, 4, 262144, [262144 - 37])])
+@pytest.mark.parametrize("B,G,T_cap,lens", [(2, 8, 10240, [10240, 3001]), (1, 8, 20480, [20480 - 100]),
+                                            (1, 4, 262144, [262144 - 37])])
 def test_attention_merge_levels(B, G, T_cap, lens):
-    """Context splits over several merge groups: 20 slices (groups of 16 and 4, the second row
-    leaving most slices empty) and the maximum of 512 slices (32 groups).  A second call with
-    the same workspace must give identical outputs (the arrival counters are reset per call)."""
+    """Context splits of several sizes: 20 slices (groups of 16 and 4, the second row leaving
+    most slices empty), 40 slices (groups of 16, 16 and 8), and the maximum of 512 slices
+    (32 groups).  A second call with the same workspace must give identical outputs (the
+    arrival counters are reset per call)."""
     preset, Hkv = "turbo3", 1
     cb, dp, cache = _setup(preset, B, Hkv, T_cap)
     rng = np.random.default_rng(13)
