@@ -233,9 +233,11 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   }
   __syncthreads();  // the input tile is dead from here on; its space holds residuals
 
-  // ---- scale, scalar code, residual -------------------------------------------------------
+  // ---- scale, scalar code, residual (sub-tiles without a token of the call are skipped; the
+  // pack below masks their rows) -----------------------------------------------------------
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
+    if (!mt_on[mt]) continue;
     // z = sqrt(d) y = acc sqrt(d) / n for the lane's rows 16 mt + 4 grp + i
     const f32x4 zsv = *reinterpret_cast<const f32x4*>(sm.zs + 16 * mt + 4 * grp);
 #pragma unroll
@@ -407,6 +409,9 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantLaunch q) {
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
   Operands op;
+  // a workgroup that only sees value tiles (tiles alternate K, V; with one tile per workgroup
+  // the odd ones) does not need the sketch matrix
+  const bool sketch = QJL && q.has_k && (static_cast<int>(gridDim.x) < q.n_tiles || (blockIdx.x & 1) == 0);
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int o = 32 * wave + 16 * nt + col;
@@ -414,8 +419,7 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantLaunch q) {
     for (int kb = 0; kb < 4; ++kb) {
       op.rh[nt][kb] = load_bf16x8(q.k.r_hi + o * D + 32 * grp + 8 * kb);
       op.rl[nt][kb] = load_bf16x8(q.k.r_lo + o * D + 32 * grp + 8 * kb);
-      if constexpr (QJL)
-        op.sb[nt][kb] = q.has_k ? load_bf16x8(q.k.s_b + o * D + 32 * grp + 8 * kb) : bf16x8{};
+      if constexpr (QJL) op.sb[nt][kb] = sketch ? load_bf16x8(q.k.s_b + o * D + 32 * grp + 8 * kb) : bf16x8{};
     }
   }
   for (int t = blockIdx.x; t < q.n_tiles; t += gridDim.x) {
@@ -426,7 +430,10 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantLaunch q) {
     const int h = bh % q.Hkv, b = bh / q.Hkv;
     if (tensor == 0 ? !q.has_k : !q.has_v) continue;
     const QuantArgs& a = tensor == 0 ? q.k : q.v;
-    const int start = a.start_pos[b];
+    // a scalar load (constant address space: start_pos does not change during the kernel), so
+    // waiting for it does not wait for the operand loads in flight
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+    const int start = ((const_i32_ptr)(uintptr_t)a.start_pos)[b];
     if (start < 0) continue;
     const int end = min(start + a.n_new, a.T_cap);  // one past the last slot written
     const int blk = start / 64 + i;
