@@ -176,6 +176,41 @@ def stream_read_gbs(dev, mib=2048):
     return gbs
 
 
+def bf16_comparator(w, layers, dev, reps=3):
+    """Uncompressed decode attention at the same shape in plain PyTorch (bf16 K/V and q, fp32
+    softmax): scores = K q^T (bmm), softmax over the context, out = P^T V (bmm), for `layers`
+    distinct K/V caches.  Every bmm operand is contiguous.  Returns us per layer."""
+    import torch
+
+    Hkv, G, T = w.B * w.Hkv, w.G, w.T
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    Ks = [torch.randn((Hkv, T, 128), generator=gen, device=dev).to(torch.bfloat16) for _ in range(layers)]
+    Vs = [torch.randn((Hkv, T, 128), generator=gen, device=dev).to(torch.bfloat16) for _ in range(layers)]
+    qT = torch.randn((Hkv, 128, G), generator=gen, device=dev).to(torch.bfloat16).contiguous()
+    scale = 1.0 / math.sqrt(128)
+
+    def layer(K, V):
+        sc = torch.bmm(K, qT).float() * scale                      # [Hkv, T, G]
+        p = torch.softmax(sc, dim=1).to(torch.bfloat16).transpose(1, 2).contiguous()  # [Hkv, G, T]
+        return torch.bmm(p, V)                                      # [Hkv, G, 128]
+
+    for K, V in zip(Ks, Vs):
+        layer(K, V)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        for K, V in zip(Ks, Vs):
+            layer(K, V)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (reps * layers)
+    del Ks, Vs
+    torch.cuda.empty_cache()
+    return us
+
+
 def copy_probe(mib: int):
     import torch
 
@@ -301,14 +336,34 @@ def main():
     achieved = bytes_per_launch / kern_s / 1e9
     log(f"attention kernel: {kern_s * 1e6:.2f} us per launch, {achieved:.0f} GB/s")
 
+    # whole attention call (query prologue + main kernel) per layer, back to back over the layers
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(args.kernel_reps):
+        for l in range(L):
+            tq.tq_attend_decode(cb, dp, caches[l], qs_l[l], seq, T, out=outs[l], workspace=ws)
+    c1.record()
+    torch.cuda.synchronize()
+    call_us = c0.elapsed_time(c1) * 1e3 / (args.kernel_reps * L)
+    log(f"attention call (prologue + main): {call_us:.2f} us per layer")
+
     # host copy of one (batch row, kv-head) of layer 0 for the oracle on the host cores
     host = {n: (None if t is None else t[0, 0].cpu().numpy()) for n, t in caches[0].tensors().items()}
 
     # ---- the other HBM-sized workloads (one cache each; the step's caches are freed first) -------
     others = []
+    comparator = None
     if args.other_workloads:
         del caches, k_new, v_new, K, V, ws, outs, qs_l, graph
         torch.cuda.empty_cache()
+        bf16_us = bf16_comparator(w, L, dev)
+        bf16_bytes = 2 * B * Hkv * T * 128 * 2
+        comparator = {"kind": "uncompressed bf16 decode attention in plain PyTorch (bmm, fp32 softmax, bmm)",
+                      "us_per_layer": bf16_us, "keys_per_s": B * Hkv * T / (bf16_us * 1e-6),
+                      "gbs": bf16_bytes / (bf16_us * 1e-6) / 1e9,
+                      "compressed_call_us_per_layer": call_us,
+                      "speedup_of_compressed_call": bf16_us / call_us}
+        log(json.dumps(comparator))
         for name, preset in OTHER_WORKLOADS:
             log("timing", name, preset)
             others.append(time_workload(name, preset, dev))
@@ -346,6 +401,8 @@ def main():
             "attend_frac_of_measured_read": achieved / read_gbs,
             "measured_read_gbs": read_gbs,
             "workloads": others,
+            "attend_call_us_per_layer": call_us,
+            "bf16_comparator": comparator,
             "step_gbs": keys_per_step * bytes_per_key / (step_ms * 1e-3) / 1e9,
             "bulk_quantize": {"vectors_per_launch": n_vec, "us_per_launch": bulk_s * 1e6,
                               "vectors_per_s": n_vec / bulk_s, "gbs": bulk_b / bulk_s / 1e9,
