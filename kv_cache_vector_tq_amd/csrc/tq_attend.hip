@@ -42,7 +42,7 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float KAPPA = 0.009791666936874390f;  // sqrt(pi/2)/128
 constexpr float NEG_BIG = -1.0e30f;
 constexpr int PREC = 132;   // floats per partial record: sums[128], m, l, scale, pad
-constexpr int MGROUP = 16;                       // slices per first-level merge group
+constexpr int MGROUP = 32;                       // slices per first-level merge group
 constexpr int MAX_GROUPS = 32;                   // merge groups per (batch row, kv-head)
 constexpr int MAX_SLICES = MGROUP * MAX_GROUPS;  // context slices per (batch row, kv-head)
 
@@ -335,46 +335,59 @@ struct Epi {
 };
 
 struct Merged {
-  f32x4 A;  // weighted sums of one 4-float chunk
+  float A0, A1;  // weighted sums of coordinates 2 lane, 2 lane + 1
   float M, L;
 };
 
-// Log-sum-exp merge of `count` partial records (sums[128], m, l at stride PREC from hs) for
-// the 4-float chunk c of the sums.  Records are loaded 16 at a time, all loads of a batch in
-// flight together, and merged online.
-__device__ Merged merge_chunk(const float* hs, int count, int c) {
-  float M = NEG_BIG, L = 0.f;
-  f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int r0 = 0; r0 < count; r0 += 16) {
-    float2 ml[16];
-    f32x4 v[16];
+// Log-sum-exp merge of `count` partial records (sums[128], m, l at stride PREC from hs) by one
+// wave: lane l takes sums 2 l and 2 l + 1 of every record, so one 8-byte load per lane covers
+// a whole record, and lane k of a batch loads (m, l) of its record k, which the merge reads
+// back as wave-uniform values.  Records are loaded NB at a time from clamped (always valid)
+// indices, all loads of a batch in flight together, and merged online; the surplus of a
+// partial batch is masked after its loads.
+template <int NB>
+__device__ Merged merge_batches(const float* hs, int count, int lane) {
+  static_assert(NB <= 64, "one (m, l) pair per lane");
+  float M = NEG_BIG, L = 0.f, A0 = 0.f, A1 = 0.f;
+  for (int r0 = 0; r0 < count; r0 += NB) {
+    float2 v[NB];
+    const float2 mine = ld_dev2(hs + static_cast<int64_t>(min(r0 + lane % NB, count - 1)) * PREC + 128);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      if (r0 + k < count) {
-        const float* rec = hs + static_cast<int64_t>(r0 + k) * PREC;
-        ml[k] = ld_dev2(rec + 128);
-        const float2 x = ld_dev2(rec + 4 * c), y = ld_dev2(rec + 4 * c + 2);
-        v[k] = f32x4{x.x, x.y, y.x, y.y};
-      } else {
-        ml[k] = make_float2(NEG_BIG, 0.f);
-        v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NB; ++k) v[k] = ld_dev2(hs + static_cast<int64_t>(min(r0 + k, count - 1)) * PREC + 2 * lane);
+    float mk[NB], lk[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      mk[k] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mine.x), k));
+      lk[k] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(mine.y), k));
+      if (r0 + k >= count) {
+        mk[k] = NEG_BIG;
+        lk[k] = 0.f;
       }
     }
     float Mb = M;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) Mb = fmaxf(Mb, ml[k].x);
+    for (int k = 0; k < NB; ++k) Mb = fmaxf(Mb, mk[k]);
     const float sc = exp2f(M - Mb);
-    A *= sc;
+    A0 *= sc;
+    A1 *= sc;
     L *= sc;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float e = exp2f(ml[k].x - Mb);  // 0 for empty records unless all are empty (then v = l = 0)
-      A += e * v[k];
-      L = fmaf(e, ml[k].y, L);
+    for (int k = 0; k < NB; ++k) {
+      // 0 for masked and empty records, unless every record so far is empty (then v = l = 0)
+      const float e = r0 + k < count ? exp2f(mk[k] - Mb) : 0.f;
+      A0 = fmaf(e, v[k].x, A0);
+      A1 = fmaf(e, v[k].y, A1);
+      L = fmaf(e, lk[k], L);
     }
     M = Mb;
   }
-  return Merged{A, M, L};
+  return Merged{A0, A1, M, L};
+}
+// batch size by count: one round of loads for up to 32 records
+__device__ __forceinline__ Merged merge_records(const float* hs, int count, int lane) {
+  if (count <= 4) return merge_batches<4>(hs, count, lane);
+  if (count <= 16) return merge_batches<16>(hs, count, lane);
+  return merge_batches<32>(hs, count, lane);
 }
 
 struct MainArgs {
@@ -489,8 +502,11 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
     qv1[i] = *reinterpret_cast<const f32x4*>(qr + 32 * g + 4 * i);
     qv2[i] = QJL ? *reinterpret_cast<const f32x4*>(qr + D + 32 * g + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // Block loads are unconditional, from clamped (always in-bounds) block indices: a load under
+  // a branch would make the compiler wait for every load in flight where the branches join,
+  // which would serialize the prefetch with the current block's compute.
   Blk cur, nxt;
-  if (blk_begin < blk_end) load_block(blk_begin, cur);  // in flight while the tables are built
+  load_block(min(blk_begin, nblk_cap - 1), cur);  // in flight while the tables are built
 
   if constexpr (KB > 0) build_code_table<(KB > 0 ? KB : 1)>(ktab, a.k_cent, tid);
   if constexpr (QJL) build_sign_table(stab, tid);
@@ -530,7 +546,7 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   for (int blk = blk_begin; blk < blk_end; ++blk) {
     Norms nrm;
     load_norms(blk, nrm);
-    if (blk + 1 < blk_end) load_block(blk + 1, nxt);
+    load_block(min(blk + 1, blk_end - 1), nxt);
 
     // ---- score MFMAs: tile t = keys 16 t .. 16 t + 15 of the block; each lane keeps the
     // tile of its column class in every set (tile s TPD + tcls of set s) ----------------------
@@ -637,6 +653,20 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
     cur = nxt;
   }
 
+  // Operands of R_eff^T for the unrotation, in case this workgroup becomes a merger: rows
+  // k = 32 wave + 16 nt + col.  Loaded now, so that their latency overlaps the epilogue below
+  // instead of following the arrival count.
+  bf16x8 th[2][4], tl[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int k = 32 * wave + 16 * nt + col;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      th[nt][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_hi + k * D + 32 * g + 8 * kb));
+      tl[nt][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_lo + k * D + 32 * g + 8 * kb));
+    }
+  }
+
   // ---- merge the 4 waves and the TPD column classes of each q-head in LDS ----------------------
   const float l_tot = col_sum(l_run);
   __syncthreads();  // every wave is done with the tables
@@ -706,53 +736,47 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   __syncthreads();
   if (ep->stage == 0) return;
   // This workgroup merges: it applies R_eff^T to what it merged (the unrotation is linear, so
-  // merging unrotated group results is the same as unrotating the merge).  Operands for this
-  // wave's output coordinates k = 32 wave + 16 nt + col, loaded before the merge's loads.
-  bf16x8 th[2][4], tl[2][4];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int k = 32 * wave + 16 * nt + col;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      th[nt][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_hi + k * D + 32 * g + 8 * kb));
-      tl[nt][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_lo + k * D + 32 * g + 8 * kb));
-    }
-  }
-  // merge the slices of this group (or all slices with a single group) into ep->amat, ep->st
+  // merging unrotated group results is the same as unrotating the merge).  Merge the slices of
+  // this group (or all slices with a single group) into ep->amat, ep->st; wave w takes q-heads
+  // w, w + 4, ...
   {
     const int first = ngrp == 1 ? 0 : mgroup * grp;
     const int count = ngrp == 1 ? ns : min(mgroup, ns - mgroup * grp);
-    for (int idx = tid; idx < G * 32; idx += 256) {
-      const int h = idx >> 5, c = idx & 31;
-      const Merged r = merge_chunk(a.part + ((bh * G + h) * ns + first) * PREC, count, c);
-      *reinterpret_cast<f32x4*>(&ep->amat[h][4 * c]) = r.A;
-      if (c == 0) {
+    for (int h = wave; h < G; h += 4) {
+      const Merged r = merge_records(a.part + ((bh * G + h) * ns + first) * PREC, count, lane);
+      *reinterpret_cast<float2*>(&ep->amat[h][2 * lane]) = make_float2(r.A0, r.A1);
+      if (lane == 0) {
         ep->st[h][0] = r.M;
         ep->st[h][1] = r.L;
       }
     }
     __syncthreads();
   }
-  // U[h][k] = sum_j A[h][j] R_eff[j][k]: rows = q-heads (rows >= G are not used), columns = k
-  f32x4 u[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  // U[h][k] = sum_j A[h][j] R_eff[j][k]: rows = q-heads (rows >= G are not used), columns = k.
+  // Each split term of A accumulates in its own registers (six independent MFMA chains).
+  f32x4 u[2], uh[2][3];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int t = 0; t < 3; ++t) uh[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     float v[8];
     const float* src = &ep->amat[col][32 * g + 8 * kb];
     *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
     *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
-    bf16x8 ph, pm, pl;
-    split3_bf16(v, ph, pm, pl);
+    bf16x8 p[3];
+    split3_bf16(v, p[0], p[1], p[2]);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      u[nt] = mfma_bf16(ph, th[nt][kb], u[nt]);
-      u[nt] = mfma_bf16(ph, tl[nt][kb], u[nt]);
-      u[nt] = mfma_bf16(pm, th[nt][kb], u[nt]);
-      u[nt] = mfma_bf16(pm, tl[nt][kb], u[nt]);
-      u[nt] = mfma_bf16(pl, th[nt][kb], u[nt]);
-      u[nt] = mfma_bf16(pl, tl[nt][kb], u[nt]);
-    }
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        uh[nt][t] = mfma_bf16(p[t], th[nt][kb], uh[nt][t]);
+        uh[nt][t] = mfma_bf16(p[t], tl[nt][kb], uh[nt][t]);
+      }
   }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) u[nt] = uh[nt][0] + (uh[nt][1] + uh[nt][2]);
   if (ngrp == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -789,14 +813,13 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   }
   __syncthreads();
   if (ep->stage != 2) return;
-  for (int idx = tid; idx < G * 32; idx += 256) {
-    const int h = idx >> 5, c = idx & 31;
-    const Merged r = merge_chunk(a.gpart + (bh * G + h) * ngrp * PREC, ngrp, c);
+  for (int h = wave; h < G; h += 4) {
+    const Merged r = merge_records(a.gpart + (bh * G + h) * ngrp * PREC, ngrp, lane);
     // value centroids enter as c / sqrt(d)
     const float f = r.L > 0.f ? INV_SQRT_D / r.L : 0.f;
-    float* o = a.out + (bh * G + h) * D + 4 * c;  // out is only 4-byte aligned
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = r.A[e] * f;
+    float* o = a.out + (bh * G + h) * D + 2 * lane;  // out is only 4-byte aligned
+    o[0] = r.A0 * f;
+    o[1] = r.A1 * f;
   }
 }
 

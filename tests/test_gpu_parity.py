@@ -154,10 +154,10 @@ def test_attention_ragged_lengths(preset, G):
 @pytest.mark.parametrize("B,G,T_cap,lens", [(2, 8, 10240, [10240, 3001]), (1, 8, 20480, [20480 - 100]),
                                             (1, 4, 262144, [262144 - 37])])
 def test_attention_merge_levels(B, G, T_cap, lens):
-    """Context splits of several sizes: 20 slices (groups of 16 and 4, the second row leaving
-    most slices empty), 40 slices (groups of 16, 16 and 8), and the maximum of 512 slices
-    (32 groups).  A second call with the same workspace must give identical outputs (the
-    arrival counters are reset per call)."""
+    """Context splits of several sizes: 20 slices (one merge group, the second row leaving
+    most slices empty), 40 slices (groups of 32 and 8), and 256 slices (8 groups of 32).  A
+    second call with the same workspace must give identical outputs (the arrival counters are
+    reset per call)."""
     preset, Hkv = "turbo3", 1
     cb, dp, cache = _setup(preset, B, Hkv, T_cap)
     rng = np.random.default_rng(13)
