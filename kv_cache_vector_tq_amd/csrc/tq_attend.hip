@@ -13,13 +13,14 @@
 // Two launches on the caller's stream:
 //  1. query prologue, one single-wave workgroup per (batch row, kv-head, 32 output
 //     coordinates): q1, q2 of the G q-heads (MFMA), stored as fp32 records;
-//  2. main: one workgroup of 4 waves per (batch row, kv-head, context slice); each wave
-//     streams the 64-key blocks of its sub-slice.  Codes are turned into f16 MFMA operands by
-//     table lookups in LDS (4 or 8 codes per lookup); keys sit on the M side of the score
-//     MFMAs (one key read serves all G q-heads of the group), the softmax weights of a
-//     score tile feed the value MFMA directly from the accumulator layout, and the value
-//     sum stays in the rotated domain.  The 4 waves merge their online-softmax states in
-//     LDS and write one partial per (q-head, slice).  Arrival counters then elect, per
+//  2. main: one workgroup of 8 waves (one workgroup per CU, two waves per SIMD) per (batch
+//     row, kv-head, context slice); each wave streams the 64-key blocks of its sub-slice.
+//     Codes are turned into f16 MFMA operands by table lookups in LDS (4 or 8 codes per
+//     lookup); keys sit on the M side of the score MFMAs (one key read serves all G q-heads
+//     of the group), the softmax weights of a score tile feed the value MFMA directly from
+//     the accumulator layout, and the value sum stays in the rotated domain.  The 8 waves
+//     merge their online-softmax states in LDS and write one partial per (q-head, slice).
+//     Arrival counters then elect, per
 //     (batch row, kv-head), the last workgroup of each group of slices to merge that
 //     group (log-sum-exp) and apply R_eff^T to it (exact bf16-split MFMA, fp32 sums), and
 //     the last of those to merge the unrotated group results - no separate merge launch.
@@ -42,6 +43,8 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float KAPPA = 0.009791666936874390f;  // sqrt(pi/2)/128
 constexpr float NEG_BIG = -1.0e30f;
 constexpr int PREC = 132;   // floats per partial record: sums[128], m, l, scale, pad
+constexpr int NW = 8;                            // waves per attention workgroup (one per CU)
+constexpr int NT = 64 * NW;                      // threads per attention workgroup
 constexpr int MGROUP = 32;                       // slices per first-level merge group
 constexpr int MAX_GROUPS = 32;                   // merge groups per (batch row, kv-head)
 constexpr int MAX_SLICES = MGROUP * MAX_GROUPS;  // context slices per (batch row, kv-head)
@@ -327,7 +330,7 @@ __device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0); 
 
 // LDS of the epilogue (aliases the decode tables)
 struct Epi {
-  float rec[64][PREC];  // per wave and lane column: rotated sums, m, l, value scale
+  float rec[64][PREC];  // per wave 0..3 and lane column: rotated sums, m, l, value scale
   float w64[64];        // weight of each record in its q-head's merge
   float amat[16][QS];   // merged rotated sums of the q-heads (rows >= G unused)
   float st[16][2];      // merged max and sum of each q-head
@@ -425,15 +428,15 @@ struct MainCfg {
   static constexpr int TABLES = KTAB + STAB + VTAB;
   // the epilogue reuses the table space once every wave has left the block loop
   static constexpr int MERGE = static_cast<int>(sizeof(Epi));
-  static constexpr int LDS = TABLES > MERGE ? TABLES : MERGE;
+  // the G query records are staged behind the tables before the block loop (the epilogue,
+  // which aliases both, comes after it)
+  static constexpr int QSTAGE = G * QREC * 4;
+  static constexpr int LDS = TABLES + QSTAGE > MERGE ? TABLES + QSTAGE : MERGE;
 };
 
-#ifndef ATTN_MIN_WG
-#define ATTN_MIN_WG 2
-#endif
 // Streams the 64-key blocks of one slice.  SCORES: also write the logits (parity runs).
 template <int KB, bool QJL, int VB, int G, bool SCORES>
-__global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
+__global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   using C = MainCfg<KB, QJL, VB, G>;
   constexpr int TPD = C::TPD, NSETS = C::NSETS;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
@@ -453,7 +456,7 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   int seq = a.seq_len[b];
   seq = seq < 1 ? 1 : (seq > a.max_seq_len ? a.max_seq_len : seq);
   const int nblk = (seq + 63) / 64;
-  const int slice = blockIdx.x * 4 + wave;
+  const int slice = blockIdx.x * NW + wave;
   const int blk_begin = slice * a.blocks_per_wave;
   const int blk_end = min(blk_begin + a.blocks_per_wave, nblk);
 
@@ -495,12 +498,17 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   // the vector's largest magnitude (the 4 lanes of a column hold the 128 coordinates).
   // logit * log2(e) = n (code_acc * c1 + rnorm * sign_acc * c2): the table holds centroids c,
   // the key term is q1 . c / sqrt(d), the sign term carries sqrt(pi/2)/m.
-  const float* qr = a.qrec + ((int64_t)b * Hq + kvh * G + hh) * QREC;
-  f32x4 qv1[8], qv2[8];
+  // The G query records of this kv-head (contiguous) go through LDS: one 16-byte load per
+  // thread (two for G = 16), issued before the block loads, so that no wave's query waits
+  // behind other waves' block loads.
+  constexpr int QWORDS = G * QREC / 4;
+  constexpr int QPT = (QWORDS + NT - 1) / NT;
+  float* const qst = reinterpret_cast<float*>(smem + C::TABLES);
+  f32x4 qw[QPT];
+  {
+    const float* qsrc = a.qrec + ((int64_t)b * Hq + kvh * G) * QREC;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    qv1[i] = *reinterpret_cast<const f32x4*>(qr + 32 * g + 4 * i);
-    qv2[i] = QJL ? *reinterpret_cast<const f32x4*>(qr + D + 32 * g + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < QPT; ++k) qw[k] = *reinterpret_cast<const f32x4*>(qsrc + 4 * min(tid + k * NT, QWORDS - 1));
   }
   // Block loads are unconditional, from clamped (always in-bounds) block indices: a load under
   // a branch would make the compiler wait for every load in flight where the branches join,
@@ -508,12 +516,24 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   Blk cur, nxt;
   load_block(min(blk_begin, nblk_cap - 1), cur);  // in flight while the tables are built
 
-  if constexpr (KB > 0) build_code_table<(KB > 0 ? KB : 1)>(ktab, a.k_cent, tid);
-  if constexpr (QJL) build_sign_table(stab, tid);
-  if constexpr (!C::SHARED) build_code_table<VB>(vtab, a.v_cent, tid);
+  if (wave < 4) {  // the table builders take 256 threads
+    if constexpr (KB > 0) build_code_table<(KB > 0 ? KB : 1)>(ktab, a.k_cent, tid);
+    if constexpr (QJL) build_sign_table(stab, tid);
+    if constexpr (!C::SHARED) build_code_table<VB>(vtab, a.v_cent, tid);
+  }
+#pragma unroll
+  for (int k = 0; k < QPT; ++k)
+    if (tid + k * NT < QWORDS) *reinterpret_cast<f32x4*>(qst + 4 * (tid + k * NT)) = qw[k];
+  __syncthreads();  // tables and query records ready
   f16x8 bq[4], bs[4];
   float c1, c2;
   {
+    f32x4 qv1[8], qv2[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qv1[i] = *reinterpret_cast<const f32x4*>(qst + hh * QREC + 32 * g + 4 * i);
+      qv2[i] = QJL ? *reinterpret_cast<const f32x4*>(qst + hh * QREC + D + 32 * g + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     float m1 = 0.f, m2 = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -541,7 +561,6 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
     c1 = ldexpf(1.0f, e1) * INV_SQRT_D * lscale;
     c2 = ldexpf(1.0f, e2) * KAPPA * lscale;
   }
-  __syncthreads();  // tables ready
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
     Norms nrm;
@@ -654,25 +673,26 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   }
 
   // Operands of R_eff^T for the unrotation, in case this workgroup becomes a merger: rows
-  // k = 32 wave + 16 nt + col.  Loaded now, so that their latency overlaps the epilogue below
-  // instead of following the arrival count.
-  bf16x8 th[2][4], tl[2][4];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int k = 32 * wave + 16 * nt + col;
+  // k = 16 wave + col.  Loaded now, so that their latency overlaps the epilogue below instead
+  // of following the arrival count.
+  bf16x8 th[4], tl[4];
+  {
+    const int k = 16 * wave + col;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      th[nt][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_hi + k * D + 32 * g + 8 * kb));
-      tl[nt][kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_lo + k * D + 32 * g + 8 * kb));
+      th[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_hi + k * D + 32 * g + 8 * kb));
+      tl[kb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(a.rt_lo + k * D + 32 * g + 8 * kb));
     }
   }
 
-  // ---- merge the 4 waves and the TPD column classes of each q-head in LDS ----------------------
-  const float l_tot = col_sum(l_run);
+  // ---- merge the waves and the TPD column classes of each q-head in LDS ------------------------
+  // Waves 4..7 hand their state to wave w - 4 (same lane columns, hence the same q-heads), which
+  // folds it into its own: sums weighted by s 2^(m - M), so the folded record has scale 1.
+  float l_tot = col_sum(l_run);
   __syncthreads();  // every wave is done with the tables
   Epi* ep = reinterpret_cast<Epi*>(smem);
-  {
-    float* rec = ep->rec[wave * 16 + col];
+  auto put_record = [&](int r) {
+    float* rec = ep->rec[r];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -682,7 +702,25 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
       rec[129] = l_tot;
       rec[130] = s_run;
     }
+  };
+  if (wave >= 4) put_record((wave - 4) * 16 + col);
+  __syncthreads();
+  if (wave < 4) {
+    const float* pr = ep->rec[wave * 16 + col];
+    const float m2 = pr[128], l2 = pr[129], s2 = pr[130];
+    const float M = fmaxf(m_run, m2);
+    const float e1 = exp2f(m_run - M), e2 = exp2f(m2 - M);
+    const float w1 = s_run * e1, w2 = s2 * e2;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(acc[mt][i], w1, pr[16 * mt + 4 * g + i] * w2);
+    m_run = M;
+    l_tot = fmaf(l_tot, e1, l2 * e2);
+    s_run = 1.0f;
   }
+  __syncthreads();  // the handed-over records are consumed
+  if (wave < 4) put_record(wave * 16 + col);
   __syncthreads();
   // record r = 16 w + c G + h belongs to q-head h; wave 0 finds each head's maximum and the
   // record weights over the lanes with the same h (xor offsets that keep r mod G)
@@ -700,7 +738,7 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
     if (tid < G) st_dev2(a.part + ((bh * G + tid) * a.n_slices + blockIdx.x) * PREC + 128, M, l);
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D / 2; idx += 256) {
+  for (int idx = tid; idx < G * D / 2; idx += NT) {
     const int h = idx / (D / 2), j = 2 * (idx % (D / 2));
     float A0 = 0.f, A1 = 0.f;
 #pragma unroll
@@ -742,7 +780,7 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   {
     const int first = ngrp == 1 ? 0 : mgroup * grp;
     const int count = ngrp == 1 ? ns : min(mgroup, ns - mgroup * grp);
-    for (int h = wave; h < G; h += 4) {
+    for (int h = wave; h < G; h += NW) {
       const Merged r = merge_records(a.part + ((bh * G + h) * ns + first) * PREC, count, lane);
       *reinterpret_cast<float2*>(&ep->amat[h][2 * lane]) = make_float2(r.A0, r.A1);
       if (lane == 0) {
@@ -752,13 +790,12 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
     }
     __syncthreads();
   }
-  // U[h][k] = sum_j A[h][j] R_eff[j][k]: rows = q-heads (rows >= G are not used), columns = k.
-  // Each split term of A accumulates in its own registers (six independent MFMA chains).
-  f32x4 u[2], uh[2][3];
+  // U[h][k] = sum_j A[h][j] R_eff[j][k]: rows = q-heads (rows >= G are not used), columns
+  // k = 16 wave + col.  Each product of a split term of A with R_hi or R_lo accumulates in its
+  // own registers (six independent MFMA chains).
+  f32x4 uh[3][2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int t = 0; t < 3; ++t) uh[nt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 3; ++t) uh[t][0] = uh[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
     float v[8];
@@ -768,15 +805,12 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
     bf16x8 p[3];
     split3_bf16(v, p[0], p[1], p[2]);
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        uh[nt][t] = mfma_bf16(p[t], th[nt][kb], uh[nt][t]);
-        uh[nt][t] = mfma_bf16(p[t], tl[nt][kb], uh[nt][t]);
-      }
+    for (int t = 0; t < 3; ++t) {
+      uh[t][0] = mfma_bf16(p[t], th[kb], uh[t][0]);
+      uh[t][1] = mfma_bf16(p[t], tl[kb], uh[t][1]);
+    }
   }
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) u[nt] = uh[nt][0] + (uh[nt][1] + uh[nt][2]);
+  const f32x4 u = (uh[0][0] + uh[0][1]) + ((uh[1][0] + uh[1][1]) + (uh[2][0] + uh[2][1]));
   if (ngrp == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -785,9 +819,7 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
       const float L = ep->st[h][1];
       // value centroids enter as c / sqrt(d)
       const float f = L > 0.f ? INV_SQRT_D / L : 0.f;
-      float* o = a.out + (bh * G + h) * D;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) o[32 * wave + 16 * nt + col] = u[nt][i] * f;
+      a.out[(bh * G + h) * D + 16 * wave + col] = u[i] * f;
     }
     return;
   }
@@ -797,9 +829,7 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
     const int h = 4 * g + i;
     if (h >= G) continue;
     float* dst = a.gpart + ((bh * G + h) * ngrp + grp) * PREC;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      __hip_atomic_store(dst + 32 * wave + 16 * nt + col, u[nt][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 16 * wave + col, u[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (tid < G) st_dev2(a.gpart + ((bh * G + tid) * ngrp + grp) * PREC + 128, ep->st[tid][0], ep->st[tid][1]);
   drain_stores();
@@ -813,7 +843,7 @@ __global__ void __launch_bounds__(256, ATTN_MIN_WG) attend_kernel(MainArgs a) {
   }
   __syncthreads();
   if (ep->stage != 2) return;
-  for (int h = wave; h < G; h += 4) {
+  for (int h = wave; h < G; h += NW) {
     const Merged r = merge_records(a.gpart + (bh * G + h) * ngrp * PREC, ngrp, lane);
     // value centroids enter as c / sqrt(d)
     const float f = r.L > 0.f ? INV_SQRT_D / r.L : 0.f;
@@ -829,9 +859,9 @@ hipError_t launch_main(const MainArgs& a, int n_slices, int B, hipStream_t s, hi
   static_assert(C::LDS <= 65536, "attention LDS budget");
   auto kern = a.scores_out != nullptr ? attend_kernel<KB, QJL, VB, G, true> : attend_kernel<KB, QJL, VB, G, false>;
   if (e0 != nullptr || e1 != nullptr)
-    hipExtLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(256), 0, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(NT), 0, s, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -938,19 +968,15 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
   const int B = cache->B;
   const int nblk_max = (max_seq_len + 63) / 64;
   const int units = B * cache->Hkv;
-  // Two workgroups per CU hide latency best when every wave still streams many blocks; when
-  // the context is short, one per CU halves the partial results the merge has to combine.
-  static const int wg_per_cu_env = env_int("TQ_ATTN_WG_PER_CU", 0, 0, 64);
+  // One workgroup of NW waves per CU (two waves per SIMD); each wave streams a run of
+  // consecutive blocks of at least MIN_BLOCKS_PER_WAVE.
   static const int MIN_BLOCKS_PER_WAVE = env_int("TQ_ATTN_MIN_BLOCKS", 2, 1, 1 << 20);
   const int cus = device_cu_count();
-  const int64_t total_blocks = static_cast<int64_t>(units) * nblk_max;
-  const int wg_per_cu = wg_per_cu_env > 0 ? wg_per_cu_env : (total_blocks >= 8ll * 8 * cus ? 2 : 1);
-  const int target_wg = wg_per_cu * cus;
-  int n_slices = (target_wg + units - 1) / units;
-  const int max_slices = std::max(1, (nblk_max + 4 * MIN_BLOCKS_PER_WAVE - 1) / (4 * MIN_BLOCKS_PER_WAVE));
+  int n_slices = (cus + units - 1) / units;
+  const int max_slices = std::max(1, (nblk_max + NW * MIN_BLOCKS_PER_WAVE - 1) / (NW * MIN_BLOCKS_PER_WAVE));
   n_slices = std::max(1, std::min({n_slices, max_slices, MAX_SLICES}));
-  const int bpw = (nblk_max + 4 * n_slices - 1) / (4 * n_slices);
-  n_slices = (nblk_max + 4 * bpw - 1) / (4 * bpw);
+  const int bpw = (nblk_max + NW * n_slices - 1) / (NW * n_slices);
+  n_slices = (nblk_max + NW * bpw - 1) / (NW * bpw);
 
   // groups of 16 slices (one load batch per merger); a single group needs no second level
   const int mgroup = MGROUP;

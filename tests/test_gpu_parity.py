@@ -151,10 +151,10 @@ def test_attention_ragged_lengths(preset, G):
             assert np.all(scores[b, hs, lens[b]:] == 0)
 
 
-@pytest.mark.parametrize("B,G,T_cap,lens", [(2, 8, 10240, [10240, 3001]), (1, 8, 20480, [20480 - 100]),
+@pytest.mark.parametrize("B,G,T_cap,lens", [(2, 8, 10240, [10240, 3001]), (1, 8, 40960, [40960 - 100]),
                                             (1, 4, 262144, [262144 - 37])])
 def test_attention_merge_levels(B, G, T_cap, lens):
-    """Context splits of several sizes: 20 slices (one merge group, the second row leaving
+    """Context splits of several sizes: 10 slices (one merge group, the second row leaving
     most slices empty), 40 slices (groups of 32 and 8), and 256 slices (8 groups of 32).  A
     second call with the same workspace must give identical outputs (the arrival counters are
     reset per call)."""
