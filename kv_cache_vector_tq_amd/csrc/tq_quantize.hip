@@ -403,7 +403,7 @@ struct QuantLaunch {
 
 // Persistent workgroups walk tiles t = ((b * Hkv + h) * nblk_max + i) * 2 + tensor.
 template <int KB, bool QJL, int VB, bool F32>
-__global__ void __launch_bounds__(256) quantize_kernel(QuantLaunch q) {
+__global__ void __launch_bounds__(256, 2) quantize_kernel(QuantLaunch q) {
   __shared__ __attribute__((aligned(16))) Smem sm;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
