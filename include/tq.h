@@ -182,7 +182,8 @@ int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, const void* k,
 
 /* One decode step of attention for all (batch row, q-head) straight from the packed cache.
  * q: device [B][Hq][128] in q_dtype.  q-head h reads kv-head h / (Hq / Hkv); Hq / Hkv must
- *   be 4, 8 or 16.
+ *   be 4, 8 or 16.  Every configuration tq_build_codebook accepts is supported (keys of 0..4
+ *   code bits with or without the sign sketch, values of 1..4 bits).
  * seq_len: device int32 [B], keys 0 .. seq_len[b]-1 are attended (1 <= seq_len[b] <= max_seq_len;
  *   values outside that range are clamped into it on the device).
  * max_seq_len: host bound on seq_len (<= T_cap); sizes the split of the context.

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import (BLOCK_TOKENS, HEAD_DIM, PARAM_NAMES, TQ_DTYPE_BF16, TQ_DTYPE_F32, TQCacheSizes, TQCodebook,
                    TQConfig, TQDevParams, TQError, TQHostParams, TQKVCache, check, lib)
 
-PRESETS = {"turbo3": (2, 1, 3), "turbo4": (3, 1, 4), "qjl1": (0, 1, 3)}
+PRESETS = {"turbo2": (1, 1, 2), "turbo3": (2, 1, 3), "turbo4": (3, 1, 4), "qjl1": (0, 1, 3)}
 
 __all__ = [
     "PRESETS", "Codebook", "DeviceParams", "KVCache", "TQError", "tq_build_codebook", "tq_cache_layout",

@@ -14,7 +14,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
-SOURCES = ["tq_host.cpp", "tq_quantize.hip", "tq_attend.hip"]
+# the attention kernels are instantiated per key code width in translation units of their own
+SOURCES = ["tq_host.cpp", "tq_quantize.hip", "tq_attend.hip"] + [f"tq_attend_k{kb}.hip" for kb in range(5)]
 ARCH = "gfx950"
 
 
@@ -51,7 +52,7 @@ def build(verbose: bool = False) -> str:
             print(msgs)
         return obj
 
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs

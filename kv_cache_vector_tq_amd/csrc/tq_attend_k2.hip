@@ -1,0 +1,10 @@
+// Instantiates the decode-attention kernels for 2-bit key codes (with and without the sign sketch).
+#include "tq_attend_kernels.h"
+
+namespace tq {
+namespace attn {
+
+TQ_ATTN_DISPATCH(2) { return qjl ? dispatch_v<2, true>(a, vb, G, n_slices, B, s, e0, e1) : dispatch_v<2, false>(a, vb, G, n_slices, B, s, e0, e1); }
+
+}  // namespace attn
+}  // namespace tq

@@ -25,7 +25,7 @@ def say(*a):
 
 
 def _setup(preset, B, Hkv, T_cap, seed=0, zero=True):
-    cb = tq.tq_build_codebook(*wl.PRESETS[preset], seed=seed)
+    cb = tq.tq_build_codebook(*(wl.PRESETS[preset] if isinstance(preset, str) else preset), seed=seed)
     dp = tq.upload_params(cb)
     cache = tq.KVCache(cb, B, Hkv, T_cap, zero=zero)
     return cb, dp, cache
@@ -70,7 +70,7 @@ def test_workload_parity(wname, preset):
     say(wname, preset, "codes", stats, "max rel err", max(e["out"] for e in errs), max(e["score"] for e in errs))
 
 
-@pytest.mark.parametrize("preset", ["turbo3", "turbo4", "qjl1"])
+@pytest.mark.parametrize("preset", ["turbo2", "turbo3", "turbo4", "qjl1"])
 def test_ragged_appends_and_canary(preset):
     """Bulk fill from unaligned starts, then one-token and block-crossing appends; slots never
     written keep their canary bytes."""
@@ -184,6 +184,43 @@ def test_attention_merge_levels(B, G, T_cap, lens):
         vg = H.unpack_values(orc, hc, b, 0, lens[b])
         e = H.compare_attention(orc, Q[b], kg, vg, lens[b], out[b], scores[b])
         say("merge-levels", b, lens[b], e)
+
+
+# Bit widths beyond turbo3/turbo4/qjl1 (the same kernels with other code widths): MSE-only
+# keys without the sketch, 1- and 4-bit key codes with and without it, 1-bit values, and
+# asymmetric key/value widths, at each group size.
+@pytest.mark.parametrize("cfg,G", [((1, 1, 2), 4), ((2, 0, 3), 8), ((3, 0, 4), 16), ((1, 0, 1), 8),
+                                   ((4, 1, 4), 4), ((4, 0, 2), 16), ((4, 1, 1), 8), ((1, 1, 4), 16),
+                                   ((0, 1, 1), 4), ((2, 1, 1), 16)])
+def test_bit_mix_variants(cfg, G):
+    B, Hkv, T_cap = 2, 2, 4096
+    lens = [4096, 2500]
+    cb, dp, cache = _setup(cfg, B, Hkv, T_cap)
+    rng = np.random.default_rng(100 * cfg[0] + 10 * cfg[1] + cfg[2])
+    K = wl.round_to_bf16(rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32) * 2)
+    V = wl.round_to_bf16(rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32))
+    Q = wl.round_to_bf16(rng.standard_normal((B, Hkv * G, 128)).astype(np.float32))
+    say("bit-mix", cfg, G, "quantize")
+    tq.tq_quantize_kv(cb, dp, cache, H.to_device(K, "bf16"), H.to_device(V, "bf16"),
+                      torch.zeros(B, dtype=torch.int32, device="cuda"))
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((B, Hkv * G, T_cap), dtype=torch.float32, device="cuda")
+    say("bit-mix", cfg, G, "attend")
+    out = tq.tq_attend_decode(cb, dp, cache, H.to_device(Q, "bf16"), seq, T_cap, scores_out=scores)
+    torch.cuda.synchronize()
+    hc, out, scores = H.cache_host(cache), out.cpu().numpy(), scores.cpu().numpy()
+    orc = H.make_oracle(cfg)
+    stats = {}
+    for b in range(B):
+        for h in range(Hkv):
+            kg = H.unpack_keys(orc, hc, b, h, lens[b])
+            vg = H.unpack_values(orc, hc, b, h, lens[b])
+            H.compare_keys(orc, K[b, h, :lens[b]], kg, stats)
+            H.compare_values(orc, V[b, h, :lens[b]], vg, stats)
+            hs = slice(h * G, (h + 1) * G)
+            H.compare_attention(orc, Q[b, hs], kg, vg, lens[b], out[b, hs], scores[b, hs])
+    H.finish_stats(stats)
+    say("bit-mix", cfg, G, "codes", stats)
 
 
 def test_special_vectors():

@@ -39,7 +39,7 @@ def test_abi_version():
     assert tq.tq_abi_version() == 2
 
 
-@pytest.mark.parametrize("preset", ["turbo3", "turbo4", "qjl1"])
+@pytest.mark.parametrize("preset", ["turbo2", "turbo3", "turbo4", "qjl1"])
 @pytest.mark.parametrize("seed", [0, 1, 12345])
 def test_parameter_build_matches_oracle_bit_for_bit(preset, seed):
     kb, kq, vb = tq.PRESETS[preset]
@@ -84,7 +84,7 @@ def test_bad_head_dim_rejected():
     assert _lib.lib.tq_build_codebook(None, ctypes.byref(cb), None) == _lib.TQ_ERR_INVALID
 
 
-@pytest.mark.parametrize("preset", ["turbo3", "turbo4", "qjl1"])
+@pytest.mark.parametrize("preset", ["turbo2", "turbo3", "turbo4", "qjl1"])
 def test_cache_layout_sizes(preset):
     kb, kq, vb = tq.PRESETS[preset]
     s = tq.tq_cache_layout(kb, kq, vb, 2, 3, 256)
