@@ -50,7 +50,9 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attend_kernel.json")
-ATTEND_SOURCE = os.path.join(ROOT, "kv_cache_vector_tq_amd", "csrc", "tq_attend.hip")
+# sources of the attention kernel: the counter figures hold only for the build they were taken on
+ATTEND_SOURCES = [os.path.join(ROOT, "kv_cache_vector_tq_amd", "csrc", f)
+                  for f in ["tq_attend_kernels.h", "tq_attend.hip"] + [f"tq_attend_k{kb}.hip" for kb in range(5)]]
 
 
 def measured_traffic(workload: str, preset: str):
@@ -61,7 +63,10 @@ def measured_traffic(workload: str, preset: str):
 
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        digest = hashlib.sha256(open(ATTEND_SOURCE, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for f in ATTEND_SOURCES:
+            h.update(open(f, "rb").read())
+        digest = h.hexdigest()
     except (OSError, ValueError):
         return None
     for e in rec.get("entries", []):
