@@ -15,6 +15,12 @@ implementations produce the same matrices:
   matrices are filled row-major.
 * Rotation: G (d x d, rotation stream) = Q U (QR); R = Q diag(sign U_ii), sign 0 -> +1.
   This is a Haar-distributed orthogonal matrix, applied as y = R x.
+* Hadamard rotation mode (page "Google TurboQuant простыми словами", section on TurboQuant
+  in llama.cpp: the rotation sped up through the Hadamard transform; read as the randomized
+  Hadamard transform): R = H diag(s) / sqrt(d), H the Sylvester Hadamard matrix
+  (H_ij = (-1)^popcount(i & j)), s_j = -1 when the top bit of the j-th output of the
+  rotation stream is set, else +1.  y = R x flips signs, then applies the Walsh-Hadamard
+  transform; R is exactly orthogonal.
 * Precision contract: R_hi = bf16(R), R_lo = bf16(R - R_hi) (difference in fp64);
   R_eff = R_hi + R_lo is the matrix both sides apply.  bf16(v) rounds v to fp32 (ties to
   even) and then to bf16 (ties to even).
@@ -92,11 +98,33 @@ def bf16_value(bits) -> np.ndarray:
     return b.view(np.float32).astype(np.float64)
 
 
-def build_params(seed: int, d: int = 128, m: int = None):
+def hadamard_signs(state: int, d: int) -> np.ndarray:
+    """s_j = -1 if the top bit of the j-th SplitMix64 output is set, else +1."""
+    g = SplitMix64(state)
+    return np.array([-1.0 if (g.next() >> 63) else 1.0 for _ in range(d)])
+
+
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """H_ij = (-1)^popcount(i & j) for i, j < d (d a power of two)."""
+    i = np.arange(d)
+    parity = np.array([[bin(a & b).count("1") & 1 for b in i] for a in i])
+    return np.where(parity == 1, -1.0, 1.0)
+
+
+ROTATIONS = ("haar", "hadamard")
+
+
+def build_params(seed: int, d: int = 128, m: int = None, rotation: str = "haar"):
     """Return dict with R (fp64), R_hi/R_lo/S_b bit patterns and their fp64 values, R_eff."""
     m = d if m is None else m
-    G = gaussian_matrix((2 * seed) & MASK64, d, d)
-    R = haar_from_gaussian(G)
+    if rotation == "haar":
+        G = gaussian_matrix((2 * seed) & MASK64, d, d)
+        R = haar_from_gaussian(G)
+    elif rotation == "hadamard":
+        G = None
+        R = sylvester_hadamard(d) * hadamard_signs((2 * seed) & MASK64, d)[None, :] / math.sqrt(d)
+    else:
+        raise ValueError(f"rotation must be one of {ROTATIONS}")
     r_hi = bf16_bits(R)
     r_lo = bf16_bits(R - bf16_value(r_hi))
     S = gaussian_matrix((2 * seed + 1) & MASK64, m, d)

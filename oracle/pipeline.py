@@ -19,11 +19,12 @@ from .quantize import quantize
 
 
 class Oracle:
-    def __init__(self, k_bits: int, k_qjl: int, v_bits: int, seed: int = 0, d: int = 128):
+    def __init__(self, k_bits: int, k_qjl: int, v_bits: int, seed: int = 0, d: int = 128, rotation: str = "haar"):
         if k_bits == 0 and not k_qjl:
             raise ValueError("keys need a scalar code or the sign sketch")
         self.k_bits, self.k_qjl, self.v_bits, self.seed, self.d = k_bits, k_qjl, v_bits, seed, d
-        self.params = build_params(seed, d)
+        self.rotation = rotation
+        self.params = build_params(seed, d, rotation=rotation)
         self.R_eff = self.params["R_eff"]
         self.S_b = self.params["S_b"] if k_qjl else None
         if k_bits > 0:

@@ -1,0 +1,97 @@
+"""Pins of the oracle's Hadamard rotation mode (R = H diag(s) / sqrt(d)), independent of its
+own construction: a fast Walsh-Hadamard transform written here as butterflies, the Kronecker
+construction of H, exact orthogonality, the sign stream, and the distortion of the whole
+value path.  (Page "Google TurboQuant простыми словами", section on TurboQuant in llama.cpp:
+the rotation sped up through the Hadamard transform.)"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle.lloyd_max import codebook_f32, lloyd_max_gaussian
+from oracle.params import SplitMix64, bf16_value, build_params
+from oracle.pipeline import Oracle
+from oracle.quantize import dequantize, quantize
+
+D = 128
+
+
+def fwht(x):
+    """Unnormalized Walsh-Hadamard transform along the last axis, in place butterflies."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    n = y.shape[-1]
+    h = 1
+    while h < n:
+        for i in range(0, n, 2 * h):
+            a = y[..., i:i + h].copy()
+            b = y[..., i + h:i + 2 * h].copy()
+            y[..., i:i + h] = a + b
+            y[..., i + h:i + 2 * h] = a - b
+        h *= 2
+    return y
+
+
+def kronecker_hadamard(n):
+    H = np.array([[1.0]])
+    while H.shape[0] < n:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+@pytest.mark.parametrize("seed", [0, 1, 777])
+def test_rotation_is_sign_flip_then_walsh_hadamard(seed):
+    p = build_params(seed, rotation="hadamard")
+    g = SplitMix64(2 * seed)
+    s = np.array([-1.0 if (g.next() >> 63) else 1.0 for _ in range(D)])
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((5, D))
+    np.testing.assert_allclose(x @ p["R"].T, fwht(x * s) / math.sqrt(D), rtol=0, atol=1e-13)
+    # H itself: the Kronecker construction, and R = H diag(s) / sqrt(d) entry by entry
+    H = kronecker_hadamard(D)
+    np.testing.assert_array_equal(p["R"] * math.sqrt(D), H * s[None, :])
+    # both signs occur (the stream is not degenerate) and the first row is s / sqrt(d)
+    assert 0 < np.sum(s > 0) < D
+    np.testing.assert_array_equal(p["R"][0] * math.sqrt(D), s)
+
+
+def test_orthogonality_exact_and_after_the_bf16_split():
+    p = build_params(0, rotation="hadamard")
+    assert np.abs(p["R"].T @ p["R"] - np.eye(D)).max() < 1e-14
+    E = p["R_eff"].T @ p["R_eff"]
+    # every entry of R_eff has the same magnitude, so distinct columns stay exactly orthogonal
+    assert np.all(E[~np.eye(D, dtype=bool)] == 0.0)
+    assert np.abs(np.diag(E) - 1.0).max() < 1e-5
+    # the bf16 pair: hi is 1/sqrt(d) rounded to bf16, lo the bf16 of the remainder
+    hi = bf16_value(p["r_hi"])
+    assert np.all(np.abs(hi) == np.abs(hi[0, 0]))
+    assert abs(abs(hi[0, 0]) - 1 / math.sqrt(D)) < 2 ** -9 / math.sqrt(D)
+
+
+def test_sketch_and_codebooks_do_not_depend_on_the_rotation():
+    a, b = build_params(5), build_params(5, rotation="hadamard")
+    np.testing.assert_array_equal(a["s_b"], b["s_b"])
+    assert not np.array_equal(a["r_hi"], b["r_hi"])
+    with pytest.raises(ValueError):
+        build_params(0, rotation="dct")
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_distortion_of_random_unit_vectors(bits):
+    # Random unit vectors through the value path with the Hadamard rotation: the rotated
+    # coordinates are close to N(0, 1/d), so the normalized MSE is close to the Gaussian
+    # optimum D_b, as with the Haar rotation.
+    c, t, _ = codebook_f32(bits)
+    _, _, Db, _ = lloyd_max_gaussian(bits)
+    p = build_params(3, rotation="hadamard")
+    rng = np.random.default_rng(200 + bits)
+    x = rng.standard_normal((20000, D))
+    x /= np.linalg.norm(x, axis=1)[:, None]
+    q = quantize(x, p["R_eff"], c, t, None)
+    xh = dequantize(q, p["R_eff"], c, None)
+    mse = np.mean(np.sum((x - xh) ** 2, axis=1))
+    assert -0.04 <= mse / Db - 1 <= 0.01
+
+
+def test_pipeline_takes_the_mode():
+    o = Oracle(2, 1, 3, seed=0, rotation="hadamard")
+    np.testing.assert_array_equal(o.R_eff, build_params(0, rotation="hadamard")["R_eff"])
