@@ -22,8 +22,9 @@ D = 128
 # Presets: (k_bits, k_qjl, v_bits).  "turbo3" / "turbo4" are the cache types named on
 # the llama.cpp benchmark page ("KV cache benchmark Qwen 3.6-35B-A3B", tables 1-3);
 # their bit splits follow the workload definitions (2+1 / 3 and 3+1 / 4).  "turbo2" is the
-# 2-bit preset of the fork named in "Google TurboQuant простыми словами" (section on
-# implementations), read the same way: 1-bit key code + sign, 2-bit values.  "qjl1" keeps
+# 2-bit preset of the fork named in "Когда в марте 2026 года Google опубликовала статью..."
+# (paragraph on community implementations), read the same way: 1-bit key code + sign,
+# 2-bit values.  "qjl1" keeps
 # only the 1-bit sign sketch for keys.
 PRESETS = {
     "turbo2": (1, 1, 2),
