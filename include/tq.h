@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 2
+#define TQ_ABI_VERSION 3
 #define TQ_HEAD_DIM 128
 #define TQ_BLOCK_TOKENS 64
 
@@ -50,15 +50,21 @@ enum {
 
 typedef enum { TQ_DTYPE_BF16 = 0, TQ_DTYPE_F32 = 1 } tq_dtype;
 
+/* Rotation modes (tq_config.rotation). */
+#define TQ_ROTATION_HAAR 0     /* seeded Haar-random orthogonal matrix */
+#define TQ_ROTATION_HADAMARD 1 /* randomized Walsh-Hadamard: H diag(s) / sqrt(d) */
+
 /* Cache configuration.  k_bits: scalar code bits per key coordinate (0..4; 0 = keys keep
  * only the sign sketch); k_qjl: 1 = keys carry the 1-bit sign sketch of their residual;
- * v_bits: value code bits (1..4); seed: fixes the rotation and the sketch.  Presets:
- * turbo3 = (2, 1, 3), turbo4 = (3, 1, 4), sign-only keys = (0, 1, 3). */
+ * v_bits: value code bits (1..4); rotation: TQ_ROTATION_*; seed: fixes the rotation and the
+ * sketch.  Presets: turbo2 = (1, 1, 2), turbo3 = (2, 1, 3), turbo4 = (3, 1, 4), sign-only
+ * keys = (0, 1, 3). */
 typedef struct tq_config {
   int32_t d;
   int32_t k_bits;
   int32_t k_qjl;
   int32_t v_bits;
+  int32_t rotation;
   uint64_t seed;
 } tq_config;
 
@@ -149,12 +155,16 @@ typedef struct tq_cache_sizes {
 /* One-time parameter build, host only, deterministic in cfg->seed.
  * Fills *cb with the key and value codebooks (Lloyd-Max fixed point for N(0,1)) and, when
  * out is not NULL, the parameter matrices of tq_host_params:
- *   G = 128x128 N(0,1) from SplitMix64 started at state 2*seed (Box-Muller, row-major);
- *   R = Q diag(sign U_ii) from the Householder QR G = Q U (a Haar rotation);
+ *   Haar mode: G = 128x128 N(0,1) from SplitMix64 started at state 2*seed (Box-Muller,
+ *     row-major); R = Q diag(sign U_ii) from the Householder QR G = Q U;
+ *   Hadamard mode (the Hadamard-transform speed-up named in "Google TurboQuant простыми
+ *     словами", section on TurboQuant in llama.cpp): R = H diag(s) / sqrt(128) with
+ *     H_ij = (-1)^popcount(i & j) and s_j = -1 when the top bit of the j-th output of the
+ *     stream started at 2*seed is set, else +1;
  *   R_hi = bf16(R), R_lo = bf16(R - R_hi), bf16() = round to fp32 then to bf16, ties to even;
  *   S_b = bf16(S), S = 128x128 N(0,1) from the stream started at 2*seed + 1.
  * Errors: TQ_ERR_INVALID (NULL cfg/cb), TQ_ERR_UNSUPPORTED (d != 128, k_bits outside 0..4,
- * v_bits outside 1..4, k_qjl not 0/1, or k_bits == 0 with k_qjl == 0). */
+ * v_bits outside 1..4, k_qjl not 0/1, k_bits == 0 with k_qjl == 0, or an unknown rotation). */
 int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, tq_host_params* out);
 
 /* Sizes of the cache arrays for B x Hkv x T_cap slots (T_cap a positive multiple of 64).

@@ -13,8 +13,8 @@ from dataclasses import dataclass
 import numpy as np
 
 from . import _lib
-from ._lib import (BLOCK_TOKENS, HEAD_DIM, PARAM_NAMES, TQ_DTYPE_BF16, TQ_DTYPE_F32, TQCacheSizes, TQCodebook,
-                   TQConfig, TQDevParams, TQError, TQHostParams, TQKVCache, check, lib)
+from ._lib import (BLOCK_TOKENS, HEAD_DIM, PARAM_NAMES, ROTATIONS, TQ_DTYPE_BF16, TQ_DTYPE_F32, TQCacheSizes,
+                   TQCodebook, TQConfig, TQDevParams, TQError, TQHostParams, TQKVCache, check, lib)
 
 PRESETS = {"turbo2": (1, 1, 2), "turbo3": (2, 1, 3), "turbo4": (3, 1, 4), "qjl1": (0, 1, 3)}
 
@@ -72,12 +72,16 @@ class Codebook:
         return np.array(self.cb.v_thresholds[: (1 << self.cfg.v_bits) - 1], dtype=np.float32)
 
 
-def _config(k_bits, k_qjl, v_bits, seed) -> TQConfig:
-    return TQConfig(HEAD_DIM, int(k_bits), int(k_qjl), int(v_bits), int(seed))
+def _config(k_bits, k_qjl, v_bits, seed, rotation="haar") -> TQConfig:
+    if rotation not in ROTATIONS:
+        raise ValueError(f"rotation must be one of {sorted(ROTATIONS)}")
+    return TQConfig(HEAD_DIM, int(k_bits), int(k_qjl), int(v_bits), ROTATIONS[rotation], int(seed))
 
 
-def tq_build_codebook(k_bits: int, k_qjl: int, v_bits: int, seed: int = 0) -> Codebook:
-    cfg = _config(k_bits, k_qjl, v_bits, seed)
+def tq_build_codebook(k_bits: int, k_qjl: int, v_bits: int, seed: int = 0, rotation: str = "haar") -> Codebook:
+    """rotation: "haar" (seeded Haar-random orthogonal matrix) or "hadamard" (randomized
+    Walsh-Hadamard); see tq_build_codebook in include/tq.h."""
+    cfg = _config(k_bits, k_qjl, v_bits, seed, rotation)
     cb = TQCodebook()
     mats = {n: np.zeros((HEAD_DIM, HEAD_DIM), dtype=np.uint16) for n in PARAM_NAMES}
     hp = TQHostParams(*(mats[n].ctypes.data for n in PARAM_NAMES))

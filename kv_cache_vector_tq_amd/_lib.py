@@ -31,7 +31,11 @@ ERROR_NAMES = {
 
 class TQConfig(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("k_bits", ctypes.c_int32), ("k_qjl", ctypes.c_int32),
-                ("v_bits", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+                ("v_bits", ctypes.c_int32), ("rotation", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+TQ_ROTATION_HAAR, TQ_ROTATION_HADAMARD = 0, 1
+ROTATIONS = {"haar": TQ_ROTATION_HAAR, "hadamard": TQ_ROTATION_HADAMARD}
 
 
 class TQCodebook(ctypes.Structure):

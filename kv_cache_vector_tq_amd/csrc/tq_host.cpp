@@ -39,6 +39,8 @@ int check_config(const tq_config& cfg) {
   if (cfg.k_qjl != 0 && cfg.k_qjl != 1) return fail(TQ_ERR_UNSUPPORTED, "k_qjl must be 0 or 1");
   if (cfg.k_bits == 0 && cfg.k_qjl == 0)
     return fail(TQ_ERR_UNSUPPORTED, "keys need a scalar code (k_bits > 0) or the sign sketch");
+  if (cfg.rotation != TQ_ROTATION_HAAR && cfg.rotation != TQ_ROTATION_HADAMARD)
+    return fail(TQ_ERR_UNSUPPORTED, "rotation must be TQ_ROTATION_HAAR or TQ_ROTATION_HADAMARD");
   return TQ_OK;
 }
 
@@ -135,6 +137,19 @@ void gaussian_fill(uint64_t state, double* out, int n) {
     out[i++] = r * std::cos(2.0 * M_PI * u2);
     if (i < n) out[i++] = r * std::sin(2.0 * M_PI * u2);
   }
+}
+
+// ---- randomized Walsh-Hadamard rotation: R = H diag(s) / sqrt(d) ------------------------
+// H_ij = (-1)^popcount(i & j) (Sylvester); s_j = -1 when the top bit of the j-th output of
+// the stream is set.  R x flips the signs of x, then applies the Walsh-Hadamard transform.
+void hadamard_rotation(uint64_t state, double* R, int d) {
+  SplitMix64 g{state};
+  std::vector<double> s(d);
+  for (int j = 0; j < d; ++j) s[j] = (g.next() >> 63) ? -1.0 : 1.0;
+  const double inv = 1.0 / std::sqrt(static_cast<double>(d));
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < d; ++j)
+      R[i * d + j] = ((__builtin_popcount(static_cast<unsigned>(i & j)) & 1) ? -inv : inv) * s[j];
 }
 
 // ---- Householder QR: G = Q U; returns Q diag(sign U_kk) --------------------------------
@@ -237,8 +252,12 @@ int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, tq_host_params* out
   const int d = cfg->d;
   const size_t n = static_cast<size_t>(d) * d;
   std::vector<double> G(n), R(n), Reff(n), S(n), Sb(n);
-  gaussian_fill(2ull * cfg->seed, G.data(), d * d);
-  haar_rotation(G.data(), R.data(), d);
+  if (cfg->rotation == TQ_ROTATION_HADAMARD) {
+    hadamard_rotation(2ull * cfg->seed, R.data(), d);
+  } else {
+    gaussian_fill(2ull * cfg->seed, G.data(), d * d);
+    haar_rotation(G.data(), R.data(), d);
+  }
   for (int i = 0; i < d; ++i)
     for (int j = 0; j < d; ++j) {
       const double r = R[static_cast<size_t>(i) * d + j];

@@ -137,9 +137,9 @@ def compare_attention(orc: Oracle, q: np.ndarray, k: dict, v: dict, T: int, got_
     return err
 
 
-def make_oracle(preset, seed: int = 0) -> Oracle:
+def make_oracle(preset, seed: int = 0, rotation: str = "haar") -> Oracle:
     """preset: a name of tq_workloads.PRESETS or a (k_bits, k_qjl, v_bits) tuple."""
-    return Oracle(*(wl.PRESETS[preset] if isinstance(preset, str) else preset), seed=seed)
+    return Oracle(*(wl.PRESETS[preset] if isinstance(preset, str) else preset), seed=seed, rotation=rotation)
 
 
 def hc_inputs_bf16(w: wl.Workload):

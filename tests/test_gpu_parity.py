@@ -24,8 +24,9 @@ def say(*a):
     sys.stdout.flush()
 
 
-def _setup(preset, B, Hkv, T_cap, seed=0, zero=True):
-    cb = tq.tq_build_codebook(*(wl.PRESETS[preset] if isinstance(preset, str) else preset), seed=seed)
+def _setup(preset, B, Hkv, T_cap, seed=0, zero=True, rotation="haar"):
+    cb = tq.tq_build_codebook(*(wl.PRESETS[preset] if isinstance(preset, str) else preset), seed=seed,
+                              rotation=rotation)
     dp = tq.upload_params(cb)
     cache = tq.KVCache(cb, B, Hkv, T_cap, zero=zero)
     return cb, dp, cache
@@ -189,6 +190,41 @@ def test_attention_merge_levels(B, G, T_cap, lens):
 # Bit widths beyond turbo3/turbo4/qjl1 (the same kernels with other code widths): MSE-only
 # keys without the sketch, 1- and 4-bit key codes with and without it, 1-bit values, and
 # asymmetric key/value widths, at each group size.
+@pytest.mark.parametrize("preset,G,dtype", [("turbo3", 4, "bf16"), ("turbo4", 8, "bf16"), ("qjl1", 16, "f32")])
+def test_hadamard_rotation(preset, G, dtype):
+    """The randomized Walsh-Hadamard rotation mode: same kernels, parameters from the other
+    builder; codes, scores and outputs against the oracle in that mode (bf16 and fp32 inputs)."""
+    B, Hkv, T_cap = 1, 2, 3072
+    lens = [3000]
+    cb, dp, cache = _setup(preset, B, Hkv, T_cap, seed=4, rotation="hadamard")
+    rng = np.random.default_rng(31)
+    K = rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32) * 1.5
+    V = rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32)
+    Q = rng.standard_normal((B, Hkv * G, 128)).astype(np.float32)
+    if dtype == "bf16":
+        K, V, Q = wl.round_to_bf16(K), wl.round_to_bf16(V), wl.round_to_bf16(Q)
+    say("hadamard", preset, G, dtype, "quantize")
+    tq.tq_quantize_kv(cb, dp, cache, H.to_device(K, dtype), H.to_device(V, dtype),
+                      torch.zeros(B, dtype=torch.int32, device="cuda"))
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((B, Hkv * G, T_cap), dtype=torch.float32, device="cuda")
+    say("hadamard", preset, G, dtype, "attend")
+    out = tq.tq_attend_decode(cb, dp, cache, H.to_device(Q, dtype), seq, T_cap, scores_out=scores)
+    torch.cuda.synchronize()
+    hc, out, scores = H.cache_host(cache), out.cpu().numpy(), scores.cpu().numpy()
+    orc = H.make_oracle(preset, seed=4, rotation="hadamard")
+    stats = {}
+    for h in range(Hkv):
+        kg = H.unpack_keys(orc, hc, 0, h, lens[0])
+        vg = H.unpack_values(orc, hc, 0, h, lens[0])
+        H.compare_keys(orc, K[0, h, :lens[0]], kg, stats)
+        H.compare_values(orc, V[0, h, :lens[0]], vg, stats)
+        hs = slice(h * G, (h + 1) * G)
+        H.compare_attention(orc, Q[0, hs], kg, vg, lens[0], out[0, hs], scores[0, hs])
+    H.finish_stats(stats)
+    say("hadamard", preset, G, dtype, "codes", stats)
+
+
 @pytest.mark.parametrize("cfg,G", [((1, 1, 2), 4), ((2, 0, 3), 8), ((3, 0, 4), 16), ((1, 0, 1), 8),
                                    ((4, 1, 4), 4), ((4, 0, 2), 16), ((4, 1, 1), 8), ((1, 1, 4), 16),
                                    ((0, 1, 1), 4), ((2, 1, 1), 16)])

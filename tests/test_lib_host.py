@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert tq.tq_abi_version() == 2
+    assert tq.tq_abi_version() == 3
 
 
 @pytest.mark.parametrize("preset", ["turbo2", "turbo3", "turbo4", "qjl1"])
@@ -67,6 +67,30 @@ def test_parameter_build_matches_oracle_bit_for_bit(preset, seed):
         assert abs(cb.cb.k_mse - kmse) < 1e-15
 
 
+@pytest.mark.parametrize("preset", ["turbo3", "qjl1"])
+@pytest.mark.parametrize("seed", [0, 9])
+def test_hadamard_parameter_build_matches_oracle_bit_for_bit(preset, seed):
+    kb, kq, vb = tq.PRESETS[preset]
+    cb = tq.tq_build_codebook(kb, kq, vb, seed, rotation="hadamard")
+    p = build_params(seed, rotation="hadamard")
+    np.testing.assert_array_equal(cb.r_hi, p["r_hi"])
+    np.testing.assert_array_equal(cb.r_lo, p["r_lo"])
+    np.testing.assert_array_equal(cb.rt_hi, p["r_hi"].T)
+    np.testing.assert_array_equal(cb.s_qjl, p["s_b"])
+    M = p["S_b"] @ p["R_eff"]
+    np.testing.assert_array_equal(cb.m_hi, bf16_bits(M))
+    assert cb.cb.cfg.rotation == _lib.TQ_ROTATION_HADAMARD
+
+
+def test_unknown_rotation_rejected():
+    cfg = _lib.TQConfig(128, 2, 1, 3, 7, 0)
+    cb = _lib.TQCodebook()
+    assert _lib.lib.tq_build_codebook(ctypes.byref(cfg), ctypes.byref(cb), None) == _lib.TQ_ERR_UNSUPPORTED
+    assert b"rotation" in _lib.lib.tq_last_error()
+    with pytest.raises(ValueError):
+        tq.tq_build_codebook(2, 1, 3, rotation="dct")
+
+
 @pytest.mark.parametrize("bad", [dict(k_bits=0, k_qjl=0, v_bits=3), dict(k_bits=5, k_qjl=1, v_bits=3),
                                  dict(k_bits=2, k_qjl=2, v_bits=3), dict(k_bits=2, k_qjl=1, v_bits=0),
                                  dict(k_bits=2, k_qjl=1, v_bits=5)])
@@ -77,7 +101,7 @@ def test_bad_configs_rejected(bad):
 
 
 def test_bad_head_dim_rejected():
-    cfg = _lib.TQConfig(64, 2, 1, 3, 0)
+    cfg = _lib.TQConfig(64, 2, 1, 3, 0, 0)
     cb = _lib.TQCodebook()
     assert _lib.lib.tq_build_codebook(ctypes.byref(cfg), ctypes.byref(cb), None) == _lib.TQ_ERR_UNSUPPORTED
     assert b"d = 128" in _lib.lib.tq_last_error()
