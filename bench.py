@@ -296,10 +296,12 @@ def main():
     seq = torch.full((B,), T, dtype=torch.int32, device=dev)
     ws = torch.zeros(tq.attend_workspace_bytes(cb, dp, caches[0], Hq, T), dtype=torch.uint8, device=dev)
 
+    # per layer: the new token's quantize-on-write, then attention (tq_decode_step: the query
+    # rotation rides in the quantize launch, so two launches per layer)
     def step():
         for l in range(L):
-            tq.tq_quantize_kv(cb, dp, caches[l], k_new[l], v_new[l], start)
-            tq.tq_attend_decode(cb, dp, caches[l], qs_l[l], seq, T, out=outs[l], workspace=ws)
+            tq.tq_decode_step(cb, dp, caches[l], k_new[l], v_new[l], start, qs_l[l], seq, T, out=outs[l],
+                              workspace=ws)
 
     step()
     torch.cuda.synchronize()
@@ -396,7 +398,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "preset": args.preset, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": 128, "context": T, "layers": L, "bytes_per_key": bytes_per_key,
-                   "step": "per layer: quantize-on-write of 1 new token (K+V) then decode attention"},
+                   "step": "per layer: quantize-on-write of 1 new token (K+V) then decode attention (tq_decode_step)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name, args.preset),
                      "kernel": "attend_kernel (main decode attention)", "bytes_per_launch": bytes_per_launch,

@@ -216,6 +216,20 @@ int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_
                      int max_seq_len, float scale, float* out, float* scores_out,
                      void* workspace, size_t* workspace_bytes, void* hip_stream);
 
+/* One decode step of a layer in two launches: quantize-on-write of one new token per
+ * (batch row, kv-head) exactly as tq_quantize_kv with n_new = 1 (k, v, kv_dtype, strides and
+ * start_pos as there; the token is at offset b*kv_stride_b + h*kv_stride_h), then attention
+ * exactly as tq_attend_decode.  The query rotation that tq_attend_decode launches on its own
+ * runs here inside the quantize launch (the two share no data), so a step costs one launch
+ * less.  seq_len must count the new token.  Workspace, outputs and errors as tq_attend_decode
+ * (a workspace query, workspace == NULL, launches nothing); the append's argument errors are
+ * those of tq_quantize_kv, also detected before any launch. */
+int tq_decode_step(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache,
+                   const void* k, const void* v, tq_dtype kv_dtype, int64_t kv_stride_b,
+                   int64_t kv_stride_h, const int32_t* start_pos, const void* q, tq_dtype q_dtype,
+                   int Hq, const int32_t* seq_len, int max_seq_len, float scale, float* out,
+                   float* scores_out, void* workspace, size_t* workspace_bytes, void* hip_stream);
+
 /* Diagnostic timing hook (for benchmarks): events (hipEvent_t, created by the caller) that
  * later calls on this thread record on their stream, attend_* immediately before and after
  * the main attention kernel of tq_attend_decode (scores, softmax, value sums, merge over

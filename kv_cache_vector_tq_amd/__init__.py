@@ -20,6 +20,7 @@ PRESETS = {"turbo2": (1, 1, 2), "turbo3": (2, 1, 3), "turbo4": (3, 1, 4), "qjl1"
 
 __all__ = [
     "PRESETS", "Codebook", "DeviceParams", "KVCache", "TQError", "tq_build_codebook", "tq_cache_layout",
+    "tq_decode_step",
     "tq_quantize_kv", "tq_attend_decode", "tq_abi_version", "tq_profile_events", "upload_params",
     "attend_workspace_bytes",
 ]
@@ -212,3 +213,39 @@ def tq_attend_decode(codebook: Codebook, params: DeviceParams, cache: KVCache, q
                                out.data_ptr(), scores_out.data_ptr() if scores_out is not None else None,
                                workspace.data_ptr(), ctypes.byref(n), _stream(q.device)), "tq_attend_decode")
     return out
+
+
+def tq_decode_step(codebook: Codebook, params: DeviceParams, cache: KVCache, k, v, start_pos, q, seq_len,
+                   max_seq_len: int, scale: float = 0.0, out=None, scores_out=None, workspace=None):
+    """One layer's decode step: quantize the new token k, v ([B, Hkv, 1, 128], last dim
+    contiguous; either may be None) into slots start_pos[b], then attend as tq_attend_decode
+    (seq_len counts the new token).  Returns out [B, Hq, 128] fp32."""
+    import torch
+
+    ref = k if k is not None else v
+    if ref is None:
+        raise ValueError("k and v are both None")
+    if k is not None and v is not None and (k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype):
+        raise ValueError("k and v must share shape, strides and dtype")
+    if ref.dim() != 4 or ref.shape[2] != 1 or ref.shape[-1] != HEAD_DIM or ref.stride(-1) != 1:
+        raise ValueError("new tokens must be [B, Hkv, 1, 128] with contiguous rows")
+    if q.dim() != 3 or q.shape[-1] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, 128] tensor")
+    B, Hq, _ = q.shape
+    if B != cache.B:
+        raise ValueError("q batch does not match the cache")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = attend_workspace_bytes(codebook, params, cache, Hq, max_seq_len)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(workspace.numel())
+    sb, sh, _, _ = ref.stride()
+    check(lib.tq_decode_step(ctypes.byref(codebook.cb), ctypes.byref(params.struct), ctypes.byref(cache.struct),
+                             k.data_ptr() if k is not None else None, v.data_ptr() if v is not None else None,
+                             _dtype_code(ref), sb, sh, start_pos.data_ptr(), q.data_ptr(), _dtype_code(q), Hq,
+                             seq_len.data_ptr(), max_seq_len, float(scale), out.data_ptr(),
+                             scores_out.data_ptr() if scores_out is not None else None, workspace.data_ptr(),
+                             ctypes.byref(n), _stream(q.device)), "tq_decode_step")
+    return out
+

@@ -82,12 +82,23 @@ int device_cu_count() {
 
 }  // namespace tq
 
-extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache,
-                                const void* q, tq_dtype q_dtype, int Hq, const int32_t* seq_len, int max_seq_len,
-                                float scale, float* out, float* scores_out, void* workspace,
-                                size_t* workspace_bytes, void* hip_stream) {
-  using namespace tq;
-  clear_error();
+namespace tq {
+namespace {
+
+// New tokens of a decode step, quantized by the launch that also rotates the queries.
+struct StepAppend {
+  const void* k;
+  const void* v;
+  tq_dtype dtype;
+  int64_t stride_b, stride_h;
+  const int32_t* start_pos;
+};
+
+// tq_attend_decode; with step != NULL the query rotation runs inside the quantize launch of
+// the step's new tokens instead of a launch of its own.
+int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache, const void* q, tq_dtype q_dtype,
+           int Hq, const int32_t* seq_len, int max_seq_len, float scale, float* out, float* scores_out,
+           void* workspace, size_t* workspace_bytes, void* hip_stream, const StepAppend* step) {
   if (cb == nullptr || p == nullptr || cache == nullptr || q == nullptr || seq_len == nullptr || out == nullptr ||
       workspace_bytes == nullptr)
     return fail(TQ_ERR_INVALID, "cb, p, cache, q, seq_len, out and workspace_bytes must not be NULL");
@@ -149,14 +160,24 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
                                : nullptr;
   if (scale == 0.f) scale = INV_SQRT_D;
 
-  PrologueArgs pa{q, p->r_hi, p->r_lo, cb->cfg.k_qjl ? p->m_hi : nullptr, cb->cfg.k_qjl ? p->m_lo : nullptr, qrec, G,
-                  q_dtype == TQ_DTYPE_F32 ? 1 : 0};
-  if (cb->cfg.k_qjl)
-    hipLaunchKernelGGL(prologue_kernel<true>, dim3(B * cache->Hkv, 4), dim3(64), 0, s, pa);
-  else
-    hipLaunchKernelGGL(prologue_kernel<false>, dim3(B * cache->Hkv, 4), dim3(64), 0, s, pa);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("query prologue launch: ") + hipGetErrorString(e));
+  const uint16_t* m_hi = cb->cfg.k_qjl ? p->m_hi : nullptr;
+  const uint16_t* m_lo = cb->cfg.k_qjl ? p->m_lo : nullptr;
+  if (step != nullptr) {
+    // the step's new tokens and the query rotation in one launch (it validates the append on
+    // the host and launches nothing when that fails)
+    const QueryRotationArgs rot{q, q_dtype == TQ_DTYPE_F32 ? 1 : 0, G, units, qrec, p->r_hi, p->r_lo, m_hi, m_lo};
+    rc = quantize_launch(cb, p, step->k, step->v, step->dtype, B, cache->Hkv, 1, step->stride_b, step->stride_h, D,
+                         step->start_pos, cache, hip_stream, &rot);
+    if (rc != TQ_OK) return rc;
+  } else {
+    PrologueArgs pa{q, p->r_hi, p->r_lo, m_hi, m_lo, qrec, G, q_dtype == TQ_DTYPE_F32 ? 1 : 0};
+    if (cb->cfg.k_qjl)
+      hipLaunchKernelGGL(prologue_kernel<true>, dim3(units, 4), dim3(64), 0, s, pa);
+    else
+      hipLaunchKernelGGL(prologue_kernel<false>, dim3(units, 4), dim3(64), 0, s, pa);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("query prologue launch: ") + hipGetErrorString(e));
+  }
 
   MainArgs ma{};
   ma.k_codes = cache->k_codes;
@@ -193,7 +214,30 @@ extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, c
     e0 = reinterpret_cast<hipEvent_t>(pe.attend_start);
     e1 = reinterpret_cast<hipEvent_t>(pe.attend_stop);
   }
-  e = dispatch_main(ma, cb->cfg, G, n_slices, B, s, e0, e1);
+  const hipError_t e = dispatch_main(ma, cb->cfg, G, n_slices, B, s, e0, e1);
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("attention launch: ") + hipGetErrorString(e));
   return TQ_OK;
+}
+
+}  // namespace
+}  // namespace tq
+
+extern "C" int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache,
+                                const void* q, tq_dtype q_dtype, int Hq, const int32_t* seq_len, int max_seq_len,
+                                float scale, float* out, float* scores_out, void* workspace,
+                                size_t* workspace_bytes, void* hip_stream) {
+  tq::clear_error();
+  return tq::attend(cb, p, cache, q, q_dtype, Hq, seq_len, max_seq_len, scale, out, scores_out, workspace,
+                    workspace_bytes, hip_stream, nullptr);
+}
+
+extern "C" int tq_decode_step(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache,
+                              const void* k, const void* v, tq_dtype kv_dtype, int64_t kv_stride_b,
+                              int64_t kv_stride_h, const int32_t* start_pos, const void* q, tq_dtype q_dtype,
+                              int Hq, const int32_t* seq_len, int max_seq_len, float scale, float* out,
+                              float* scores_out, void* workspace, size_t* workspace_bytes, void* hip_stream) {
+  tq::clear_error();
+  const tq::StepAppend step{k, v, kv_dtype, kv_stride_b, kv_stride_h, start_pos};
+  return tq::attend(cb, p, cache, q, q_dtype, Hq, seq_len, max_seq_len, scale, out, scores_out, workspace,
+                    workspace_bytes, hip_stream, &step);
 }

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "tq_common.h"
+#include "tq_qrot.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -195,138 +196,14 @@ __device__ __forceinline__ void load_dwords(uint32_t* dst, const uint8_t* src) {
     *reinterpret_cast<u32x4*>(dst + 4 * i) = *reinterpret_cast<const u32x4*>(src + 16 * i);
 }
 
-// ---- query rotation ---------------------------------------------------------------------------
-// At its start every workgroup computes, for the G (<= 16) q-heads of its kv-head,
-// q1 = R_eff q and q2 = S_b q1 = M q (M = S_b R_eff, given as the bf16 pair m_hi + m_lo) as
-// 16x16x32 bf16 MFMA products: the q-heads are the M rows, the wave's 32 output coordinates
-// the N columns.  A bf16 query is exact in one bf16 term and an fp32 query is split into
-// three, so the products are exact and the sums fp32.  The results are staged in LDS with
-// each head's largest magnitude, from which the f16 MFMA operands of the score products get
-// a power-of-two scale.
-constexpr int QS = 132;  // LDS row stride (floats) of q1 and q2
-
-__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
-}
-
-// Operands of one lane: rows o = 32 wave + 16 nt + col of R_hi, R_lo, M_hi, M_lo (k-slots
-// 32 g + 8 kb + e) and the raw words of the query of head col at the same coordinates
-// (8 x 16 bytes for fp32, the first 4 x 16 bytes for bf16).  Everything is loaded in one
-// batch; the query is converted only when first used.
-template <bool QJL>
-struct QOperands {
-  bf16x8 rh[2][4], rl[2][4], mh[QJL ? 2 : 1][4], ml[QJL ? 2 : 1][4];
-  u32x4 raw[8];
-  bool valid;  // col < G
-};
-
-template <bool QJL>
-__device__ __forceinline__ void load_query_operands(QOperands<QJL>& o, const void* q, bool q_f32, int64_t head0,
-                                                    int G, const uint16_t* r_hi, const uint16_t* r_lo,
-                                                    const uint16_t* m_hi, const uint16_t* m_lo, int wave, int col,
-                                                    int g) {
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int row = 32 * wave + 16 * nt + col;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      o.rh[nt][kb] = load_bf16x8(r_hi + row * D + 32 * g + 8 * kb);
-      o.rl[nt][kb] = load_bf16x8(r_lo + row * D + 32 * g + 8 * kb);
-      if constexpr (QJL) {
-        o.mh[nt][kb] = load_bf16x8(m_hi + row * D + 32 * g + 8 * kb);
-        o.ml[nt][kb] = load_bf16x8(m_lo + row * D + 32 * g + 8 * kb);
-      }
-    }
-  }
-  // unconditional loads from clamped, in-bounds addresses (no branch that would force an
-  // early wait); lanes of rows >= G and the unused chunks of a bf16 query are masked on use
-  const int esz = q_f32 ? 4 : 2;
-  o.valid = col < G;
-  const uint8_t* base = reinterpret_cast<const uint8_t*>(q) + ((head0 + (o.valid ? col : 0)) * D + 32 * g) * esz;
-  const int last = q_f32 ? 7 : 3;  // last 16-byte chunk of this lane's 32 coordinates
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o.raw[i] = *reinterpret_cast<const u32x4*>(base + 16 * min(i, last));
-}
-
-// Accumulates the products of one k-block for both output tiles: q1 += a (r_hi + r_lo),
-// q2 += a (m_hi + m_lo).
-template <bool QJL>
-__device__ __forceinline__ void rotate_step(const QOperands<QJL>& o, int kb, bf16x8 a, f32x4* d1, f32x4* d2) {
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    d1[nt] = mfma_bf16(a, o.rh[nt][kb], d1[nt]);
-    d1[nt] = mfma_bf16(a, o.rl[nt][kb], d1[nt]);
-    if constexpr (QJL) {
-      d2[nt] = mfma_bf16(a, o.mh[nt][kb], d2[nt]);
-      d2[nt] = mfma_bf16(a, o.ml[nt][kb], d2[nt]);
-    }
-  }
-}
-
-// d1 += q (R_hi + R_lo), d2 += q (M_hi + M_lo) for the lane's output tiles (all k-blocks).
-template <bool QJL>
-__device__ __forceinline__ void rotate_products(const QOperands<QJL>& o, bool q_f32, f32x4* d1, f32x4* d2) {
-  const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-  if (q_f32) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float x[8];
-      const u32x4 lo = o.raw[2 * kb], hi = o.raw[2 * kb + 1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = o.valid ? __uint_as_float(lo[e]) : 0.f;
-        x[4 + e] = o.valid ? __uint_as_float(hi[e]) : 0.f;
-      }
-      bf16x8 ph, pm, pl;
-      split3_bf16(x, ph, pm, pl);
-      rotate_step<QJL>(o, kb, ph, d1, d2);
-      rotate_step<QJL>(o, kb, pm, d1, d2);
-      rotate_step<QJL>(o, kb, pl, d1, d2);
-    }
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      rotate_step<QJL>(o, kb, o.valid ? __builtin_bit_cast(bf16x8, o.raw[kb]) : zero, d1, d2);
-  }
-}
-
-// Query prologue: one single-wave workgroup per (batch row, kv-head, 32 output coordinates)
-// writes q1 and q2 (fp32) of the G q-heads into a record per q-head: q1[128], q2[128].
-constexpr int QREC = 2 * D;  // floats per record
-
-struct PrologueArgs {
-  const void* q;  // [B*Hq][128] bf16 or fp32 (q_f32)
-  const uint16_t* r_hi;
-  const uint16_t* r_lo;
-  const uint16_t* m_hi;  // NULL without a sketch
-  const uint16_t* m_lo;
-  float* qrec;  // [B*Hq][QREC]
-  int G, q_f32;
-};
+// ---- query prologue --------------------------------------------------------------------------
+// One single-wave workgroup per (batch row, kv-head, 32 output coordinates) writes q1 and q2
+// (fp32) of the G q-heads into a record per q-head (rotate_query_tile).
+constexpr int QS = 132;  // LDS row stride (floats) of the merged sums in the epilogue
 
 template <bool QJL>
 __global__ void __launch_bounds__(64) prologue_kernel(PrologueArgs a) {
-  const int lane = threadIdx.x, wave = blockIdx.y;  // output coordinates 32 wave .. 32 wave + 31
-  const int col = lane & 15, g = lane >> 4;
-  const int G = a.G;
-  const int64_t head0 = static_cast<int64_t>(blockIdx.x) * G;
-  QOperands<QJL> qo;
-  load_query_operands<QJL>(qo, a.q, a.q_f32 != 0, head0, G, a.r_hi, a.r_lo, a.m_hi, a.m_lo, wave, col, g);
-  f32x4 d1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  f32x4 d2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  rotate_products<QJL>(qo, a.q_f32 != 0, d1, d2);
-  // D layout: lane (col, g) holds head 4 g + i, output coordinate 32 wave + 16 nt + col
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * g + i;
-    if (h >= G) continue;
-    float* rec = a.qrec + (head0 + h) * QREC;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      rec[32 * wave + 16 * nt + col] = d1[nt][i];
-      rec[D + 32 * wave + 16 * nt + col] = QJL ? d2[nt][i] : 0.f;
-    }
-  }
+  rotate_query_tile<QJL>(a, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 // ---- main kernel ----------------------------------------------------------------------------

@@ -26,6 +26,11 @@ __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// 8 bf16 values from 16 bytes (16-byte aligned).
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
+}
+
 // fp32 -> bf16 bit pattern, round to nearest, ties to even (finite inputs).
 __device__ __forceinline__ uint16_t f2bf(float x) {
   uint32_t u = __builtin_bit_cast(uint32_t, x);

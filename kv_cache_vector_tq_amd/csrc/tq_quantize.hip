@@ -27,6 +27,7 @@
 
 #include "tq_common.h"
 #include "tq_internal.h"
+#include "tq_qrot.h"
 
 namespace tq {
 namespace {
@@ -50,10 +51,6 @@ struct QuantArgs {
   float centroids[16];
   float thresholds[16];
 };
-
-__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
-}
 
 // Packs 32 codes of BITS bits (code j at bit BITS*j) into BITS dwords.
 template <int BITS>
@@ -235,6 +232,14 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
 
   // ---- scale, scalar code, residual (sub-tiles without a token of the call are skipped; the
   // pack below masks their rows) -----------------------------------------------------------
+  // The codebook as wave-uniform register values (readfirstlane), so that the compare chain
+  // selects values rather than addresses of the argument block.
+  float cent[L], thr[L];
+#pragma unroll
+  for (int l = 0; l < L; ++l) {
+    cent[l] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.centroids[l])));
+    thr[l] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.thresholds[l])));
+  }
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     if (!mt_on[mt]) continue;
@@ -250,12 +255,12 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
         float c = 0.f;
         if constexpr (BITS > 0) {
           int idx = 0;
-          c = a.centroids[0];
+          c = cent[0];
 #pragma unroll
           for (int l = 1; l < L; ++l) {
-            const bool ge = z >= a.thresholds[l - 1];
+            const bool ge = z >= thr[l - 1];
             idx = ge ? l : idx;
-            c = ge ? a.centroids[l] : c;
+            c = ge ? cent[l] : c;
           }
           s_idx[row * IDX_STRIDE + o] = static_cast<uint8_t>(idx);
         }
@@ -401,17 +406,19 @@ struct QuantLaunch {
   int Hkv, nblk_max, n_tiles;
 };
 
-// Persistent workgroups walk tiles t = ((b * Hkv + h) * nblk_max + i) * 2 + tensor.
-template <int KB, bool QJL, int VB, bool F32>
-__global__ void __launch_bounds__(256, 2) quantize_kernel(QuantLaunch q) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
+// Persistent workgroups walk tiles t = ((b * Hkv + h) * nblk_max + i) * 2 + tensor.  This is
+// workgroup blockIdx.x of gridDim.x, or of the first nwg_fused workgroups of a fused launch.
+template <int KB, bool QJL, int VB, bool F32, bool FUSED>
+__device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& sm, int nwg_fused) {
+  const int wg = static_cast<int>(blockIdx.x);
+  const int nwg = FUSED ? nwg_fused : static_cast<int>(gridDim.x);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
   Operands op;
   // a workgroup that only sees value tiles (tiles alternate K, V; with one tile per workgroup
   // the odd ones) does not need the sketch matrix
-  const bool sketch = QJL && q.has_k && (static_cast<int>(gridDim.x) < q.n_tiles || (blockIdx.x & 1) == 0);
+  const bool sketch = QJL && q.has_k && (nwg < q.n_tiles || (wg & 1) == 0);
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int o = 32 * wave + 16 * nt + col;
@@ -422,7 +429,7 @@ __global__ void __launch_bounds__(256, 2) quantize_kernel(QuantLaunch q) {
       if constexpr (QJL) op.sb[nt][kb] = sketch ? load_bf16x8(q.k.s_b + o * D + 32 * grp + 8 * kb) : bf16x8{};
     }
   }
-  for (int t = blockIdx.x; t < q.n_tiles; t += gridDim.x) {
+  for (int t = wg; t < q.n_tiles; t += nwg) {
     const int tensor = t & 1;
     const int rest = t >> 1;
     const int i = rest % q.nblk_max;
@@ -448,43 +455,80 @@ __global__ void __launch_bounds__(256, 2) quantize_kernel(QuantLaunch q) {
   }
 }
 
-template <int KB, bool QJL, int VB>
-hipError_t launch_quantize(const QuantLaunch& q, bool f32, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  auto kern = f32 ? quantize_kernel<KB, QJL, VB, true> : quantize_kernel<KB, QJL, VB, false>;
-  if (e0 != nullptr || e1 != nullptr)
-    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, e0, e1, 0, q);
+template <int KB, bool QJL, int VB, bool F32>
+__global__ void __launch_bounds__(256, 2) quantize_kernel(QuantLaunch q) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  quantize_workgroup<KB, QJL, VB, F32, false>(q, sm, 0);
+}
+
+// Decode step: the first n_qwg workgroups quantize the new tokens, each further workgroup
+// rotates the queries of one (batch row, kv-head) unit (wave w: output coordinates
+// 32 w .. 32 w + 31), all in one launch; the two parts share no data.
+template <int KB, bool QJL, int VB, bool F32>
+__global__ void __launch_bounds__(256, 2) append_rotate_kernel(QuantLaunch q, PrologueArgs pa, int n_qwg) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  if (static_cast<int>(blockIdx.x) < n_qwg)
+    quantize_workgroup<KB, QJL, VB, F32, true>(q, sm, n_qwg);
   else
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, q);
+    rotate_query_tile<QJL>(pa, static_cast<int>(blockIdx.x) - n_qwg, threadIdx.x >> 6, threadIdx.x & 63);
+}
+
+// Launch shape: grid workgroups of quantize, plus rot_wgs rotation workgroups when pa is set.
+struct QuantGrid {
+  int grid;
+  const PrologueArgs* pa;
+  int rot_wgs;
+};
+
+template <int KB, bool QJL, int VB>
+hipError_t launch_quantize(const QuantLaunch& q, bool f32, const QuantGrid& g, hipStream_t s, hipEvent_t e0,
+                           hipEvent_t e1) {
+  const bool ext = e0 != nullptr || e1 != nullptr;
+  if (g.pa != nullptr) {
+    auto kern = f32 ? append_rotate_kernel<KB, QJL, VB, true> : append_rotate_kernel<KB, QJL, VB, false>;
+    const dim3 grid(g.grid + g.rot_wgs);
+    if (ext)
+      hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, s, e0, e1, 0, q, *g.pa, g.grid);
+    else
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, q, *g.pa, g.grid);
+  } else {
+    auto kern = f32 ? quantize_kernel<KB, QJL, VB, true> : quantize_kernel<KB, QJL, VB, false>;
+    if (ext)
+      hipExtLaunchKernelGGL(kern, dim3(g.grid), dim3(256), 0, s, e0, e1, 0, q);
+    else
+      hipLaunchKernelGGL(kern, dim3(g.grid), dim3(256), 0, s, q);
+  }
   return hipGetLastError();
 }
 
 template <int KB, bool QJL>
-hipError_t dispatch_v(const QuantLaunch& q, int vb, bool f32, int grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+hipError_t dispatch_v(const QuantLaunch& q, int vb, bool f32, const QuantGrid& g, hipStream_t s, hipEvent_t e0,
+                      hipEvent_t e1) {
   switch (vb) {
-    case 1: return launch_quantize<KB, QJL, 1>(q, f32, grid, s, e0, e1);
-    case 2: return launch_quantize<KB, QJL, 2>(q, f32, grid, s, e0, e1);
-    case 3: return launch_quantize<KB, QJL, 3>(q, f32, grid, s, e0, e1);
-    case 4: return launch_quantize<KB, QJL, 4>(q, f32, grid, s, e0, e1);
+    case 1: return launch_quantize<KB, QJL, 1>(q, f32, g, s, e0, e1);
+    case 2: return launch_quantize<KB, QJL, 2>(q, f32, g, s, e0, e1);
+    case 3: return launch_quantize<KB, QJL, 3>(q, f32, g, s, e0, e1);
+    case 4: return launch_quantize<KB, QJL, 4>(q, f32, g, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t dispatch(const QuantLaunch& q, const tq_config& c, bool f32, int grid, hipStream_t s, hipEvent_t e0,
-                    hipEvent_t e1) {
+hipError_t dispatch(const QuantLaunch& q, const tq_config& c, bool f32, const QuantGrid& g, hipStream_t s,
+                    hipEvent_t e0, hipEvent_t e1) {
   if (c.k_qjl) {
     switch (c.k_bits) {
-      case 0: return dispatch_v<0, true>(q, c.v_bits, f32, grid, s, e0, e1);
-      case 1: return dispatch_v<1, true>(q, c.v_bits, f32, grid, s, e0, e1);
-      case 2: return dispatch_v<2, true>(q, c.v_bits, f32, grid, s, e0, e1);
-      case 3: return dispatch_v<3, true>(q, c.v_bits, f32, grid, s, e0, e1);
-      case 4: return dispatch_v<4, true>(q, c.v_bits, f32, grid, s, e0, e1);
+      case 0: return dispatch_v<0, true>(q, c.v_bits, f32, g, s, e0, e1);
+      case 1: return dispatch_v<1, true>(q, c.v_bits, f32, g, s, e0, e1);
+      case 2: return dispatch_v<2, true>(q, c.v_bits, f32, g, s, e0, e1);
+      case 3: return dispatch_v<3, true>(q, c.v_bits, f32, g, s, e0, e1);
+      case 4: return dispatch_v<4, true>(q, c.v_bits, f32, g, s, e0, e1);
     }
   } else {
     switch (c.k_bits) {
-      case 1: return dispatch_v<1, false>(q, c.v_bits, f32, grid, s, e0, e1);
-      case 2: return dispatch_v<2, false>(q, c.v_bits, f32, grid, s, e0, e1);
-      case 3: return dispatch_v<3, false>(q, c.v_bits, f32, grid, s, e0, e1);
-      case 4: return dispatch_v<4, false>(q, c.v_bits, f32, grid, s, e0, e1);
+      case 1: return dispatch_v<1, false>(q, c.v_bits, f32, g, s, e0, e1);
+      case 2: return dispatch_v<2, false>(q, c.v_bits, f32, g, s, e0, e1);
+      case 3: return dispatch_v<3, false>(q, c.v_bits, f32, g, s, e0, e1);
+      case 4: return dispatch_v<4, false>(q, c.v_bits, f32, g, s, e0, e1);
     }
   }
   return hipErrorInvalidValue;
@@ -493,12 +537,12 @@ hipError_t dispatch(const QuantLaunch& q, const tq_config& c, bool f32, int grid
 }  // namespace
 }  // namespace tq
 
-extern "C" int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, const void* k, const void* v,
-                              tq_dtype in_dtype, int B, int Hkv, int n_new, int64_t stride_b, int64_t stride_h,
-                              int64_t stride_t, const int32_t* start_pos, const tq_kv_cache* cache,
-                              void* hip_stream) {
-  using namespace tq;
-  clear_error();
+namespace tq {
+
+int quantize_launch(const tq_codebook* cb, const tq_dev_params* p, const void* k, const void* v, tq_dtype in_dtype,
+                    int B, int Hkv, int n_new, int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                    const int32_t* start_pos, const tq_kv_cache* cache, void* hip_stream,
+                    const QueryRotationArgs* rot) {
   if (cb == nullptr || p == nullptr || cache == nullptr || start_pos == nullptr)
     return fail(TQ_ERR_INVALID, "cb, p, cache and start_pos must not be NULL");
   int rc = check_config(cb->cfg);
@@ -566,7 +610,25 @@ extern "C" int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, con
     e0 = reinterpret_cast<hipEvent_t>(pe.quant_start);
     e1 = reinterpret_cast<hipEvent_t>(pe.quant_stop);
   }
-  hipError_t e = dispatch(q, cb->cfg, f32, grid, s, e0, e1);
+  PrologueArgs pa{};
+  QuantGrid qg{grid, nullptr, 0};
+  if (rot != nullptr) {
+    pa = PrologueArgs{rot->q, rot->r_hi, rot->r_lo, rot->m_hi, rot->m_lo, rot->qrec, rot->G, rot->q_f32};
+    qg.pa = &pa;
+    qg.rot_wgs = rot->units;
+  }
+  hipError_t e = dispatch(q, cb->cfg, f32, qg, s, e0, e1);
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("quantize launch: ") + hipGetErrorString(e));
   return TQ_OK;
+}
+
+}  // namespace tq
+
+extern "C" int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, const void* k, const void* v,
+                              tq_dtype in_dtype, int B, int Hkv, int n_new, int64_t stride_b, int64_t stride_h,
+                              int64_t stride_t, const int32_t* start_pos, const tq_kv_cache* cache,
+                              void* hip_stream) {
+  tq::clear_error();
+  return tq::quantize_launch(cb, p, k, v, in_dtype, B, Hkv, n_new, stride_b, stride_h, stride_t, start_pos, cache,
+                             hip_stream, nullptr);
 }

@@ -259,6 +259,53 @@ def test_bit_mix_variants(cfg, G):
     say("bit-mix", cfg, G, "codes", stats)
 
 
+@pytest.mark.parametrize("preset,G,dtype", [("turbo3", 4, "bf16"), ("turbo4", 8, "f32"), ("qjl1", 16, "bf16")])
+def test_decode_step_matches_separate_calls(preset, G, dtype):
+    """tq_decode_step (new token + query rotation in one launch, then attention) gives the same
+    cache bytes and bit-identical outputs as tq_quantize_kv followed by tq_attend_decode, and
+    its output matches the oracle."""
+    B, Hkv, T_cap = 2, 2, 2048
+    lens = [1500, 900]
+    rng = np.random.default_rng(41)
+    K = rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32)
+    Q = rng.standard_normal((B, Hkv * G, 128)).astype(np.float32)
+    if dtype == "bf16":
+        K, V, Q = wl.round_to_bf16(K), wl.round_to_bf16(V), wl.round_to_bf16(Q)
+    caches = []
+    for _ in range(2):
+        cb, dp, cache = _setup(preset, B, Hkv, T_cap)
+        # prefill: the first lens[b] tokens (the rest of each row is written but not attended)
+        tq.tq_quantize_kv(cb, dp, cache, H.to_device(K, dtype), H.to_device(V, dtype),
+                          torch.zeros(B, dtype=torch.int32, device="cuda"))
+        caches.append(cache)
+    # row b's new token is token lens[b] of the host arrays
+    k1 = torch.stack([H.to_device(K[b, :, lens[b]:lens[b] + 1], dtype) for b in range(B)])
+    v1 = torch.stack([H.to_device(V[b, :, lens[b]:lens[b] + 1], dtype) for b in range(B)])
+    start = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    seq = torch.tensor([n + 1 for n in lens], dtype=torch.int32, device="cuda")
+    qd = H.to_device(Q, dtype)
+    say("decode-step", preset, G, dtype, "separate calls")
+    tq.tq_quantize_kv(cb, dp, caches[0], k1, v1, start)
+    out_a = tq.tq_attend_decode(cb, dp, caches[0], qd, seq, T_cap).clone()
+    say("decode-step", preset, G, dtype, "fused step")
+    out_b = tq.tq_decode_step(cb, dp, caches[1], k1, v1, start, qd, seq, T_cap)
+    torch.cuda.synchronize()
+    for name, t in caches[0].tensors().items():
+        if t is not None:
+            assert torch.equal(t, caches[1].tensors()[name]), name
+    np.testing.assert_array_equal(out_a.cpu().numpy(), out_b.cpu().numpy())
+    hc, out = H.cache_host(caches[1]), out_b.cpu().numpy()
+    orc = H.make_oracle(preset)
+    for b in range(B):
+        for h in range(Hkv):
+            n = lens[b] + 1
+            kg = H.unpack_keys(orc, hc, b, h, n)
+            vg = H.unpack_values(orc, hc, b, h, n)
+            hs = slice(h * G, (h + 1) * G)
+            H.compare_attention(orc, Q[b, hs], kg, vg, n, out[b, hs], None)
+
+
 def test_special_vectors():
     """Zero vectors, one-hot vectors, huge and tiny magnitudes, fp32 inputs."""
     preset = "turbo3"

@@ -186,3 +186,29 @@ def test_attend_workspace_query_and_checks():
     # the transposed rotation halves are required
     no_rt = _lib.TQDevParams(1 << 15, 1 << 16, 1 << 17, None, 1 << 19, 1 << 20, 1 << 21)
     assert _attend_rc(cb, cache, Hq=8, max_seq=4096, params=no_rt)[0] == _lib.TQ_ERR_INVALID
+
+
+def _step_rc(cb, cache, k=1 << 12, v=1 << 13, ws=None, ws_bytes=None, Hq=8, start=1 << 14, sb=128, sh=128):
+    n = ctypes.c_size_t(0 if ws_bytes is None else ws_bytes)
+    params = _lib.TQDevParams(1 << 15, 1 << 16, 1 << 17, 1 << 18, 1 << 19, 1 << 20, 1 << 21)
+    rc = _lib.lib.tq_decode_step(ctypes.byref(cb.cb), ctypes.byref(params), ctypes.byref(cache.struct), k, v,
+                                 _lib.TQ_DTYPE_BF16, sb, sh, start, 1 << 22, _lib.TQ_DTYPE_BF16, Hq, 1 << 23, 4096,
+                                 0.0, 1 << 24, None, ws, ctypes.byref(n), None)
+    return rc, n.value
+
+
+def test_decode_step_checks_before_any_launch():
+    cb = tq.tq_build_codebook(2, 1, 3)
+    cache = _FakeCache(cb, B=2, Hkv=2, T_cap=4096)
+    # workspace query: the attention workspace, nothing launched
+    rc, need = _step_rc(cb, cache)
+    assert rc == _lib.TQ_OK and need == _attend_rc(cb, cache, Hq=8, max_seq=4096)[1]
+    # append errors of tq_quantize_kv, detected on the host with a valid workspace
+    assert _step_rc(cb, cache, k=None, v=None, ws=1 << 20, ws_bytes=need)[0] == _lib.TQ_ERR_INVALID
+    assert _step_rc(cb, cache, k=(1 << 12) + 2, ws=1 << 20, ws_bytes=need)[0] == _lib.TQ_ERR_INVALID
+    assert _step_rc(cb, cache, start=None, ws=1 << 20, ws_bytes=need)[0] == _lib.TQ_ERR_INVALID
+    assert _step_rc(cb, cache, sb=-128, ws=1 << 20, ws_bytes=need)[0] == _lib.TQ_ERR_INVALID
+    # attention errors come first
+    assert _step_rc(cb, cache, Hq=6, ws=1 << 20, ws_bytes=need)[0] == _lib.TQ_ERR_UNSUPPORTED
+    assert _step_rc(cb, cache, ws=1 << 20, ws_bytes=need - 1)[0] == _lib.TQ_ERR_WORKSPACE
+
