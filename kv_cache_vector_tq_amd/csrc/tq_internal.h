@@ -44,6 +44,13 @@ int quantize_launch(const tq_codebook* cb, const tq_dev_params* p, const void* k
                     const int32_t* start_pos, const tq_kv_cache* cache, void* hip_stream,
                     const QueryRotationArgs* rot);
 
+// Validates the arguments of a quantize call (those of tq_quantize_kv) and fills the kernel
+// arguments of its keys and values (tq_quantize_tile.h).
+struct QuantArgs;
+int quantize_args(const tq_codebook* cb, const tq_dev_params* p, const void* k, const void* v, tq_dtype in_dtype,
+                  int B, int Hkv, int n_new, int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                  const int32_t* start_pos, const tq_kv_cache* cache, QuantArgs* ka, QuantArgs* va);
+
 // Events of the timing hook (tq_profile_events), per thread; NULL when disabled.
 struct ProfileEvents {
   void* attend_start = nullptr;

@@ -161,10 +161,9 @@ hipError_t dispatch(const QuantLaunch& q, const tq_config& c, bool f32, const Qu
 
 namespace tq {
 
-int quantize_launch(const tq_codebook* cb, const tq_dev_params* p, const void* k, const void* v, tq_dtype in_dtype,
-                    int B, int Hkv, int n_new, int64_t stride_b, int64_t stride_h, int64_t stride_t,
-                    const int32_t* start_pos, const tq_kv_cache* cache, void* hip_stream,
-                    const QueryRotationArgs* rot) {
+int quantize_args(const tq_codebook* cb, const tq_dev_params* p, const void* k, const void* v, tq_dtype in_dtype,
+                  int B, int Hkv, int n_new, int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                  const int32_t* start_pos, const tq_kv_cache* cache, QuantArgs* ka, QuantArgs* va) {
   if (cb == nullptr || p == nullptr || cache == nullptr || start_pos == nullptr)
     return fail(TQ_ERR_INVALID, "cb, p, cache and start_pos must not be NULL");
   int rc = check_config(cb->cfg);
@@ -186,8 +185,6 @@ int quantize_launch(const tq_codebook* cb, const tq_dev_params* p, const void* k
   if (cb->cfg.k_qjl && k && (p->s_qjl == nullptr || !aligned(p->s_qjl, 16)))
     return fail(TQ_ERR_INVALID, "sketch matrix missing or not 16-byte aligned");
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
-  const bool f32 = in_dtype == TQ_DTYPE_F32;
   QuantArgs a{};
   a.sb = stride_b;
   a.sh = stride_h;
@@ -198,24 +195,36 @@ int quantize_launch(const tq_codebook* cb, const tq_dev_params* p, const void* k
   a.T_cap = cache->T_cap;
   a.r_hi = p->r_hi;
   a.r_lo = p->r_lo;
-  QuantLaunch q{};
-  q.k = a;
-  q.k.x = k;
-  q.k.s_b = p->s_qjl;
-  q.k.codes = cache->k_codes;
-  q.k.signs = cache->k_signs;
-  q.k.norm = cache->k_norm;
-  q.k.rnorm = cache->k_rnorm;
-  q.v = a;
-  q.v.x = v;
-  q.v.codes = cache->v_codes;
-  q.v.norm = cache->v_norm;
+  *ka = a;
+  ka->x = k;
+  ka->s_b = p->s_qjl;
+  ka->codes = cache->k_codes;
+  ka->signs = cache->k_signs;
+  ka->norm = cache->k_norm;
+  ka->rnorm = cache->k_rnorm;
+  *va = a;
+  va->x = v;
+  va->codes = cache->v_codes;
+  va->norm = cache->v_norm;
   for (int l = 0; l < 16; ++l) {
-    q.k.centroids[l] = cb->k_centroids[l];
-    q.k.thresholds[l] = cb->k_thresholds[l];
-    q.v.centroids[l] = cb->v_centroids[l];
-    q.v.thresholds[l] = cb->v_thresholds[l];
+    ka->centroids[l] = cb->k_centroids[l];
+    ka->thresholds[l] = cb->k_thresholds[l];
+    va->centroids[l] = cb->v_centroids[l];
+    va->thresholds[l] = cb->v_thresholds[l];
   }
+  return TQ_OK;
+}
+
+int quantize_launch(const tq_codebook* cb, const tq_dev_params* p, const void* k, const void* v, tq_dtype in_dtype,
+                    int B, int Hkv, int n_new, int64_t stride_b, int64_t stride_h, int64_t stride_t,
+                    const int32_t* start_pos, const tq_kv_cache* cache, void* hip_stream,
+                    const QueryRotationArgs* rot) {
+  QuantLaunch q{};
+  const int rc = quantize_args(cb, p, k, v, in_dtype, B, Hkv, n_new, stride_b, stride_h, stride_t, start_pos,
+                               cache, &q.k, &q.v);
+  if (rc != TQ_OK) return rc;
+  hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
+  const bool f32 = in_dtype == TQ_DTYPE_F32;
   q.has_k = k != nullptr;
   q.has_v = v != nullptr;
   q.Hkv = Hkv;

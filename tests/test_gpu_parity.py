@@ -259,13 +259,15 @@ def test_bit_mix_variants(cfg, G):
     say("bit-mix", cfg, G, "codes", stats)
 
 
-@pytest.mark.parametrize("preset,G,dtype", [("turbo3", 4, "bf16"), ("turbo4", 8, "f32"), ("qjl1", 16, "bf16")])
-def test_decode_step_matches_separate_calls(preset, G, dtype):
+@pytest.mark.parametrize("preset,G,dtype,lens", [("turbo3", 4, "bf16", [1500, 900]), ("turbo4", 8, "f32", [1500, 900]),
+                                                  ("qjl1", 16, "bf16", [1500, 900]), ("turbo4", 4, "bf16", [0, 63]),
+                                                  ("turbo3", 8, "bf16", [64, 2047]), ("turbo2", 16, "bf16", [640, 1])])
+def test_decode_step_matches_separate_calls(preset, G, dtype, lens):
     """tq_decode_step (new token + query rotation in one launch, then attention) gives the same
     cache bytes and bit-identical outputs as tq_quantize_kv followed by tq_attend_decode, and
-    its output matches the oracle."""
+    its output matches the oracle; new tokens mid-block, in block 0, at a block start and in
+    the last slot."""
     B, Hkv, T_cap = 2, 2, 2048
-    lens = [1500, 900]
     rng = np.random.default_rng(41)
     K = rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32)
     V = rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32)
