@@ -182,38 +182,53 @@ def stream_read_gbs(dev, mib=2048):
 
 
 def bf16_comparator(w, layers, dev, reps=3):
-    """Uncompressed decode attention at the same shape in plain PyTorch (bf16 K/V and q, fp32
-    softmax): scores = K q^T (bmm), softmax over the context, out = P^T V (bmm), for `layers`
-    distinct K/V caches.  Every bmm operand is contiguous.  Returns us per layer."""
+    """Uncompressed bf16 decode attention at the same shape, `layers` distinct K/V caches, timed
+    back to back: (a) this library's bf16 baseline kernel (tq_bf16_attend_decode, V stored
+    transposed per 32-key chunk), (b) plain PyTorch (bmm with contiguous operands, fp32
+    softmax, bmm).  Returns us per layer of each."""
     import torch
 
-    Hkv, G, T = w.B * w.Hkv, w.G, w.T
+    import kv_cache_vector_tq_amd as tq
+
+    B, Hkv, Hq, G, T = w.B, w.Hkv, w.Hq, w.G, w.T
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
-    Ks = [torch.randn((Hkv, T, 128), generator=gen, device=dev).to(torch.bfloat16) for _ in range(layers)]
-    Vs = [torch.randn((Hkv, T, 128), generator=gen, device=dev).to(torch.bfloat16) for _ in range(layers)]
-    qT = torch.randn((Hkv, 128, G), generator=gen, device=dev).to(torch.bfloat16).contiguous()
+    Ks = [torch.randn((B, Hkv, T, 128), generator=gen, device=dev).to(torch.bfloat16) for _ in range(layers)]
+    Vs = [torch.randn((B, Hkv, T, 128), generator=gen, device=dev).to(torch.bfloat16) for _ in range(layers)]
+    q = torch.randn((B, Hq, 128), generator=gen, device=dev).to(torch.bfloat16)
+    seq = torch.full((B,), T, dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e3 / (reps * layers)
+
+    # (a) baseline kernel
+    Vts = [tq.bf16_value_chunks(v) for v in Vs]
+    ws = torch.empty(tq.bf16_attend_workspace_bytes(B, Hkv, T, Hq, T), dtype=torch.uint8, device=dev)
+    hip_us = timed(lambda: [tq.tq_bf16_attend_decode(Ks[l], Vts[l], q, seq, T, out=out, workspace=ws)
+                            for l in range(layers)])
+    del Vts
+    # (b) plain PyTorch, one bmm per kv-head group
+    qT = q.view(B * Hkv, G, 128).transpose(1, 2).contiguous()  # [B*Hkv, 128, G]
     scale = 1.0 / math.sqrt(128)
 
     def layer(K, V):
-        sc = torch.bmm(K, qT).float() * scale                      # [Hkv, T, G]
-        p = torch.softmax(sc, dim=1).to(torch.bfloat16).transpose(1, 2).contiguous()  # [Hkv, G, T]
-        return torch.bmm(p, V)                                      # [Hkv, G, 128]
+        sc = torch.bmm(K.view(B * Hkv, T, 128), qT).float() * scale  # [B*Hkv, T, G]
+        p = torch.softmax(sc, dim=1).to(torch.bfloat16).transpose(1, 2).contiguous()  # [B*Hkv, G, T]
+        return torch.bmm(p, V.view(B * Hkv, T, 128))  # [B*Hkv, G, 128]
 
-    for K, V in zip(Ks, Vs):
-        layer(K, V)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(reps):
-        for K, V in zip(Ks, Vs):
-            layer(K, V)
-    t1.record()
-    torch.cuda.synchronize()
-    us = t0.elapsed_time(t1) * 1e3 / (reps * layers)
+    torch_us = timed(lambda: [layer(K, V) for K, V in zip(Ks, Vs)])
     del Ks, Vs
     torch.cuda.empty_cache()
-    return us
+    return hip_us, torch_us
 
 
 def copy_probe(mib: int):
@@ -363,11 +378,13 @@ def main():
     if args.other_workloads:
         del caches, k_new, v_new, K, V, ws, outs, qs_l, graph
         torch.cuda.empty_cache()
-        bf16_us = bf16_comparator(w, L, dev)
+        bf16_us, torch_us = bf16_comparator(w, L, dev)
         bf16_bytes = 2 * B * Hkv * T * 128 * 2
-        comparator = {"kind": "uncompressed bf16 decode attention in plain PyTorch (bmm, fp32 softmax, bmm)",
+        comparator = {"kind": "uncompressed bf16 decode attention, same shape: tq_bf16_attend_decode (this "
+                              "library's baseline kernel) and plain PyTorch (bmm, fp32 softmax, bmm)",
                       "us_per_layer": bf16_us, "keys_per_s": B * Hkv * T / (bf16_us * 1e-6),
                       "gbs": bf16_bytes / (bf16_us * 1e-6) / 1e9,
+                      "torch_us_per_layer": torch_us,
                       "compressed_call_us_per_layer": call_us,
                       "speedup_of_compressed_call": bf16_us / call_us}
         log(json.dumps(comparator))

@@ -230,6 +230,20 @@ int tq_decode_step(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_ca
                    int Hq, const int32_t* seq_len, int max_seq_len, float scale, float* out,
                    float* scores_out, void* workspace, size_t* workspace_bytes, void* hip_stream);
 
+/* Baseline for comparison: uncompressed bf16 decode attention at the same shapes (not part of
+ * the compressed path).  p = softmax(scale * K q) (scale 0 selects 1/sqrt(128)),
+ * out = sum_i p_i V_i, fp32 accumulation, for all (batch row, q-head); q-head h reads kv-head
+ * h / (Hq / Hkv), Hq / Hkv in {4, 8, 16}; keys 0 .. seq_len[b]-1 (clamped into 1..max_seq_len).
+ * k: device bf16 [B][Hkv][T_cap][128]; vt: device bf16 [B][Hkv][T_cap/32][128][32], V
+ * transposed per 32-key chunk, slot 8 g + e of a coordinate row holding key
+ * 16 (e / 4) + 4 g + e % 4 of the chunk; q: device bf16 [B][Hq][128]; out: fp32 [B][Hq][128].
+ * T_cap a positive multiple of 32; k, vt, q 16-byte aligned.  workspace: device scratch of
+ * *workspace_bytes bytes (query with workspace == NULL); no initial contents needed.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED (group size), TQ_ERR_WORKSPACE, TQ_ERR_DEVICE. */
+int tq_bf16_attend_decode(const void* k, const void* vt, int B, int Hkv, int T_cap, const void* q, int Hq,
+                          const int32_t* seq_len, int max_seq_len, float scale, float* out, void* workspace,
+                          size_t* workspace_bytes, void* hip_stream);
+
 /* Diagnostic timing hook (for benchmarks): events (hipEvent_t, created by the caller) that
  * later calls on this thread record on their stream, attend_* immediately before and after
  * the main attention kernel of tq_attend_decode (scores, softmax, value sums, merge over

@@ -20,7 +20,7 @@ PRESETS = {"turbo2": (1, 1, 2), "turbo3": (2, 1, 3), "turbo4": (3, 1, 4), "qjl1"
 
 __all__ = [
     "PRESETS", "Codebook", "DeviceParams", "KVCache", "TQError", "tq_build_codebook", "tq_cache_layout",
-    "tq_decode_step",
+    "tq_decode_step", "tq_bf16_attend_decode", "bf16_value_chunks", "bf16_attend_workspace_bytes",
     "tq_quantize_kv", "tq_attend_decode", "tq_abi_version", "tq_profile_events", "upload_params",
     "attend_workspace_bytes",
 ]
@@ -247,5 +247,44 @@ def tq_decode_step(codebook: Codebook, params: DeviceParams, cache: KVCache, k, 
                              seq_len.data_ptr(), max_seq_len, float(scale), out.data_ptr(),
                              scores_out.data_ptr() if scores_out is not None else None, workspace.data_ptr(),
                              ctypes.byref(n), _stream(q.device)), "tq_decode_step")
+    return out
+
+
+def bf16_value_chunks(v):
+    """V [B, Hkv, T, 128] (T a multiple of 32) -> the transposed chunk layout of
+    tq_bf16_attend_decode: [B, Hkv, T/32, 128, 32], slot 8 g + e holding key 16 (e / 4) + 4 g + e % 4."""
+    import torch
+
+    B, Hkv, T, _ = v.shape
+    order = torch.tensor([16 * (e // 4) + 4 * g + e % 4 for g in range(4) for e in range(8)], device=v.device)
+    return v.reshape(B, Hkv, T // 32, 32, HEAD_DIM)[:, :, :, order, :].transpose(3, 4).contiguous()
+
+
+def bf16_attend_workspace_bytes(B: int, Hkv: int, T_cap: int, Hq: int, max_seq_len: int) -> int:
+    """Bytes of workspace tq_bf16_attend_decode needs (no initial contents)."""
+    n = ctypes.c_size_t(0)
+    # a workspace query needs no device data; dummy aligned pointers satisfy the argument checks
+    check(lib.tq_bf16_attend_decode(ctypes.c_void_p(256), ctypes.c_void_p(256), B, Hkv, T_cap, ctypes.c_void_p(256),
+                                    Hq, ctypes.c_void_p(256), max_seq_len, 0.0, ctypes.c_void_p(256), None,
+                                    ctypes.byref(n), None), "tq_bf16_attend_decode")
+    return n.value
+
+
+def tq_bf16_attend_decode(k, vt, q, seq_len, max_seq_len: int, scale: float = 0.0, out=None, workspace=None):
+    """Uncompressed bf16 baseline: k [B, Hkv, T_cap, 128] bf16, vt from bf16_value_chunks(v),
+    q [B, Hq, 128] bf16.  Returns out [B, Hq, 128] fp32."""
+    import torch
+
+    B, Hkv, T_cap, _ = k.shape
+    Hq = q.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = bf16_attend_workspace_bytes(B, Hkv, T_cap, Hq, max_seq_len)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    n = ctypes.c_size_t(workspace.numel())
+    check(lib.tq_bf16_attend_decode(k.data_ptr(), vt.data_ptr(), B, Hkv, T_cap, q.data_ptr(), Hq, seq_len.data_ptr(),
+                                    max_seq_len, float(scale), out.data_ptr(), workspace.data_ptr(), ctypes.byref(n),
+                                    _stream(q.device)), "tq_bf16_attend_decode")
     return out
 

@@ -100,6 +100,9 @@ def _load():
     lib.tq_decode_step.argtypes = [P(TQCodebook), P(TQDevParams), P(TQKVCache), vp, vp, ctypes.c_int,
                                    ctypes.c_int64, ctypes.c_int64, vp, vp, ctypes.c_int, ctypes.c_int, vp,
                                    ctypes.c_int, ctypes.c_float, vp, vp, vp, P(ctypes.c_size_t), vp]
+    lib.tq_bf16_attend_decode.restype = ctypes.c_int
+    lib.tq_bf16_attend_decode.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp,
+                                          ctypes.c_int, ctypes.c_float, vp, vp, P(ctypes.c_size_t), vp]
     lib.tq_profile_events.restype = ctypes.c_int
     lib.tq_profile_events.argtypes = [vp, vp, vp, vp]
     return lib

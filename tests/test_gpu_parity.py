@@ -308,6 +308,32 @@ def test_decode_step_matches_separate_calls(preset, G, dtype, lens):
             H.compare_attention(orc, Q[b, hs], kg, vg, n, out[b, hs], None)
 
 
+@pytest.mark.parametrize("G", [4, 8, 16])
+def test_bf16_baseline(G):
+    """The uncompressed bf16 baseline against plain softmax attention in fp64 (bf16-rounded
+    inputs).  Its softmax weights enter the value products as bf16, so outputs agree to the
+    bf16 unit roundoff (2^-8) relative to the output's largest magnitude."""
+    B, Hkv, T_cap = 2, 2, 2048
+    lens = [2048, 777]
+    rng = np.random.default_rng(50 + G)
+    K = wl.round_to_bf16(rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32))
+    V = wl.round_to_bf16(rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32))
+    Q = wl.round_to_bf16(rng.standard_normal((B, Hkv * G, 128)).astype(np.float32))
+    kd, vd, qd = (H.to_device(x, "bf16") for x in (K, V, Q))
+    say("bf16-baseline", G)
+    out = tq.tq_bf16_attend_decode(kd, tq.bf16_value_chunks(vd), qd, torch.tensor(lens, dtype=torch.int32,
+                                                                               device="cuda"), T_cap)
+    out = out.cpu().numpy()
+    for b in range(B):
+        for h in range(Hkv * G):
+            k = K[b, h // G, :lens[b]].astype(np.float64)
+            v = V[b, h // G, :lens[b]].astype(np.float64)
+            s = k @ Q[b, h].astype(np.float64) / np.sqrt(128.0)
+            p = np.exp(s - s.max())
+            ref = (p / p.sum()) @ v
+            assert np.abs(out[b, h] - ref).max() <= 2.0 ** -8 * np.abs(ref).max(), (b, h)
+
+
 def test_special_vectors():
     """Zero vectors, one-hot vectors, huge and tiny magnitudes, fp32 inputs."""
     preset = "turbo3"

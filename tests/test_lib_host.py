@@ -212,3 +212,18 @@ def test_decode_step_checks_before_any_launch():
     assert _step_rc(cb, cache, Hq=6, ws=1 << 20, ws_bytes=need)[0] == _lib.TQ_ERR_UNSUPPORTED
     assert _step_rc(cb, cache, ws=1 << 20, ws_bytes=need - 1)[0] == _lib.TQ_ERR_WORKSPACE
 
+
+def test_bf16_baseline_checks():
+    n = ctypes.c_size_t(0)
+    a = [1 << 12, 1 << 13, 2, 2, 2048, 1 << 14, 8, 1 << 15, 2048, 0.0, 1 << 16]
+    assert _lib.lib.tq_bf16_attend_decode(*a, None, ctypes.byref(n), None) == _lib.TQ_OK and n.value > 0
+    bad_tcap = list(a)
+    bad_tcap[4] = 100
+    assert _lib.lib.tq_bf16_attend_decode(*bad_tcap, None, ctypes.byref(n), None) == _lib.TQ_ERR_INVALID
+    bad_g = list(a)
+    bad_g[6] = 6
+    assert _lib.lib.tq_bf16_attend_decode(*bad_g, None, ctypes.byref(n), None) == _lib.TQ_ERR_UNSUPPORTED
+    need = n.value
+    small = ctypes.c_size_t(need - 1)
+    assert _lib.lib.tq_bf16_attend_decode(*a, 1 << 20, ctypes.byref(small), None) == _lib.TQ_ERR_WORKSPACE
+
