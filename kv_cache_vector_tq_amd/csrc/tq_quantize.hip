@@ -33,14 +33,34 @@
 namespace tq {
 namespace {
 
-struct QuantLaunch {
-  QuantArgs k, v;
-  int has_k, has_v;
-  int Hkv, nblk_max, n_tiles;
-};
+// From tile t on (stride nwg), finds the next tile the call writes (index tf); false when
+// there is none.  All values are uniform over the workgroup.
+__device__ __forceinline__ bool find_tile(const QuantLaunch& q, int t, int nwg, int& tf, TileRef& r) {
+  for (; t < q.n_tiles; t += nwg) {
+    const int tensor = t & 1;
+    const int rest = t >> 1;
+    const int i = rest % q.nblk_max;
+    const int bh = rest / q.nblk_max;
+    if (tensor == 0 ? !q.has_k : !q.has_v) continue;
+    // a scalar load (constant address space: start_pos does not change during the kernel), so
+    // waiting for it does not wait for the vector loads in flight
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+    const int start = ((const_i32_ptr)(uintptr_t)q.k.start_pos)[bh / q.Hkv];
+    if (start < 0) continue;
+    const int end = min(start + q.k.n_new, q.k.T_cap);  // one past the last slot written
+    const int blk = start / 64 + i;
+    const int p0 = blk * 64;
+    if (p0 >= end) continue;
+    r = TileRef{tensor, bh / q.Hkv, bh % q.Hkv, start, blk, max(start, p0), min(end, p0 + 64)};
+    tf = t;
+    return true;
+  }
+  return false;
+}
 
 // Persistent workgroups walk tiles t = ((b * Hkv + h) * nblk_max + i) * 2 + tensor.  This is
 // workgroup blockIdx.x of gridDim.x, or of the first nwg_fused workgroups of a fused launch.
+// Each tile's inputs are loaded while the previous tile computes.
 template <int KB, bool QJL, int VB, bool F32, bool FUSED>
 __device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& sm, int nwg_fused) {
   const int wg = static_cast<int>(blockIdx.x);
@@ -48,32 +68,35 @@ __device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& s
   const int tid = threadIdx.x;
   Operands op;
   // a workgroup that only sees value tiles (tiles alternate K, V; with one tile per workgroup
-  // the odd ones) does not need the sketch matrix
+  // the odd ones) does not need the sketch matrix.  The operands are requested first: they
+  // are the largest loads, and their latency overlaps the search for the first tile.
   const bool sketch = QJL && q.has_k && (nwg < q.n_tiles || (wg & 1) == 0);
   load_operands<QJL>(op, q.k, sketch, tid);
-  for (int t = wg; t < q.n_tiles; t += nwg) {
-    const int tensor = t & 1;
-    const int rest = t >> 1;
-    const int i = rest % q.nblk_max;
-    const int bh = rest / q.nblk_max;
-    const int h = bh % q.Hkv, b = bh / q.Hkv;
-    if (tensor == 0 ? !q.has_k : !q.has_v) continue;
-    const QuantArgs& a = tensor == 0 ? q.k : q.v;
-    // a scalar load (constant address space: start_pos does not change during the kernel), so
-    // waiting for it does not wait for the operand loads in flight
-    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-    const int start = ((const_i32_ptr)(uintptr_t)a.start_pos)[b];
-    if (start < 0) continue;
-    const int end = min(start + a.n_new, a.T_cap);  // one past the last slot written
-    const int blk = start / 64 + i;
-    const int p0 = blk * 64;
-    if (p0 >= end) continue;  // uniform over the workgroup
-    const int lo_slot = max(start, p0), hi_slot = min(end, p0 + 64);
-    __syncthreads();  // the previous tile is fully stored
-    if (tensor == 0)
-      quantize_tile<true, KB, QJL, F32>(q.k, sm, op, b, h, start, blk, lo_slot, hi_slot, tid);
+  int t;
+  TileRef cur;
+  if (!find_tile(q, wg, nwg, t, cur)) return;  // uniform
+  // issued after the operands, so that waiting for the first tile's rows implies them
+  TileIn<F32> in;
+  load_tile<F32, VB>(q, cur, tid, in);
+  for (;;) {
+    int tn = 0;
+    TileRef nxt;
+    const bool more = find_tile(q, t + nwg, nwg, tn, nxt);
+    lds_barrier();  // the previous tile is done with LDS
+    load_rows_norms<F32>(sm, cur, in, tid);
+    uint32_t prev[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) prev[i] = in.prev[i];
+    // the next tile's inputs are in flight while this tile computes
+    if (more) load_tile<F32, VB>(q, nxt, tid, in);  // uniform
+    lds_barrier();
+    if (cur.tensor == 0)
+      quantize_tile<true, KB, QJL, F32>(q.k, sm, op, cur, prev, tid);
     else
-      quantize_tile<false, VB, false, F32>(q.v, sm, op, b, h, start, blk, lo_slot, hi_slot, tid);
+      quantize_tile<false, VB, false, F32>(q.v, sm, op, cur, prev, tid);
+    if (!more) break;
+    cur = nxt;
+    t = tn;
   }
 }
 
@@ -234,7 +257,10 @@ int quantize_launch(const tq_codebook* cb, const tq_dev_params* p, const void* k
   q.n_tiles = static_cast<int>(tiles);
   // two workgroups per CU are resident (register budget); a larger persistent grid only adds a
   // late-starting tail
-  const int grid = static_cast<int>(std::min<int64_t>(tiles, 2ll * device_cu_count()));
+  int grid = static_cast<int>(std::min<int64_t>(tiles, 2ll * device_cu_count()));
+  // an odd stride lets every workgroup alternate key and value tiles (tiles alternate K, V),
+  // so no workgroup is left with only the costlier key tiles
+  if (grid < tiles && grid % 2 == 0) --grid;
   const ProfileEvents& pe = profile_events();
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (pe.quant_start && pe.quant_stop) {

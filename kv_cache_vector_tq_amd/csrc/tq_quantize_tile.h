@@ -26,13 +26,49 @@ struct QuantArgs {
   float thresholds[16];
 };
 
+// One quantize launch: keys and values of the same call.
+struct QuantLaunch {
+  QuantArgs k, v;
+  int has_k, has_v;
+  int Hkv, nblk_max, n_tiles;
+};
+
+// A tile the call writes: tokens [lo_slot, hi_slot) of block blk of (b, h), tensor 0 = keys.
+struct TileRef {
+  int tensor, b, h, start, blk, lo_slot, hi_slot;
+};
+
+// A tile's global inputs, loaded one tile ahead: each thread's 32 input elements of row
+// tid / 4 (16-byte words), and for a value tile that does not cover its whole block the
+// value-code words it rewrites (4 tokens share a word; zero otherwise).
+template <bool F32>
+struct TileIn {
+  static constexpr int NW = F32 ? 8 : 4;
+  u32x4 w[NW];
+  uint32_t prev[4];
+};
+
+// Whether value tile r leaves other tokens of its block to other calls.
+__device__ __forceinline__ bool partial_tile(const TileRef& r) {
+  return r.lo_slot > r.blk * 64 || r.hi_slot < r.blk * 64 + 64;
+}
+
 namespace {
 
 
 constexpr int XS_BF16 = 136;  // LDS row stride (bf16 elements) of the input tile
 constexpr int XS_F32 = 132;   // LDS row stride (floats) of the fp32 input / residual tile
 constexpr int IDX_STRIDE = 144;  // LDS row stride (bytes) of the code / sign tiles
+constexpr int PLANE = 64 * XS_BF16;  // bf16 elements of one residual plane (hi, mid or lo)
 
+
+// Workgroup barrier ordering LDS accesses only: global loads and stores in flight (the next
+// tile's inputs, the last tile's outputs) stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // Packs 32 codes of BITS bits (code j at bit BITS*j) into BITS dwords.
 template <int BITS>
@@ -50,7 +86,8 @@ __device__ __forceinline__ void pack32(const uint8_t* c, uint32_t* w) {
 }
 
 struct Smem {
-  float tile[64 * XS_F32];  // input tile, later residuals
+  // input tile; later the fp32 residuals, then their three exact bf16 terms as planes
+  float tile[3 * PLANE / 2];
   uint8_t idx[64 * IDX_STRIDE];
   uint8_t sgn[64 * IDX_STRIDE];
   float norm[64];
@@ -64,61 +101,48 @@ struct Operands {
   bf16x8 rh[2][4], rl[2][4], sb[2][4];
 };
 
-// Quantizes the tokens of block blk of (b, h) that fall in [lo_slot, hi_slot).
-// KEY: key layout (and sketch when QJL); otherwise value layout.  BITS = 0 only for keys
-// that keep only the sketch.  F32: input elements are fp32 (else bf16).
-template <bool KEY, int BITS, bool QJL, bool F32>
-__device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, const Operands& op, int b, int h,
-                                              int start, int blk, int lo_slot, int hi_slot, int tid) {
-  constexpr int L = 1 << (BITS > 0 ? BITS : 1);
-  float* s_tile = sm.tile;
-  uint8_t* s_idx = sm.idx;
-  uint8_t* s_sgn = sm.sgn;
-  float* s_norm = sm.norm;
-  float* s_rnorm = sm.rnorm;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int col = lane & 15, grp = lane >> 4;
-  const int p0 = blk * 64;
-  // 16-token sub-tiles holding at least one token of the call
-  const int r0 = lo_slot - p0, r1 = hi_slot - p0;
-  bool mt_on[4];
+// Issues the loads of tile r's inputs.  Rows outside [lo_slot, hi_slot) read a clamped
+// (written) row and are masked by the consumer.  VB: value code bits of the launch.
+template <bool F32, int VB>
+__device__ __forceinline__ void load_tile(const QuantLaunch& q, const TileRef& r, int tid, TileIn<F32>& in) {
+  const int row = tid >> 2, qq = tid & 3;
+  const int srow = min(max(r.blk * 64 + row, r.lo_slot), r.hi_slot - 1);
+  const void* x = r.tensor == 0 ? q.k.x : q.v.x;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(x) +
+                       ((int64_t)r.b * q.k.sb + (int64_t)r.h * q.k.sh + (int64_t)(srow - r.start) * q.k.st + 32 * qq) *
+                           (F32 ? 4 : 2);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) mt_on[mt] = (16 * mt < r1) && (16 * mt + 16 > r0);
-  const int64_t bh = (int64_t)b * a.Hkv + h;
-  const int nblk = a.T_cap / 64;
-  // Value words hold codes of 4 tokens: a tile that does not cover the whole block reads the
-  // words it will modify now, so the read-modify-write at the end costs no extra round trip.
-  const bool partial = lo_slot > p0 || hi_slot < p0 + 64;  // uniform over the workgroup
-  uint32_t prev[KEY ? 1 : (BITS > 0 ? BITS : 1)];
-  if constexpr (!KEY) {
-    const uint32_t* pw = reinterpret_cast<const uint32_t*>(a.codes + (bh * nblk + blk) * (1024 * BITS) +
-                                                           (tid >> 2) * 16 * BITS + (tid & 3) * 4 * BITS);
+  for (int i = 0; i < TileIn<F32>::NW; ++i) in.w[i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
 #pragma unroll
-    for (int i = 0; i < BITS; ++i) prev[i] = partial ? pw[i] : 0u;
+  for (int i = 0; i < 4; ++i) in.prev[i] = 0u;
+  if (r.tensor == 1 && partial_tile(r)) {  // uniform
+    const int64_t bh = (int64_t)r.b * q.Hkv + r.h;
+    const uint32_t* pw = reinterpret_cast<const uint32_t*>(q.v.codes + (bh * (q.v.T_cap / 64) + r.blk) * (1024 * VB) +
+                                                           (tid >> 2) * 16 * VB + (tid & 3) * 4 * VB);
+#pragma unroll
+    for (int i = 0; i < VB; ++i) in.prev[i] = pw[i];
   }
+}
 
-  // ---- load the tile, row norms ----------------------------------------------------------
+// First step of every tile, keys and values alike: the tile's input rows (from `in`) go to
+// LDS, and each row's norm n and sqrt(d) / n are computed.  Rows outside [lo_slot, hi_slot)
+// are zero.
+template <bool F32>
+__device__ __forceinline__ void load_rows_norms(Smem& sm, const TileRef& tr, const TileIn<F32>& in, int tid) {
+  const int p0 = tr.blk * 64, lo_slot = tr.lo_slot, hi_slot = tr.hi_slot;
+  float* s_tile = sm.tile;
+  float* s_norm = sm.norm;
   // The norm is taken after an exact power-of-two rescaling by the row's largest magnitude,
   // so that squares neither overflow nor underflow fp32 over the whole bf16 / fp32 range.
   {
     const int row = tid >> 2, q = tid & 3;
     const int slot = p0 + row;
     const bool valid = slot >= lo_slot && slot < hi_slot;
-    // all loads first, from a clamped (always written) row, so that they are in flight together;
-    // rows outside [lo_slot, hi_slot) are masked afterwards
-    constexpr int NW = F32 ? 8 : 4;  // 16-byte words of this thread's 32 elements
+    constexpr int NW = TileIn<F32>::NW;  // 16-byte words of this thread's 32 elements
     u32x4 w[NW];
-    {
-      const int srow = min(max(slot, lo_slot), hi_slot - 1);
-      const uint8_t* src = reinterpret_cast<const uint8_t*>(a.x) +
-                           ((int64_t)b * a.sb + (int64_t)h * a.sh + (int64_t)(srow - start) * a.st + 32 * q) *
-                               (F32 ? 4 : 2);
 #pragma unroll
-      for (int i = 0; i < NW; ++i) w[i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
-#pragma unroll
-      for (int i = 0; i < NW; ++i)
-        if (!valid) w[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < NW; ++i) w[i] = valid ? in.w[i] : u32x4{0u, 0u, 0u, 0u};
+
     float v[32];
     if constexpr (F32) {
       float* dst = s_tile + row * XS_F32 + 32 * q;
@@ -147,13 +171,11 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
     mx = fmaxf(mx, __shfl_xor(mx, 2));
     int ex = 0;
     if (mx > 0.f) frexpf(mx, &ex);
-    // mx * 2^-ex lies in [0.5, 1); the scale is applied in two exact halves so that neither
-    // factor leaves the fp32 range for any finite input
-    const float sc1 = ldexpf(1.0f, -ex / 2), sc2 = ldexpf(1.0f, -ex - (-ex / 2));
+    // mx * 2^-ex lies in [0.5, 1); ldexp scales exactly over the whole fp32 range
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      const float t = (v[e] * sc1) * sc2;
+      const float t = ldexpf(v[e], -ex);
       ss = fmaf(t, t, ss);
     }
     ss += __shfl_xor(ss, 1);
@@ -164,7 +186,39 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
       sm.zs[row] = n > 0.f ? SQRT_D / n : 0.f;
     }
   }
-  __syncthreads();
+}
+
+// Quantizes the tokens of block blk of (b, h) that fall in [lo_slot, hi_slot).
+// KEY: key layout (and sketch when QJL); otherwise value layout.  BITS = 0 only for keys
+// that keep only the sketch.  F32: input elements are fp32 (else bf16).
+// The input rows and norms are in LDS already (load_rows_norms); prev holds the value words
+// a partial value tile rewrites (TileIn).
+template <bool KEY, int BITS, bool QJL, bool F32>
+__device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, const Operands& op, const TileRef& tr,
+                                              const uint32_t* prev, int tid) {
+  const int b = tr.b, h = tr.h, blk = tr.blk, lo_slot = tr.lo_slot, hi_slot = tr.hi_slot;
+  constexpr int L = 1 << (BITS > 0 ? BITS : 1);
+  float* s_tile = sm.tile;
+  uint8_t* s_idx = sm.idx;
+  uint8_t* s_sgn = sm.sgn;
+  float* s_norm = sm.norm;
+  float* s_rnorm = sm.rnorm;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int p0 = blk * 64;
+  // 16-token sub-tiles holding at least one token of the call
+  const int r0 = lo_slot - p0, r1 = hi_slot - p0;
+  bool mt_on[4];
+  int n_on = 0;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    mt_on[mt] = (16 * mt < r1) && (16 * mt + 16 > r0);
+    n_on += mt_on[mt] ? 1 : 0;
+  }
+  const int64_t bh = (int64_t)b * a.Hkv + h;
+  const int nblk = a.T_cap / 64;
+  const bool partial = partial_tile(tr);  // uniform over the workgroup
+
 
   // ---- rotation: acc[mt][nt] = X[16 mt.., :] R_eff[32 wave + 16 nt.., :]^T ---------------
   f32x4 acc[4][2];
@@ -209,7 +263,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
       }
     }
   }
-  __syncthreads();  // the input tile is dead from here on; its space holds residuals
+  lds_barrier();  // the input tile is dead from here on; its space holds residuals
 
   // ---- scale, scalar code, residual (sub-tiles without a token of the call are skipped; the
   // pack below masks their rows) -----------------------------------------------------------
@@ -254,22 +308,40 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   if constexpr (KEY && QJL) {
-    // ---- residual norms ---------------------------------------------------------------------
-    if constexpr (BITS > 0) {
+    // ---- residual norms; with more than one active sub-tile, r is split once into its three
+    // exact bf16 terms (planes), else each wave splits the sub-tile's rows itself ----------------
+    const bool planes = n_on > 1;  // uniform
+    {
       const int row = tid >> 2, q = tid & 3;
       const float* src = s_tile + row * XS_F32 + 32 * q;
-      float ss = 0.f;
+      float v[32];
 #pragma unroll
-      for (int j = 0; j < 32; j += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + j);
-        ss = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], ss))));
+      for (int j = 0; j < 32; j += 4) *reinterpret_cast<f32x4*>(v + j) = *reinterpret_cast<const f32x4*>(src + j);
+      if constexpr (BITS > 0) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; j += 4) ss = fmaf(v[j], v[j], fmaf(v[j + 1], v[j + 1], fmaf(v[j + 2], v[j + 2], fmaf(v[j + 3], v[j + 3], ss))));
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        if (q == 0) s_rnorm[row] = s_norm[row] > 0.f ? sqrtf(ss) : 0.f;
       }
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      if (q == 0) s_rnorm[row] = s_norm[row] > 0.f ? sqrtf(ss) : 0.f;
+      if (planes) {
+        bf16x8 ph[4], pm[4], pl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split3_bf16(v + 8 * i, ph[i], pm[i], pl[i]);
+        lds_barrier();  // every residual is read before the planes overwrite the tile
+        bf16x8* dst = reinterpret_cast<bf16x8*>(reinterpret_cast<uint16_t*>(s_tile) + row * XS_BF16 + 32 * q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dst[i] = ph[i];
+          dst[i + PLANE / 8] = pm[i];
+          dst[i + PLANE / 4] = pl[i];
+        }
+        lds_barrier();
+      }
     }
     // ---- sketch: u = S_b r, signs -----------------------------------------------------------
     const auto& sb = op.sb;
@@ -280,12 +352,19 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
       const int row = 16 * mt + col;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const float* src = s_tile + row * XS_F32 + 32 * grp + 8 * kb;
-        float v[8];
-        *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
-        *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
         bf16x8 rh, rm, rl;
-        split3_bf16(v, rh, rm, rl);
+        if (planes) {
+          const uint16_t* src = reinterpret_cast<const uint16_t*>(s_tile) + row * XS_BF16 + 32 * grp + 8 * kb;
+          rh = load_bf16x8(src);
+          rm = load_bf16x8(src + PLANE);
+          rl = load_bf16x8(src + 2 * PLANE);
+        } else {
+          const float* src = s_tile + row * XS_F32 + 32 * grp + 8 * kb;
+          float v[8];
+          *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
+          *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
+          split3_bf16(v, rh, rm, rl);
+        }
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           u[nt] = mfma_bf16(rh, sb[nt][kb], u[nt]);
@@ -301,7 +380,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
           s_sgn[orow * IDX_STRIDE + 32 * wave + 16 * nt + col] = u[nt][i] >= 0.f ? 1 : 0;
         }
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- pack and store ------------------------------------------------------------------------
@@ -362,12 +441,18 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
       }
       uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + (bh * nblk + blk) * (1024 * BITS) + Lc * 16 * BITS +
                                                   part * 4 * BITS);
+      if (!partial) {
+        // a whole block: every word is written, the old words are not needed (nor waited for)
 #pragma unroll
-      for (int i = 0; i < BITS; ++i) {
-        if (m[i] == 0xFFFFFFFFu) {
-          dst[i] = w[i];
-        } else if (m[i] != 0u) {
-          dst[i] = (prev[i] & ~m[i]) | w[i];
+        for (int i = 0; i < BITS; ++i) dst[i] = w[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) {
+          if (m[i] == 0xFFFFFFFFu) {
+            dst[i] = w[i];
+          } else if (m[i] != 0u) {
+            dst[i] = (prev[i] & ~m[i]) | w[i];
+          }
         }
       }
     }
