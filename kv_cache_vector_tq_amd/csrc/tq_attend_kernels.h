@@ -367,8 +367,10 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
     }
   };
   // score operands from the prologue's record of head hh: lane (col, g) holds
-  // q[hh][32 g + 8 kb + e] of every k-block kb in f16, scaled by 2^-e with e the exponent of
-  // the vector's largest magnitude (the 4 lanes of a column hold the 128 coordinates).
+  // q[hh][32 g + 8 kb + e] of every k-block kb as two f16 terms (hi + lo, the fp32 value to
+  // about 22 bits), scaled by 2^-e with e the exponent of the vector's largest magnitude (the
+  // 4 lanes of a column hold the 128 coordinates).  One f16 term alone leaves a relative
+  // error of 2^-12 per coordinate, which large logits carry into the softmax weights.
   // logit * log2(e) = n (code_acc * c1 + rnorm * sign_acc * c2): the table holds centroids c,
   // the key term is q1 . c / sqrt(d), the sign term carries sqrt(pi/2)/m.
   // The G query records of this kv-head (contiguous) go through LDS: one 16-byte load per
@@ -398,7 +400,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   for (int k = 0; k < QPT; ++k)
     if (tid + k * NT < QWORDS) *reinterpret_cast<f32x4*>(qst + 4 * (tid + k * NT)) = qw[k];
   __syncthreads();  // tables and query records ready
-  f16x8 bq[4], bs[4];
+  f16x8 bq[4], bs[4], bql[4], bsl[4];
   float c1, c2;
   {
     f32x4 qv1[8], qv2[8];
@@ -421,14 +423,17 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
     if (m1 > 0.f) frexpf(m1, &e1);
     if (m2 > 0.f) frexpf(m2, &e2);
     const float s1 = ldexpf(1.0f, -e1), s2 = ldexpf(1.0f, -e2);  // exact powers of two
+    auto lo16 = [](float x, _Float16 hi) { return static_cast<_Float16>(x - static_cast<float>(hi)); };
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        bq[kb][e] = static_cast<_Float16>(qv1[2 * kb][e] * s1);
-        bq[kb][4 + e] = static_cast<_Float16>(qv1[2 * kb + 1][e] * s1);
-        bs[kb][e] = static_cast<_Float16>(qv2[2 * kb][e] * s2);
-        bs[kb][4 + e] = static_cast<_Float16>(qv2[2 * kb + 1][e] * s2);
+      for (int j = 0; j < 8; ++j) {
+        const float x1 = qv1[2 * kb + j / 4][j % 4] * s1, x2 = qv2[2 * kb + j / 4][j % 4] * s2;
+        const _Float16 h1 = static_cast<_Float16>(x1), h2 = static_cast<_Float16>(x2);
+        bq[kb][j] = h1;
+        bql[kb][j] = lo16(x1, h1);
+        bs[kb][j] = h2;
+        bsl[kb][j] = lo16(x2, h2);
       }
     const float lscale = a.scale * LOG2E;
     c1 = ldexpf(1.0f, e1) * INV_SQRT_D * lscale;
@@ -446,18 +451,25 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
     static_for<0, 4>([&](auto T_) {
       constexpr int t = decltype(T_)::value;
       f32x4 dc = f32x4{0.f, 0.f, 0.f, 0.f}, ds = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 dcl = f32x4{0.f, 0.f, 0.f, 0.f}, dsl = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (KB > 0) {
         static_for<0, 4>([&](auto KB_) {
           constexpr int kb = decltype(KB_)::value;
-          dc = mfma_f16(decode8<KB, 32 * KB * t + 8 * KB * kb>(cur.kd, ktab), bq[kb], dc);
+          const f16x8 ak = decode8<KB, 32 * KB * t + 8 * KB * kb>(cur.kd, ktab);
+          dc = mfma_f16(ak, bq[kb], dc);
+          dcl = mfma_f16(ak, bql[kb], dcl);
         });
       }
       if constexpr (QJL) {
         static_for<0, 4>([&](auto KB_) {
           constexpr int kb = decltype(KB_)::value;
-          ds = mfma_f16(decode_signs<32 * t + 8 * kb>(cur.sd, stab), bs[kb], ds);
+          const f16x8 as = decode_signs<32 * t + 8 * kb>(cur.sd, stab);
+          ds = mfma_f16(as, bs[kb], ds);
+          dsl = mfma_f16(as, bsl[kb], dsl);
         });
       }
+      dc += dcl;
+      ds += dsl;
       constexpr int st_ = t / TPD, ct = t % TPD;
       if constexpr (ct == 0) {
         cs[st_] = dc;

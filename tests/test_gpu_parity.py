@@ -71,6 +71,52 @@ def test_workload_parity(wname, preset):
     say(wname, preset, "codes", stats, "max rel err", max(e["out"] for e in errs), max(e["score"] for e in errs))
 
 
+@pytest.mark.parametrize("wname,preset", [("c3_batch16_t128k", "turbo3"), ("c4_llama70b_layer_b8_t128k", "qjl1"),
+                                          ("c5_moe_attn_t1m", "turbo3"), ("c5_moe_attn_t1m", "turbo4")])
+def test_full_size_sampled(wname, preset):
+    """The large workloads at full size, in the calls and launch shapes the benchmark times:
+    the whole context quantized by one call, one attention call over every (batch row,
+    kv-head) unit, inputs drawn on the device by the seeded workload generator.  The oracle
+    checks the first and the last unit: codes, signs and norms of a token sample (the first
+    and last 64-token blocks plus 16384 random tokens), and every q-head's output over the
+    full context (decoded from the GPU-written cache)."""
+    w = wl.workload(wname)
+    T = w.T
+    cb, dp, cache = _setup(preset, w.B, w.Hkv, T, zero=False)
+    K = torch.empty((w.B, w.Hkv, T, 128), dtype=torch.bfloat16, device="cuda")
+    V = torch.empty_like(K)
+    for b in range(w.B):
+        for h in range(w.Hkv):
+            wl.device_slice(w, b, h, wl.TENSOR_K, out=K[b, h])
+            wl.device_slice(w, b, h, wl.TENSOR_V, out=V[b, h])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.cfg_seed)
+    Q = torch.randn((w.B, w.Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+    say(wname, preset, "quantize", tuple(K.shape))
+    tq.tq_quantize_kv(cb, dp, cache, K, V, torch.zeros(w.B, dtype=torch.int32, device="cuda"))
+    say(wname, preset, "attend")
+    out = tq.tq_attend_decode(cb, dp, cache, Q, torch.full((w.B,), T, dtype=torch.int32, device="cuda"), T)
+    torch.cuda.synchronize()
+    say(wname, preset, "device done")
+    orc = H.make_oracle(preset)
+    rng = np.random.default_rng(7)
+    sample = np.unique(np.concatenate([np.arange(64), np.arange(T - 64, T), rng.integers(0, T, 16384)]))
+    stats, errs = {}, []
+    for b, h in [(0, 0), (w.B - 1, w.Hkv - 1)]:
+        hc = {n: (None if t is None else t[b:b + 1, h:h + 1].cpu().numpy()) for n, t in cache.tensors().items()}
+        kg = H.unpack_keys(orc, hc, 0, 0, T)
+        vg = H.unpack_values(orc, hc, 0, 0, T)
+        xk = K[b, h].float().cpu().numpy()
+        xv = V[b, h].float().cpu().numpy()
+        H.compare_keys(orc, xk[sample], {n: a[sample] for n, a in kg.items()}, stats)
+        H.compare_values(orc, xv[sample], {n: a[sample] for n, a in vg.items()}, stats)
+        hs = slice(h * w.G, (h + 1) * w.G)
+        errs.append(H.compare_attention(orc, Q[b, hs].float().cpu().numpy(), kg, vg, T, out[b, hs].cpu().numpy()))
+        say(wname, preset, "unit", (b, h), "checked")
+    H.finish_stats(stats)
+    say(wname, preset, "codes", stats, "max rel err", max(e["out"] for e in errs))
+
+
 @pytest.mark.parametrize("preset", ["turbo2", "turbo3", "turbo4", "qjl1"])
 def test_ragged_appends_and_canary(preset):
     """Bulk fill from unaligned starts, then one-token and block-crossing appends; slots never
