@@ -72,12 +72,19 @@ __device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& s
   // are the largest loads, and their latency overlaps the search for the first tile.
   const bool sketch = QJL && q.has_k && (nwg < q.n_tiles || (wg & 1) == 0);
   load_operands<QJL>(op, q.k, sketch, tid);
+  TileIn<F32> in;
+  // A one-token call (a decode step) reads row 0 of its (batch row, kv-head) input whatever
+  // the slot: that load is issued now, ahead of the start_pos read the tile search waits for.
+  const bool one = q.k.n_new == 1 && wg < q.n_tiles;  // uniform
+  if (one) {
+    const int tensor = wg & 1, bh = (wg >> 1) / q.nblk_max;
+    if (tensor == 0 ? q.has_k : q.has_v) load_rows<F32>(q, TileRef{tensor, bh / q.Hkv, bh % q.Hkv, 0, 0, 0, 1}, tid, in);
+  }
   int t;
   TileRef cur;
   if (!find_tile(q, wg, nwg, t, cur)) return;  // uniform
   // issued after the operands, so that waiting for the first tile's rows implies them
-  TileIn<F32> in;
-  load_tile<F32, VB>(q, cur, tid, in);
+  if (!one) load_rows<F32>(q, cur, tid, in);
   for (;;) {
     int tn = 0;
     TileRef nxt;
@@ -85,10 +92,9 @@ __device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& s
     lds_barrier();  // the previous tile is done with LDS
     load_rows_norms<F32>(sm, cur, in, tid);
     uint32_t prev[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) prev[i] = in.prev[i];
-    // the next tile's inputs are in flight while this tile computes
-    if (more) load_tile<F32, VB>(q, nxt, tid, in);  // uniform
+    load_prev<VB>(q, cur, tid, prev);  // used at the end of the tile
+    // the next tile's rows are in flight while this tile computes
+    if (more) load_rows<F32>(q, nxt, tid, in);  // uniform
     lds_barrier();
     if (cur.tensor == 0)
       quantize_tile<true, KB, QJL, F32>(q.k, sm, op, cur, prev, tid);

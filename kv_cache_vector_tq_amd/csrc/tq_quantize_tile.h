@@ -38,14 +38,12 @@ struct TileRef {
   int tensor, b, h, start, blk, lo_slot, hi_slot;
 };
 
-// A tile's global inputs, loaded one tile ahead: each thread's 32 input elements of row
-// tid / 4 (16-byte words), and for a value tile that does not cover its whole block the
-// value-code words it rewrites (4 tokens share a word; zero otherwise).
+// A tile's input rows, loaded one tile ahead: each thread's 32 input elements of row
+// tid / 4, as 16-byte words.
 template <bool F32>
 struct TileIn {
   static constexpr int NW = F32 ? 8 : 4;
   u32x4 w[NW];
-  uint32_t prev[4];
 };
 
 // Whether value tile r leaves other tokens of its block to other calls.
@@ -101,10 +99,10 @@ struct Operands {
   bf16x8 rh[2][4], rl[2][4], sb[2][4];
 };
 
-// Issues the loads of tile r's inputs.  Rows outside [lo_slot, hi_slot) read a clamped
-// (written) row and are masked by the consumer.  VB: value code bits of the launch.
-template <bool F32, int VB>
-__device__ __forceinline__ void load_tile(const QuantLaunch& q, const TileRef& r, int tid, TileIn<F32>& in) {
+// Issues the loads of tile r's input rows.  Rows outside [lo_slot, hi_slot) read a clamped
+// (written) row and are masked by the consumer.
+template <bool F32>
+__device__ __forceinline__ void load_rows(const QuantLaunch& q, const TileRef& r, int tid, TileIn<F32>& in) {
   const int row = tid >> 2, qq = tid & 3;
   const int srow = min(max(r.blk * 64 + row, r.lo_slot), r.hi_slot - 1);
   const void* x = r.tensor == 0 ? q.k.x : q.v.x;
@@ -113,14 +111,20 @@ __device__ __forceinline__ void load_tile(const QuantLaunch& q, const TileRef& r
                            (F32 ? 4 : 2);
 #pragma unroll
   for (int i = 0; i < TileIn<F32>::NW; ++i) in.w[i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
+}
+
+// For a value tile that does not cover its whole block: the value-code words it rewrites
+// (4 tokens share a word); zero otherwise.  VB: value code bits of the launch.
+template <int VB>
+__device__ __forceinline__ void load_prev(const QuantLaunch& q, const TileRef& r, int tid, uint32_t* prev) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) in.prev[i] = 0u;
+  for (int i = 0; i < 4; ++i) prev[i] = 0u;
   if (r.tensor == 1 && partial_tile(r)) {  // uniform
     const int64_t bh = (int64_t)r.b * q.Hkv + r.h;
     const uint32_t* pw = reinterpret_cast<const uint32_t*>(q.v.codes + (bh * (q.v.T_cap / 64) + r.blk) * (1024 * VB) +
                                                            (tid >> 2) * 16 * VB + (tid & 3) * 4 * VB);
 #pragma unroll
-    for (int i = 0; i < VB; ++i) in.prev[i] = pw[i];
+    for (int i = 0; i < VB; ++i) prev[i] = pw[i];
   }
 }
 
@@ -192,7 +196,7 @@ __device__ __forceinline__ void load_rows_norms(Smem& sm, const TileRef& tr, con
 // KEY: key layout (and sketch when QJL); otherwise value layout.  BITS = 0 only for keys
 // that keep only the sketch.  F32: input elements are fp32 (else bf16).
 // The input rows and norms are in LDS already (load_rows_norms); prev holds the value words
-// a partial value tile rewrites (TileIn).
+// a partial value tile rewrites (load_prev).
 template <bool KEY, int BITS, bool QJL, bool F32>
 __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, const Operands& op, const TileRef& tr,
                                               const uint32_t* prev, int tid) {
@@ -470,6 +474,9 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
 template <bool QJL>
 __device__ __forceinline__ void load_operands(Operands& op, const QuantArgs& k, bool sketch, int tid) {
   const int wave = tid >> 6, lane = tid & 63;
+  // without the sketch the sketch registers read the rotation rows instead (unused): the loads
+  // stay unconditional, so the compiler issues them all before the first wait
+  const uint16_t* sb = sketch ? k.s_b : k.r_hi;
   const int col = lane & 15, grp = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
@@ -478,7 +485,7 @@ __device__ __forceinline__ void load_operands(Operands& op, const QuantArgs& k, 
     for (int kb = 0; kb < 4; ++kb) {
       op.rh[nt][kb] = load_bf16x8(k.r_hi + o * D + 32 * grp + 8 * kb);
       op.rl[nt][kb] = load_bf16x8(k.r_lo + o * D + 32 * grp + 8 * kb);
-      if constexpr (QJL) op.sb[nt][kb] = sketch ? load_bf16x8(k.s_b + o * D + 32 * grp + 8 * kb) : bf16x8{};
+      if constexpr (QJL) op.sb[nt][kb] = load_bf16x8(sb + o * D + 32 * grp + 8 * kb);
     }
   }
 }
