@@ -73,18 +73,36 @@ __device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& s
   const bool sketch = QJL && q.has_k && (nwg < q.n_tiles || (wg & 1) == 0);
   load_operands<QJL>(op, q.k, sketch, tid);
   TileIn<F32> in;
-  // A one-token call (a decode step) reads row 0 of its (batch row, kv-head) input whatever
-  // the slot: that load is issued now, ahead of the start_pos read the tile search waits for.
-  const bool one = q.k.n_new == 1 && wg < q.n_tiles;  // uniform
-  if (one) {
-    const int tensor = wg & 1, bh = (wg >> 1) / q.nblk_max;
-    if (tensor == 0 ? q.has_k : q.has_v) load_rows<F32>(q, TileRef{tensor, bh / q.Hkv, bh % q.Hkv, 0, 0, 0, 1}, tid, in);
+  // A one-token call with a workgroup per tile (a decode step): every step up to the packing
+  // works on the token as row 0 of the tile; its slot (start_pos) is needed only by the
+  // stores, so its load overlaps the input loads.  start_pos is read with a vector load (the
+  // index is offset by a lane count that is always 0): waiting for it then never waits for
+  // LDS traffic, as waiting for a scalar load would.
+  if (q.k.n_new == 1 && nwg >= q.n_tiles) {  // uniform
+    if (wg >= q.n_tiles) return;
+    const int tensor = wg & 1, bh = wg >> 1, b = bh / q.Hkv, h = bh % q.Hkv;  // one block per row
+    if (tensor == 0 ? !q.has_k : !q.has_v) return;
+    const int start_lane = q.k.start_pos[b + static_cast<int>(__builtin_amdgcn_mbcnt_lo(0u, 0u))];
+    const TileRef row0{tensor, b, h, 0, 0, 0, 1};
+    load_rows<F32>(q, row0, tid, in);
+    load_rows_norms<F32>(sm, row0, in, tid);
+    const int start = __builtin_amdgcn_readfirstlane(start_lane);
+    if (start < 0 || start >= q.k.T_cap) return;  // uniform: the row is not written
+    const TileRef cur{tensor, b, h, start, start / 64, start, start + 1};
+    uint32_t prev[4];
+    load_prev<VB>(q, cur, tid, prev);
+    lds_barrier();
+    if (tensor == 0)
+      quantize_tile<true, KB, QJL, F32>(q.k, sm, op, cur, prev, tid, true);
+    else
+      quantize_tile<false, VB, false, F32>(q.v, sm, op, cur, prev, tid, true);
+    return;
   }
   int t;
   TileRef cur;
   if (!find_tile(q, wg, nwg, t, cur)) return;  // uniform
   // issued after the operands, so that waiting for the first tile's rows implies them
-  if (!one) load_rows<F32>(q, cur, tid, in);
+  load_rows<F32>(q, cur, tid, in);
   for (;;) {
     int tn = 0;
     TileRef nxt;
@@ -97,9 +115,9 @@ __device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& s
     if (more) load_rows<F32>(q, nxt, tid, in);  // uniform
     lds_barrier();
     if (cur.tensor == 0)
-      quantize_tile<true, KB, QJL, F32>(q.k, sm, op, cur, prev, tid);
+      quantize_tile<true, KB, QJL, F32>(q.k, sm, op, cur, prev, tid, false);
     else
-      quantize_tile<false, VB, false, F32>(q.v, sm, op, cur, prev, tid);
+      quantize_tile<false, VB, false, F32>(q.v, sm, op, cur, prev, tid, false);
     if (!more) break;
     cur = nxt;
     t = tn;

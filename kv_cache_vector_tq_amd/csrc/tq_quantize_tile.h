@@ -196,10 +196,11 @@ __device__ __forceinline__ void load_rows_norms(Smem& sm, const TileRef& tr, con
 // KEY: key layout (and sketch when QJL); otherwise value layout.  BITS = 0 only for keys
 // that keep only the sketch.  F32: input elements are fp32 (else bf16).
 // The input rows and norms are in LDS already (load_rows_norms); prev holds the value words
-// a partial value tile rewrites (load_prev).
+// a partial value tile rewrites (load_prev).  one: the tile's single token was loaded and is
+// computed as row 0 (a one-token call); only the stores use its slot.
 template <bool KEY, int BITS, bool QJL, bool F32>
 __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, const Operands& op, const TileRef& tr,
-                                              const uint32_t* prev, int tid) {
+                                              const uint32_t* prev, int tid, bool one) {
   const int b = tr.b, h = tr.h, blk = tr.blk, lo_slot = tr.lo_slot, hi_slot = tr.hi_slot;
   constexpr int L = 1 << (BITS > 0 ? BITS : 1);
   float* s_tile = sm.tile;
@@ -211,7 +212,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   const int col = lane & 15, grp = lane >> 4;
   const int p0 = blk * 64;
   // 16-token sub-tiles holding at least one token of the call
-  const int r0 = lo_slot - p0, r1 = hi_slot - p0;
+  const int r0 = one ? 0 : lo_slot - p0, r1 = one ? 1 : hi_slot - p0;
   bool mt_on[4];
   int n_on = 0;
 #pragma unroll
@@ -395,11 +396,12 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
       const int row = 16 * part + c;  // part is the tile t of the chunk
       const int slot = p0 + row;
       if (slot >= lo_slot && slot < hi_slot) {
+        const int sr = one ? 0 : row;  // LDS row that holds the token
         if constexpr (BITS > 0) {
           uint8_t cv[32];
-          *reinterpret_cast<u32x4*>(cv) = *reinterpret_cast<const u32x4*>(s_idx + row * IDX_STRIDE + 32 * g);
+          *reinterpret_cast<u32x4*>(cv) = *reinterpret_cast<const u32x4*>(s_idx + sr * IDX_STRIDE + 32 * g);
           *reinterpret_cast<u32x4*>(cv + 16) =
-              *reinterpret_cast<const u32x4*>(s_idx + row * IDX_STRIDE + 32 * g + 16);
+              *reinterpret_cast<const u32x4*>(s_idx + sr * IDX_STRIDE + 32 * g + 16);
           uint32_t w[BITS];
           pack32<BITS>(cv, w);
           uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + (bh * nblk + blk) * (1024 * BITS) + Lc * 16 * BITS +
@@ -409,9 +411,9 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
         }
         if constexpr (QJL) {
           uint8_t sv[32];
-          *reinterpret_cast<u32x4*>(sv) = *reinterpret_cast<const u32x4*>(s_sgn + row * IDX_STRIDE + 32 * g);
+          *reinterpret_cast<u32x4*>(sv) = *reinterpret_cast<const u32x4*>(s_sgn + sr * IDX_STRIDE + 32 * g);
           *reinterpret_cast<u32x4*>(sv + 16) =
-              *reinterpret_cast<const u32x4*>(s_sgn + row * IDX_STRIDE + 32 * g + 16);
+              *reinterpret_cast<const u32x4*>(s_sgn + sr * IDX_STRIDE + 32 * g + 16);
           uint32_t w[1];
           pack32<1>(sv, w);
           *reinterpret_cast<uint32_t*>(a.signs + (bh * nblk + blk) * 1024 + Lc * 16 + part * 4) = w[0];
@@ -431,7 +433,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * t + 4 * g + r;
           const int slot = p0 + row;
-          const uint32_t v = s_idx[row * IDX_STRIDE + 16 * mt + c];
+          const uint32_t v = s_idx[(one ? 0 : row) * IDX_STRIDE + 16 * mt + c];
           const uint32_t mk = (slot >= lo_slot && slot < hi_slot) ? ((1u << BITS) - 1u) : 0u;
           const int bit = 4 * BITS * k + BITS * r;
           const int word = bit >> 5, off = bit & 31;
@@ -464,8 +466,8 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   if (tid < 64) {
     const int slot = p0 + tid;
     if (slot >= lo_slot && slot < hi_slot) {
-      a.norm[bh * a.T_cap + slot] = s_norm[tid];
-      if constexpr (KEY && QJL && BITS > 0) a.rnorm[bh * a.T_cap + slot] = s_rnorm[tid];
+      a.norm[bh * a.T_cap + slot] = s_norm[one ? 0 : tid];
+      if constexpr (KEY && QJL && BITS > 0) a.rnorm[bh * a.T_cap + slot] = s_rnorm[one ? 0 : tid];
     }
   }
 }
