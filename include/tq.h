@@ -176,8 +176,8 @@ int tq_cache_layout(const tq_config* cfg, int B, int Hkv, int T_cap, tq_cache_si
  *   (strides in elements; the 128 coordinates of a vector are contiguous); dtype in_dtype.
  *   Either may be NULL to write only keys or only values.
  * start_pos: device int32 [B]; token t of row b goes to slot start_pos[b] + t.  Slots at or
- *   beyond T_cap are skipped (the positions live in device memory, so they are not checked
- *   on the host).  n_new = 1 is the per-step append, n_new = T the bulk (prefill) fill.
+ *   beyond T_cap are skipped, and a negative start_pos[b] skips row b (the positions live in
+ *   device memory, so they are not checked on the host).  n_new = 1 is the per-step append, n_new = T the bulk (prefill) fill.
  * Per vector x: n = ||x||, y = R_eff x / n, z = sqrt(d) y, code = #{l : z >= threshold[l]};
  *   keys with the sketch: r = y - c[code]/sqrt(d) (r = y when k_bits == 0), stored residual
  *   norm ||r||, sign bits [S_b r >= 0].  A zero vector gets code 2^(b-1), residual norm 0,

@@ -131,13 +131,18 @@ def test_ragged_appends_and_canary(preset):
                 t.fill_(0.5)
     rng = np.random.default_rng(7)
     starts = [0, 37, 64]
-    steps = [(150, starts), (1, [s + 150 for s in starts]), (5, [s + 151 for s in starts])]
+    # the last step writes row 0's last slot and skips rows 1 (negative start) and 2 (beyond T_cap)
+    steps = [(150, starts), (1, [s + 150 for s in starts]), (5, [s + 151 for s in starts]),
+             (1, [T_cap - 1, -1, T_cap + 3])]
     X = {"k": np.zeros((B, Hkv, T_cap, 128), np.float32), "v": np.zeros((B, Hkv, T_cap, 128), np.float32)}
     written = np.zeros((B, T_cap), dtype=bool)
     for n_new, st in steps:
         k = wl.round_to_bf16(rng.standard_normal((B, Hkv, n_new, 128)).astype(np.float32) * 3)
         v = wl.round_to_bf16(rng.standard_normal((B, Hkv, n_new, 128)).astype(np.float32))
         for b in range(B):
+            if st[b] < 0 or st[b] + n_new > T_cap:
+                assert n_new == 1  # rows that the call skips
+                continue
             X["k"][b, :, st[b]:st[b] + n_new] = k[b]
             X["v"][b, :, st[b]:st[b] + n_new] = v[b]
             written[b, st[b]:st[b] + n_new] = True
