@@ -339,6 +339,17 @@ def main():
     keys_per_step = L * B * Hkv * T
     value = keys_per_step / (step_ms * 1e-3)
     log(f"step {step_ms:.3f} ms ({L} layers), wall {wall:.3f} s for {args.steps} steps")
+    # spread of single steps, from further replays with an event pair around each (outside the
+    # timed region above, which `value` comes from)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev[0].record()
+    for i in range(args.steps):
+        graph.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    one_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    step_spread = {"median": float(np.median(one_ms)), "p10": float(np.percentile(one_ms, 10)),
+                   "p90": float(np.percentile(one_ms, 90)), "steps": args.steps}
 
     # ---- dominant kernel: main attention kernel, HIP events on its stream ------------------------
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -354,6 +365,9 @@ def main():
             kern_ms.append(a0.elapsed_time(a1))
     tq.tq_profile_events()
     kern_s = float(np.mean(kern_ms)) * 1e-3
+    kern_us = np.array(kern_ms) * 1e3
+    kern_spread = {"median": float(np.median(kern_us)), "p10": float(np.percentile(kern_us, 10)),
+                   "p90": float(np.percentile(kern_us, 90)), "launches": len(kern_ms)}
     bytes_per_launch = B * Hkv * T * bytes_per_key
     achieved = bytes_per_launch / kern_s / 1e9
     log(f"attention kernel: {kern_s * 1e6:.2f} us per launch, {achieved:.0f} GB/s")
@@ -428,6 +442,10 @@ def main():
             "attend_call_us_per_layer": call_us,
             "bf16_comparator": comparator,
             "step_gbs": keys_per_step * bytes_per_key / (step_ms * 1e-3) / 1e9,
+            "step_ms_spread": step_spread,
+            "scores_per_s": keys_per_step * G / (step_ms * 1e-3),
+            "attend_launch_us_spread": kern_spread,
+            "attend_kernel_scores_per_s": B * Hq * T / kern_s,
             "bulk_quantize": {"vectors_per_launch": n_vec, "us_per_launch": bulk_s * 1e6,
                               "vectors_per_s": n_vec / bulk_s, "gbs": bulk_b / bulk_s / 1e9,
                               "frac": bulk_b / bulk_s / 1e9 / HBM_PEAK_GBS},
