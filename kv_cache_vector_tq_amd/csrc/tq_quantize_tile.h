@@ -293,7 +293,16 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
         const int o = 32 * wave + 16 * nt + col;
         const float z = acc[mt][nt][i] * zsv[i];
         float c = 0.f;
-        if constexpr (BITS > 0) {
+        if constexpr (BITS == 3 && !(KEY && QJL)) {
+          // only the code is needed: binary search over the sorted thresholds (the count of
+          // thresholds <= z, as the linear scan below), one compare per code bit.  (For 4-bit
+          // codes the select tree of the last step measured slower than the scan.)
+          const bool b0 = z >= thr[3];
+          const bool b1 = z >= (b0 ? thr[5] : thr[1]);
+          const float t2 = b0 ? (b1 ? thr[6] : thr[4]) : (b1 ? thr[2] : thr[0]);
+          const int idx = (b0 ? 4 : 0) | (b1 ? 2 : 0) | (z >= t2 ? 1 : 0);
+          s_idx[row * IDX_STRIDE + o] = static_cast<uint8_t>(idx);
+        } else if constexpr (BITS > 0) {
           int idx = 0;
           c = cent[0];
 #pragma unroll
