@@ -173,6 +173,52 @@ def test_ragged_appends_and_canary(preset):
     H.finish_stats(stats)
 
 
+@pytest.mark.parametrize("preset", ["turbo3", "turbo4"])
+def test_many_units_partial_tiles(preset):
+    """More tiles than persistent workgroups: a 100-token append from unaligned starts (partial
+    first and last blocks, several tiles per workgroup, so the next tile's rows are prefetched
+    across partial tiles), then a one-token append over 512 tiles (the general path, not the
+    one-tile-per-workgroup one).  Every written vector is checked against the oracle; slots
+    never written keep their canary bytes."""
+    B, Hkv, T_cap = 4, 64, 256
+    cb, dp, cache = _setup(preset, B, Hkv, T_cap, zero=False)
+    for t in cache.tensors().values():
+        if t is not None:
+            t.fill_(0xA5) if t.dtype == torch.uint8 else t.fill_(0.5)
+    rng = np.random.default_rng(11)
+    X = {"k": np.zeros((B, Hkv, T_cap, 128), np.float32), "v": np.zeros((B, Hkv, T_cap, 128), np.float32)}
+    written = np.zeros((B, T_cap), dtype=bool)
+    starts = [37, 64, 101, 0]
+    for n_new, st in [(100, starts), (1, [s + 100 for s in starts])]:
+        k = wl.round_to_bf16(rng.standard_normal((B, Hkv, n_new, 128)).astype(np.float32) * 2)
+        v = wl.round_to_bf16(rng.standard_normal((B, Hkv, n_new, 128)).astype(np.float32))
+        for b in range(B):
+            X["k"][b, :, st[b]:st[b] + n_new] = k[b]
+            X["v"][b, :, st[b]:st[b] + n_new] = v[b]
+            written[b, st[b]:st[b] + n_new] = True
+        say("many-units", preset, "append", n_new, st)
+        tq.tq_quantize_kv(cb, dp, cache, H.to_device(k, "bf16"), H.to_device(v, "bf16"),
+                          torch.tensor(st, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    hc = H.cache_host(cache)
+    orc = H.make_oracle(preset)
+    canary = {name: np.full_like(a, 0xA5) for name, a in hc.items() if a is not None and a.dtype == np.uint8}
+    stats = {}
+    for b in range(B):
+        wr = np.nonzero(written[b])[0]
+        un = np.nonzero(~written[b])[0]
+        for h in range(Hkv):
+            kg = H.unpack_keys(orc, hc, b, h, T_cap)
+            vg = H.unpack_values(orc, hc, b, h, T_cap)
+            H.compare_keys(orc, X["k"][b, h, wr], {n: a[wr] for n, a in kg.items()}, stats)
+            H.compare_values(orc, X["v"][b, h, wr], {n: a[wr] for n, a in vg.items()}, stats)
+            assert np.all(hc["k_norm"][b, h, un] == 0.5) and np.all(hc["v_norm"][b, h, un] == 0.5)
+            vc = H.unpack_values(orc, {**hc, **canary}, b, h, T_cap)
+            np.testing.assert_array_equal(vg["idx"][un], vc["idx"][un])
+    H.finish_stats(stats)
+    say("many-units", preset, stats)
+
+
 @pytest.mark.parametrize("preset,G", [("turbo3", 4), ("turbo4", 8), ("qjl1", 8), ("turbo3", 16)])
 def test_attention_ragged_lengths(preset, G):
     """Different sequence lengths per batch row (1, partial blocks, several slices)."""
