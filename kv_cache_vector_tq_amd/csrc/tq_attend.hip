@@ -24,6 +24,8 @@
 //     (batch row, kv-head), the last workgroup of each group of slices to merge that
 //     group (log-sum-exp) and apply R_eff^T to it (exact bf16-split MFMA, fp32 sums), and
 //     the last of those to merge the unrotated group results - no separate merge launch.
+#include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <mutex>
 #include <vector>
@@ -96,6 +98,59 @@ struct StepAppend {
 
 // tq_attend_decode; with step != NULL the query rotation runs inside the quantize launch of
 // the step's new tokens instead of a launch of its own.
+// Relative error of rounding x (> 0, within the f16 normal range) to f16's 11 significant bits,
+// ties to even as the device conversion.
+double f16_rel_error(float x) {
+  int e = 0;
+  const double f = std::frexp(static_cast<double>(x), &e);  // x = f 2^e, f in [0.5, 1)
+  const double r = std::nearbyint(f * 2048.0) / 2048.0;
+  return std::fabs(r - f) / f;
+}
+
+// The key centroid table holds f16(s c_l).  A common factor s (undone in fp32 with the logit
+// scale) is chosen so that the few distinct centroid magnitudes all sit nearly on the f16
+// grid: s = m / (smallest magnitude) with m an 11-bit integer, the m with the smallest largest
+// rounding error.  For 2-bit codes that error falls from 2e-4 to 4e-7, for 3-bit codes to
+// 4e-5.  s = 1 when the table is shared with the values (equal bit widths) or there are no
+// key codes.  Cached per codebook.
+float key_table_scale(const tq_codebook* cb) {
+  const int kb = cb->cfg.k_bits;
+  if (kb == 0 || kb == cb->cfg.v_bits) return 1.0f;
+  static std::mutex mu;
+  static std::vector<std::pair<std::vector<float>, float>> cache;
+  std::vector<float> key(cb->k_centroids, cb->k_centroids + (1 << kb));
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& e : cache)
+    if (e.first == key) return e.second;
+  std::vector<double> mags;
+  for (float c : key) {
+    const double m = std::fabs(static_cast<double>(c));
+    bool seen = false;
+    for (double x : mags) seen = seen || x == m;
+    if (!seen && m > 0) mags.push_back(m);
+  }
+  double lo = mags[0], hi = mags[0];
+  for (double x : mags) {
+    lo = std::min(lo, x);
+    hi = std::max(hi, x);
+  }
+  float best = 1.0f;
+  double best_err = 0;
+  for (double x : mags) best_err = std::max(best_err, f16_rel_error(static_cast<float>(x)));
+  for (int m = 1024; m < 2048; ++m) {
+    const float sc = static_cast<float>(m / lo);
+    if (static_cast<double>(sc) * hi > 60000.0) break;  // stay inside the f16 range
+    double err = 0;
+    for (double x : mags) err = std::max(err, f16_rel_error(static_cast<float>(x * sc)));
+    if (err < best_err) {
+      best_err = err;
+      best = sc;
+    }
+  }
+  cache.emplace_back(key, best);
+  return best;
+}
+
 int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache, const void* q, tq_dtype q_dtype,
            int Hq, const int32_t* seq_len, int max_seq_len, float scale, float* out, float* scores_out,
            void* workspace, size_t* workspace_bytes, void* hip_stream, const StepAppend* step) {
@@ -204,10 +259,12 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
   ma.mgroup = mgroup;
   ma.scale = scale;
   ma.scale_log2 = scale * LOG2E;
+  const float ks = key_table_scale(cb);
   for (int l = 0; l < 16; ++l) {
-    ma.k_cent[l] = cb->k_centroids[l];
+    ma.k_cent[l] = static_cast<float>(static_cast<double>(cb->k_centroids[l]) * ks);
     ma.v_cent[l] = cb->v_centroids[l];
   }
+  ma.k_unscale = static_cast<float>(1.0 / static_cast<double>(ks));
   const ProfileEvents& pe = profile_events();
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (pe.attend_start && pe.attend_stop) {

@@ -38,7 +38,8 @@ struct MainArgs {
   int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices, mgroup;
   float scale_log2;   // scale * log2(e)
   float scale;
-  float k_cent[16];
+  float k_cent[16];   // key centroids times k_scale (see key_table_scale in tq_attend.hip)
+  float k_unscale;     // 1 / k_scale
   float v_cent[16];
 };
 
@@ -436,7 +437,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
         bsl[kb][j] = lo16(x2, h2);
       }
     const float lscale = a.scale * LOG2E;
-    c1 = ldexpf(1.0f, e1) * INV_SQRT_D * lscale;
+    c1 = ldexpf(1.0f, e1) * INV_SQRT_D * lscale * a.k_unscale;
     c2 = ldexpf(1.0f, e2) * KAPPA * lscale;
   }
 
