@@ -431,36 +431,53 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
     } else {
       // value chunk Lc, fields 8 part .. 8 part + 7; field f = 4 mt + t holds tokens
       // 16 t + 4 g + r (r = 0..3) of coordinate 16 mt + c.
-      uint32_t w[BITS], m[BITS];
-#pragma unroll
-      for (int i = 0; i < BITS; ++i) w[i] = m[i] = 0;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int f = 8 * part + k;
-        const int mt = f >> 2, t = f & 3;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * t + 4 * g + r;
-          const int slot = p0 + row;
-          const uint32_t v = s_idx[(one ? 0 : row) * IDX_STRIDE + 16 * mt + c];
-          const uint32_t mk = (slot >= lo_slot && slot < hi_slot) ? ((1u << BITS) - 1u) : 0u;
-          const int bit = 4 * BITS * k + BITS * r;
-          const int word = bit >> 5, off = bit & 31;
-          w[word] |= (v & mk) << off;
-          m[word] |= mk << off;
-          if (off + BITS > 32) {
-            w[word + 1] |= (v & mk) >> (32 - off);
-            m[word + 1] |= mk >> (32 - off);
-          }
-        }
-      }
       uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + (bh * nblk + blk) * (1024 * BITS) + Lc * 16 * BITS +
                                                   part * 4 * BITS);
       if (!partial) {
-        // a whole block: every word is written, the old words are not needed (nor waited for)
+        // a whole block (every tile of a bulk fill): no slot masks, and every word is written,
+        // so the old words are not needed (nor waited for)
+        uint32_t w[BITS];
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) w[i] = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int f = 8 * part + k;
+          const int mt = f >> 2, t = f & 3;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t v = s_idx[(16 * t + 4 * g + r) * IDX_STRIDE + 16 * mt + c];
+            const int bit = 4 * BITS * k + BITS * r;
+            const int word = bit >> 5, off = bit & 31;
+            w[word] |= v << off;
+            if (off + BITS > 32) w[word + 1] |= v >> (32 - off);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < BITS; ++i) dst[i] = w[i];
       } else {
+        uint32_t w[BITS], m[BITS];
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) w[i] = m[i] = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int f = 8 * part + k;
+          const int mt = f >> 2, t = f & 3;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * t + 4 * g + r;
+            const int slot = p0 + row;
+            const uint32_t v = s_idx[(one ? 0 : row) * IDX_STRIDE + 16 * mt + c];
+            const uint32_t mk = (slot >= lo_slot && slot < hi_slot) ? ((1u << BITS) - 1u) : 0u;
+            const int bit = 4 * BITS * k + BITS * r;
+            const int word = bit >> 5, off = bit & 31;
+            w[word] |= (v & mk) << off;
+            m[word] |= mk << off;
+            if (off + BITS > 32) {
+              w[word + 1] |= (v & mk) >> (32 - off);
+              m[word + 1] |= mk >> (32 - off);
+            }
+          }
+        }
 #pragma unroll
         for (int i = 0; i < BITS; ++i) {
           if (m[i] == 0xFFFFFFFFu) {
