@@ -186,7 +186,7 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
   const int bpw = (nblk_max + NW * n_slices - 1) / (NW * n_slices);
   n_slices = (nblk_max + NW * bpw - 1) / (NW * bpw);
 
-  // groups of 16 slices (one load batch per merger); a single group needs no second level
+  // groups of MGROUP slices (one load batch per merger); a single group needs no second level
   const int mgroup = MGROUP;
   const int n_mgroups = (n_slices + mgroup - 1) / mgroup;
   const size_t cnt_bytes = align256(static_cast<size_t>(B) * cache->Hkv * (MAX_GROUPS + 1) * sizeof(unsigned));

@@ -638,7 +638,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
     st_dev2(a.part + ((bh * G + h) * a.n_slices + blockIdx.x) * PREC + j, A0, A1);
   }
 
-  // ---- merge over the slices: the last workgroup of each group of 16 slices merges the
+  // ---- merge over the slices: the last workgroup of each group of MGROUP slices merges the
   // group and applies R_eff^T, the last group merger merges the groups ---------------------
   const int ns = a.n_slices;
   const int mgroup = a.mgroup;
