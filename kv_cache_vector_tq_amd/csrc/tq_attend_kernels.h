@@ -191,13 +191,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int N>
-// Nontemporal: the cache stream is read once per call, and marking it so keeps it from
-// evicting what stays hot across calls (the parameter matrices the next decode step's
-// append reads, query records, partial records).
 __device__ __forceinline__ void load_dwords(uint32_t* dst, const uint8_t* src) {
 #pragma unroll
   for (int i = 0; i < N / 4; ++i)
-    *reinterpret_cast<u32x4*>(dst + 4 * i) = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 16 * i));
+    *reinterpret_cast<u32x4*>(dst + 4 * i) = *reinterpret_cast<const u32x4*>(src + 16 * i);
 }
 
 // ---- query prologue --------------------------------------------------------------------------
@@ -365,9 +362,9 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
 #pragma unroll
     for (int s = 0; s < NSETS; ++s) {
       const int64_t tok = bh * a.T_cap + blk * 64 + 16 * (s * TPD + tcls) + 4 * g;
-      d.kn[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.k_norm + tok));
-      if constexpr (QJL && KB > 0) d.kr[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.k_rnorm + tok));
-      d.vn[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.v_norm + tok));
+      d.kn[s] = *reinterpret_cast<const f32x4*>(a.k_norm + tok);
+      if constexpr (QJL && KB > 0) d.kr[s] = *reinterpret_cast<const f32x4*>(a.k_rnorm + tok);
+      d.vn[s] = *reinterpret_cast<const f32x4*>(a.v_norm + tok);
     }
   };
   // score operands from the prologue's record of head hh: lane (col, g) holds
