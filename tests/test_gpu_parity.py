@@ -173,6 +173,47 @@ def test_ragged_appends_and_canary(preset):
     H.finish_stats(stats)
 
 
+def test_keys_only_and_values_only():
+    """tq_quantize_kv with one tensor: a key-only 70-token append from unaligned starts (the
+    general path), then a value-only one-token append (one workgroup per tile, the row's last
+    slot included).  The written tensor matches the oracle; the other keeps its canary bytes."""
+    preset = "turbo3"
+    B, Hkv, T_cap = 2, 4, 128
+    cb, dp, cache = _setup(preset, B, Hkv, T_cap, zero=False)
+    for t in cache.tensors().values():
+        if t is not None:
+            t.fill_(0xA5) if t.dtype == torch.uint8 else t.fill_(0.5)
+    rng = np.random.default_rng(13)
+    k = wl.round_to_bf16(rng.standard_normal((B, Hkv, 70, 128)).astype(np.float32))
+    v = wl.round_to_bf16(rng.standard_normal((B, Hkv, 1, 128)).astype(np.float32))
+    k_st, v_st = [5, 0], [80, T_cap - 1]
+    say("one-tensor", "keys", k_st)
+    tq.tq_quantize_kv(cb, dp, cache, H.to_device(k, "bf16"), None, torch.tensor(k_st, dtype=torch.int32, device="cuda"))
+    say("one-tensor", "values", v_st)
+    tq.tq_quantize_kv(cb, dp, cache, None, H.to_device(v, "bf16"), torch.tensor(v_st, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    hc = H.cache_host(cache)
+    orc = H.make_oracle(preset)
+    canary = {name: np.full_like(a, 0xA5) for name, a in hc.items() if a is not None and a.dtype == np.uint8}
+    stats = {}
+    for b in range(B):
+        kw = np.arange(k_st[b], k_st[b] + 70)
+        k_un = np.setdiff1d(np.arange(T_cap), kw)
+        v_un = np.setdiff1d(np.arange(T_cap), [v_st[b]])
+        for h in range(Hkv):
+            kg = H.unpack_keys(orc, hc, b, h, T_cap)
+            vg = H.unpack_values(orc, hc, b, h, T_cap)
+            H.compare_keys(orc, k[b, h], {n: a[kw] for n, a in kg.items()}, stats)
+            H.compare_values(orc, v[b, h], {n: a[[v_st[b]]] for n, a in vg.items()}, stats)
+            assert np.all(hc["k_norm"][b, h, k_un] == 0.5) and np.all(hc["v_norm"][b, h, v_un] == 0.5)
+            kc = H.unpack_keys(orc, {**hc, **canary}, b, h, T_cap)
+            vc = H.unpack_values(orc, {**hc, **canary}, b, h, T_cap)
+            np.testing.assert_array_equal(kg["idx"][k_un], kc["idx"][k_un])
+            np.testing.assert_array_equal(kg["sign"][k_un], kc["sign"][k_un])
+            np.testing.assert_array_equal(vg["idx"][v_un], vc["idx"][v_un])
+    H.finish_stats(stats)
+
+
 @pytest.mark.parametrize("preset", ["turbo3", "turbo4"])
 def test_many_units_partial_tiles(preset):
     """More tiles than persistent workgroups: a 100-token append from unaligned starts (partial
