@@ -107,18 +107,17 @@ double f16_rel_error(float x) {
   return std::fabs(r - f) / f;
 }
 
-// The key centroid table holds f16(s c_l).  A common factor s (undone in fp32 with the logit
-// scale) is chosen so that the few distinct centroid magnitudes all sit nearly on the f16
-// grid: s = m / (smallest magnitude) with m an 11-bit integer, the m with the smallest largest
-// rounding error.  For 2-bit codes that error falls from 2e-4 to 4e-7, for 3-bit codes to
-// 4e-5.  s = 1 when the table is shared with the values (equal bit widths) or there are no
-// key codes.  Cached per codebook.
-float key_table_scale(const tq_codebook* cb) {
-  const int kb = cb->cfg.k_bits;
-  if (kb == 0 || kb == cb->cfg.v_bits) return 1.0f;
+// A centroid table holds f16(s c_l).  A common factor s (undone in fp32: with the logit scale
+// for keys, with the output normalisation for values) is chosen so that the few distinct
+// centroid magnitudes all sit nearly on the f16 grid: s = m / (smallest magnitude) with m an
+// 11-bit integer, the m with the smallest largest rounding error.  For 2-bit codes that error
+// falls from 2e-4 to 4e-7, for 3-bit codes to 4e-5.  Equal codebooks get equal factors, so a
+// table shared by keys and values (equal bit widths) serves both.  Cached per codebook.
+float table_scale(const float* cent, int bits) {
+  if (bits == 0) return 1.0f;
   static std::mutex mu;
   static std::vector<std::pair<std::vector<float>, float>> cache;
-  std::vector<float> key(cb->k_centroids, cb->k_centroids + (1 << kb));
+  std::vector<float> key(cent, cent + (1 << bits));
   std::lock_guard<std::mutex> lock(mu);
   for (const auto& e : cache)
     if (e.first == key) return e.second;
@@ -259,12 +258,15 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
   ma.mgroup = mgroup;
   ma.scale = scale;
   ma.scale_log2 = scale * LOG2E;
-  const float ks = key_table_scale(cb);
+  const float ks = table_scale(cb->k_centroids, cb->cfg.k_bits);
+  // equal widths share the key table (built from the key centroids), so they share its factor
+  const float vs = cb->cfg.k_bits == cb->cfg.v_bits ? ks : table_scale(cb->v_centroids, cb->cfg.v_bits);
   for (int l = 0; l < 16; ++l) {
     ma.k_cent[l] = static_cast<float>(static_cast<double>(cb->k_centroids[l]) * ks);
-    ma.v_cent[l] = cb->v_centroids[l];
+    ma.v_cent[l] = static_cast<float>(static_cast<double>(cb->v_centroids[l]) * vs);
   }
   ma.k_unscale = static_cast<float>(1.0 / static_cast<double>(ks));
+  ma.v_unscale = static_cast<float>(1.0 / static_cast<double>(vs));
   const ProfileEvents& pe = profile_events();
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (pe.attend_start && pe.attend_stop) {

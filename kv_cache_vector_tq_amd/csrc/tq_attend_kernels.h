@@ -38,9 +38,10 @@ struct MainArgs {
   int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices, mgroup;
   float scale_log2;   // scale * log2(e)
   float scale;
-  float k_cent[16];   // key centroids times k_scale (see key_table_scale in tq_attend.hip)
+  float k_cent[16];   // key centroids times a factor k_scale (table_scale in tq_attend.hip)
   float k_unscale;     // 1 / k_scale
-  float v_cent[16];
+  float v_cent[16];   // value centroids times v_scale
+  float v_unscale;     // 1 / v_scale
 };
 
 // Launches the attention kernel for key code width KB (k_qjl selects the sign sketch), value
@@ -703,8 +704,8 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
       const int h = 4 * g + i;
       if (h >= G) continue;
       const float L = ep->st[h][1];
-      // value centroids enter as c / sqrt(d)
-      const float f = L > 0.f ? INV_SQRT_D / L : 0.f;
+      // value centroids enter as c v_scale / sqrt(d)
+      const float f = L > 0.f ? INV_SQRT_D * a.v_unscale / L : 0.f;
       a.out[(bh * G + h) * D + 16 * wave + col] = u[i] * f;
     }
     return;
@@ -731,8 +732,8 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   if (ep->stage != 2) return;
   for (int h = wave; h < G; h += NW) {
     const Merged r = merge_records(a.gpart + (bh * G + h) * ngrp * PREC, ngrp, lane);
-    // value centroids enter as c / sqrt(d)
-    const float f = r.L > 0.f ? INV_SQRT_D / r.L : 0.f;
+    // value centroids enter as c v_scale / sqrt(d)
+    const float f = r.L > 0.f ? INV_SQRT_D * a.v_unscale / r.L : 0.f;
     float* o = a.out + (bh * G + h) * D + 2 * lane;  // out is only 4-byte aligned
     o[0] = r.A0 * f;
     o[1] = r.A1 * f;
