@@ -495,7 +495,19 @@ def cpu_baseline(w, host, Qh, preset, seconds):
             "sample": f"{reps} decode passes of one (batch row, kv-head) of one layer: unpack + attention of "
                       f"{G} q-heads over {T} keys, fp64 NumPy ({el:.1f} s)",
             "quantize_vectors_per_s": qreps * 4096 / qel,
-            "quantize_sample": f"{qreps} x (2048 keys + 2048 values) of the same slice ({qel:.1f} s)"}
+            "quantize_sample": f"{qreps} x (2048 keys + 2048 values) of the same slice ({qel:.1f} s)",
+            "cpu_model": host_cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
