@@ -187,10 +187,10 @@ extern "C" int tq_bf16_attend_decode(const void* k, const void* vt, int B, int H
     return fail(TQ_ERR_INVALID, "k, vt, q must be 16-byte aligned and out 4-byte aligned");
   const int units = B * Hkv;
   const int nch = (max_seq_len + 31) / 32;
-  // about two workgroups (8 waves) per CU, at least 4 chunks per wave
+  // about one workgroup per CU, at least 8 chunks per wave (fewer records to merge)
   const int cus = device_cu_count();
-  int n_wg = std::max(1, (2 * cus + units - 1) / units);
-  n_wg = std::min(n_wg, std::max(1, (nch + 15) / 16));
+  int n_wg = std::max(1, (cus + units - 1) / units);
+  n_wg = std::min(n_wg, std::max(1, (nch + 31) / 32));
   const int cpw = (nch + 4 * n_wg - 1) / (4 * n_wg);
   n_wg = (nch + 4 * cpw - 1) / (4 * cpw);
   const int n_waves = 4 * n_wg;
