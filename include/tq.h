@@ -208,9 +208,11 @@ int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, const void* k,
  *   be zero-filled before its first use (it holds arrival counters); every call leaves the
  *   counters zero again, so a workspace is reused without clearing.  Calls that share a
  *   workspace must not run concurrently (same stream, or ordered).
- * Environment: TQ_ATTN_MIN_BLOCKS (read once per process, default 2) is the smallest number
- *   of 64-key blocks a wave streams when the context is split over workgroups; it changes the
- *   split (and so the workspace size and the fp32 summation order), not the result's bound.
+ * Environment (read once per process; both change the split, and so the workspace size and
+ *   the fp32 summation order, not the result's bound): TQ_ATTN_MIN_BLOCKS (default 2) is the
+ *   smallest number of 64-key blocks a wave streams when the context is split over
+ *   workgroups; TQ_ATTN_MGROUP (default 16, at most 32) is the number of context slices a
+ *   first-level merge combines.
  * Errors: TQ_ERR_INVALID (NULL arguments, Hq not a multiple of Hkv, max_seq_len outside
  *   1..T_cap), TQ_ERR_UNSUPPORTED (group size or config), TQ_ERR_WORKSPACE (too small;
  *   required size written to *workspace_bytes), TQ_ERR_DEVICE (launch failure). */

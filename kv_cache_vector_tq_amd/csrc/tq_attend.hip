@@ -185,8 +185,12 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
   const int bpw = (nblk_max + NW * n_slices - 1) / (NW * n_slices);
   n_slices = (nblk_max + NW * bpw - 1) / (NW * bpw);
 
-  // groups of MGROUP slices (one load batch per merger); a single group needs no second level
-  const int mgroup = MGROUP;
+  // groups of 16 slices by default (TQ_ATTN_MGROUP, up to MGROUP: one load batch per merger);
+  // a single group needs no second level, and at most MAX_GROUPS groups are formed.  On the
+  // Llama-3.1-8B decode step (32 slices per unit) two groups of 16 took the 32-layer step from
+  // 0.90 to 0.85 ms against one group of 32.
+  static const int MGROUP_ASKED = env_int("TQ_ATTN_MGROUP", 16, 1, MGROUP);
+  const int mgroup = std::max(MGROUP_ASKED, (n_slices + MAX_GROUPS - 1) / MAX_GROUPS);
   const int n_mgroups = (n_slices + mgroup - 1) / mgroup;
   const size_t cnt_bytes = align256(static_cast<size_t>(B) * cache->Hkv * (MAX_GROUPS + 1) * sizeof(unsigned));
   const size_t part_bytes = align256(static_cast<size_t>(B) * Hq * n_slices * PREC * sizeof(float));
