@@ -293,10 +293,31 @@ def test_attention_ragged_lengths(preset, G):
 @pytest.mark.parametrize("B,G,T_cap,lens", [(2, 8, 10240, [10240, 3001]), (1, 8, 40960, [40960 - 100]),
                                             (1, 4, 262144, [262144 - 37])])
 def test_attention_merge_levels(B, G, T_cap, lens):
-    """Context splits of several sizes: 10 slices (one merge group, the second row leaving
-    most slices empty), 40 slices (groups of 32 and 8), and 256 slices (8 groups of 32).  A
-    second call with the same workspace must give identical outputs (the arrival counters are
-    reset per call)."""
+    """Context splits of several sizes with the default merge groups of 16 slices: 10 slices
+    (one merge group, the second row leaving most slices empty), 40 slices (groups of 16, 16
+    and 8), and 256 slices (16 groups of 16).  A second call with the same workspace must give
+    identical outputs (the arrival counters are reset per call)."""
+    _merge_case(B, G, T_cap, lens)
+
+
+@pytest.mark.parametrize("mgroup", [1, 32])
+def test_attention_merge_group_sizes(mgroup):
+    """TQ_ATTN_MGROUP at both ends of its range.  The library reads it once per process, so
+    the cases run in a child process.  1: 10 slices form 10 groups of one slice and 40 slices
+    form 20 groups of two (the group grows to keep at most 32 groups); 32: 10 slices form one
+    group, 40 slices groups of 32 and 8."""
+    import os
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("from tests.test_gpu_parity import _merge_case; "
+            "_merge_case(2, 8, 10240, [10240, 3001]); _merge_case(1, 8, 40960, [40960 - 100])")
+    say("merge group size", mgroup, "in a child process")
+    r = subprocess.run([sys.executable, "-u", "-c", code], cwd=root, timeout=100,
+                       env=dict(os.environ, TQ_ATTN_MGROUP=str(mgroup)))
+    assert r.returncode == 0, f"child exited with {r.returncode}"
+
+
+def _merge_case(B, G, T_cap, lens):
     preset, Hkv = "turbo3", 1
     cb, dp, cache = _setup(preset, B, Hkv, T_cap)
     rng = np.random.default_rng(13)
