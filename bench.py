@@ -252,7 +252,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 

@@ -1,0 +1,31 @@
+"""Host-side checks of bench.py: the one-GPU refusal and the bulk-quantize byte accounting."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("gpus", [2, 8])
+def test_more_than_one_gpu_is_refused(gpus):
+    """--gpus above 1 exits with status 2 and one JSON line that says why, before any GPU work."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", str(gpus)],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == gpus and "one GPU" in line["error"]
+
+
+@pytest.mark.parametrize("kb,kq,vb", [(2, 1, 3), (3, 1, 4), (0, 1, 3), (1, 1, 2), (4, 0, 4)])
+def test_bulk_bytes_match_the_layout(kb, kq, vb):
+    """Bulk quantize moves, per token and head, a bf16 key and value in (2 x 128 x 2 bytes) and
+    the packed record out (the layout's bytes per token)."""
+    B, Hkv, n = 3, 2, 1000
+    assert bench.bulk_bytes(B, Hkv, n, kb, kq, vb) == B * Hkv * n * (512 + layout.bytes_per_token(kb, kq, vb)["total"])
