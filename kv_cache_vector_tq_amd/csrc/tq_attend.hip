@@ -96,8 +96,6 @@ struct StepAppend {
   const int32_t* start_pos;
 };
 
-// tq_attend_decode; with step != NULL the query rotation runs inside the quantize launch of
-// the step's new tokens instead of a launch of its own.
 // Relative error of rounding x (> 0, within the f16 normal range) to f16's 11 significant bits,
 // ties to even as the device conversion.
 double f16_rel_error(float x) {
@@ -128,6 +126,7 @@ float table_scale(const float* cent, int bits) {
     for (double x : mags) seen = seen || x == m;
     if (!seen && m > 0) mags.push_back(m);
   }
+  if (mags.empty()) return 1.0f;  // an all-zero table is exact at any scale
   double lo = mags[0], hi = mags[0];
   for (double x : mags) {
     lo = std::min(lo, x);
@@ -150,6 +149,8 @@ float table_scale(const float* cent, int bits) {
   return best;
 }
 
+// tq_attend_decode; with step != NULL the query rotation runs inside the quantize launch of
+// the step's new tokens instead of a launch of its own.
 int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache, const void* q, tq_dtype q_dtype,
            int Hq, const int32_t* seq_len, int max_seq_len, float scale, float* out, float* scores_out,
            void* workspace, size_t* workspace_bytes, void* hip_stream, const StepAppend* step) {
