@@ -1,17 +1,20 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the TurboQuant compressed-KV hot path on one MI355X.
 
-Workload: a Llama-3.1-8B-shaped decode layer (batch 1, 32 q-heads / 8 kv-heads, d = 128,
-context 32768, bf16 K/V ~ N(0,1) x per-channel LogNormal(0, 0.5) scales), stacked as 32
-layers with distinct caches so that the packed caches (32 x 28.3 MB at turbo3) do not
-fit the 256 MB Infinity Cache.  One step = for every layer: quantize-on-write of the new
-token's K and V (8 + 8 vectors) into the packed cache, then decode attention of the 32
-q-heads over the 32768-key context straight from the codes.  The step is captured once
-in a HIP graph and replayed.
+Workload (default): batched decode, batch 16, 32 query heads / 8 kv-heads (GQA 4), d = 128,
+context 131072 per sequence, bf16 K/V drawn Student-t(5) per coordinate with 4 outlier
+channels x8, turbo3 (2-bit key codes + 1-bit sign sketch, 3-bit values).  Its packed cache
+(1.81 GB) is resident in HBM.  One step = quantize-on-write of the new token's K and V for
+every (batch row, kv-head) (16 x 8 + 16 x 8 vectors) into the packed cache, with the query
+rotation in the same launch, then decode attention of the 512 (batch row, q-head) pairs over
+the full context straight from the codes (tq_decode_step).  The step is captured once in a
+HIP graph and replayed.
 
 Prints one JSON line: keys/s (value), the roofline of the dominant kernel (the main
-decode-attention kernel: algorithmic bytes per launch over its average duration, timed
-with HIP events on its stream), and the oracle's rate on the host cores (cpu_baseline).
+decode-attention kernel: algorithmic bytes per launch over its average duration, timed with
+HIP events on its stream), and the oracle's rate on the host cores (cpu_baseline).  Further
+workloads (the Llama-3.1-8B decode layer as 32 layers at turbo3 and turbo4, the 70B-shaped
+layer, the 1M-context layer) and the uncompressed bf16 comparator go to "extra".
 """
 from __future__ import annotations
 
@@ -28,6 +31,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+HEADLINE = ("c3_batch16_t128k", "turbo3")
+# workloads whose 32-layer decode step is timed as well (caches of one layer fit the 256 MB
+# Infinity Cache, so 32 distinct layers are cycled)
+EXTRA_STEPS = [("c2_llama8b_layer_t32k", "turbo3"), ("c2_llama8b_layer_t32k", "turbo4")]
+OTHER_WORKLOADS = [("c4_llama70b_layer_b8_t128k", "qjl1"), ("c5_moe_attn_t1m", "turbo3"),
+                   ("c5_moe_attn_t1m", "turbo4")]
 
 
 def parse():
@@ -35,15 +44,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--preset", default="turbo3", choices=["turbo3", "turbo4", "qjl1"])
+    ap.add_argument("--workload", default=HEADLINE[0])
+    ap.add_argument("--preset", default=HEADLINE[1], choices=["turbo2", "turbo3", "turbo4", "qjl1"])
+    ap.add_argument("--layers", type=int, default=0,
+                    help="distinct layer caches cycled per step (0: 1 when a layer's cache exceeds 1 GiB, else 32)")
+    ap.add_argument("--kernel-launches", type=int, default=30,
+                    help="eager attention launches timed one by one for the roofline (at least 20)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="wall time spent timing the oracle on the host (0 disables)")
-    ap.add_argument("--kernel-reps", type=int, default=4, help="eager passes over the layers for kernel timing")
-    ap.add_argument("--workload", default="c2_llama8b_layer_t32k",
-                    help="workload name (default: the Llama-3.1-8B decode layer); others are for exploration")
+                    help="wall time spent timing the oracle on the host cores (0 disables)")
     ap.add_argument("--other-workloads", type=int, default=1,
-                    help="also time the attention kernel and bulk quantize on the other HBM-sized workloads (0: off)")
+                    help="also time the extra workloads and the bf16 comparator (0: headline only)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (calibrates the HBM byte counters) and exit")
     return ap.parse_args()
@@ -55,28 +65,28 @@ ATTEND_SOURCES = [os.path.join(ROOT, "kv_cache_vector_tq_amd", "csrc", f)
                   for f in ["tq_attend_kernels.h", "tq_attend.hip"] + [f"tq_attend_k{kb}.hip" for kb in range(5)]]
 
 
+def attend_sources_sha256() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ATTEND_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(workload: str, preset: str):
     """HBM bytes per launch of the attention kernel from the committed counter summary (FETCH_SIZE
     and WRITE_SIZE, each scaled by the same counter's reading for a copy of known size), or None
     when there is none for this workload or the kernel source changed since it was taken."""
-    import hashlib
-
     try:
         rec = json.load(open(TRAFFIC_FILE))
-        h = hashlib.sha256()
-        for f in ATTEND_SOURCES:
-            h.update(open(f, "rb").read())
-        digest = h.hexdigest()
+        digest = attend_sources_sha256()
     except (OSError, ValueError):
         return None
     for e in rec.get("entries", []):
         if e.get("workload") == workload and e.get("preset") == preset and e.get("source_sha256") == digest:
             return float(e["hbm_bytes_per_launch"])
     return None
-
-
-OTHER_WORKLOADS = [("c3_batch16_t128k", "turbo3"), ("c4_llama70b_layer_b8_t128k", "qjl1"),
-                   ("c5_moe_attn_t1m", "turbo3"), ("c5_moe_attn_t1m", "turbo4")]
 
 
 def draw_kv(w, dev):
@@ -105,7 +115,163 @@ def bulk_bytes(B, Hkv, n, kb, kq, vb):
     return B * Hkv * n * (256 + k_out) + B * Hkv * n * (256 + v_out)
 
 
-def time_workload(name, preset, dev, reps=5):
+def spread(values) -> dict:
+    a = np.asarray(values, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def event_pair():
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0, e1
+
+
+def run_step(name, preset, dev, layers, steps, warmup, launches, keep_host=False):
+    """The decode step of one workload over `layers` distinct layer caches: per layer,
+    tq_decode_step (the new token's K and V quantized into slot T-1 with the query rotation in
+    the same launch, then attention over the T keys), captured in a HIP graph and replayed.
+    Also times the bulk quantize that fills the caches, the attention kernel on its own
+    (`launches` eager launches, HIP events on its stream) and the append launch."""
+    import torch
+
+    import kv_cache_vector_tq_amd as tq
+    import tq_workloads as wl
+
+    w = wl.workload(name)
+    B, Hkv, Hq, T = w.B, w.Hkv, w.Hq, w.T
+    kb, kq, vb = wl.PRESETS[preset]
+    log("drawing inputs", w.name, preset)
+    K, V = draw_kv(w, dev)
+    Qh = wl.host_tensor(w, wl.TENSOR_Q)
+    Q = torch.from_numpy(Qh).to(dev).to(K.dtype)
+    cb = tq.tq_build_codebook(kb, kq, vb, seed=0)
+    dp = tq.upload_params(cb, dev)
+    caches = [tq.KVCache(cb, B, Hkv, T, device=dev, zero=False) for _ in range(layers)]
+    bytes_per_key = caches[0].bytes_per_token
+    zero = torch.zeros(B, dtype=torch.int32, device=dev)
+
+    # prefill: bulk quantize of the first T-1 tokens into every layer, timed per launch
+    qs, qe = event_pair()
+    tq.tq_profile_events(quant=(qs, qe))
+    bulk_ms = []
+    Kp, Vp = K[:, :, : T - 1], V[:, :, : T - 1]
+    for rep in range(max(layers, 3)):
+        tq.tq_quantize_kv(cb, dp, caches[rep % layers], Kp, Vp, zero)
+        torch.cuda.synchronize()
+        bulk_ms.append(qs.elapsed_time(qe))
+    tq.tq_profile_events()
+    n_vec = 2 * B * Hkv * (T - 1)
+    bulk_b = bulk_bytes(B, Hkv, T - 1, kb, kq, vb)
+    bulk_s = float(np.median(bulk_ms[1:])) * 1e-3
+    log(f"bulk quantize: {n_vec} vectors in {bulk_s * 1e6:.1f} us ({bulk_b / bulk_s / 1e9:.0f} GB/s)")
+
+    k_new = [K[:, :, T - 1:T].contiguous() for _ in range(layers)]
+    v_new = [V[:, :, T - 1:T].contiguous() for _ in range(layers)]
+    del K, V, Kp, Vp
+    torch.cuda.empty_cache()
+    qs_l = [Q.clone() for _ in range(layers)]
+    outs = [torch.empty((B, Hq, 128), dtype=torch.float32, device=dev) for _ in range(layers)]
+    start = torch.full((B,), T - 1, dtype=torch.int32, device=dev)
+    seq = torch.full((B,), T, dtype=torch.int32, device=dev)
+    ws = torch.empty(tq.attend_workspace_bytes(cb, dp, caches[0], Hq, T), dtype=torch.uint8, device=dev)
+
+    def step():
+        for l in range(layers):
+            tq.tq_decode_step(cb, dp, caches[l], k_new[l], v_new[l], start, qs_l[l], seq, T, out=outs[l],
+                              workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / steps
+    log(f"{w.name} {preset}: step {step_ms:.4f} ms ({layers} layer(s)), wall {wall:.3f} s for {steps} steps")
+    # single steps, from further replays with an event pair around each (outside the timed region)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        graph.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    one_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    del graph
+
+    # the attention kernel alone: eager launches, HIP events on its own stream around it
+    a0, a1 = event_pair()
+    tq.tq_profile_events(attend=(a0, a1))
+    kern_us = []
+    for i in range(launches):
+        l = i % layers
+        tq.tq_attend_decode(cb, dp, caches[l], qs_l[l], seq, T, out=outs[l], workspace=ws)
+        torch.cuda.synchronize()
+        kern_us.append(a0.elapsed_time(a1) * 1e3)
+    tq.tq_profile_events()
+    # the step's append launch (new K and V of every unit plus the query rotation)
+    tq.tq_profile_events(quant=(qs, qe))
+    app_us = []
+    for i in range(launches):
+        l = i % layers
+        tq.tq_decode_step(cb, dp, caches[l], k_new[l], v_new[l], start, qs_l[l], seq, T, out=outs[l],
+                          workspace=ws)
+        torch.cuda.synchronize()
+        app_us.append(qs.elapsed_time(qe) * 1e3)
+    tq.tq_profile_events()
+    kern = spread(kern_us)
+    bytes_per_launch = B * Hkv * T * bytes_per_key
+    achieved = bytes_per_launch / (kern["mean"] * 1e-6) / 1e9
+    log(f"attention kernel: mean {kern['mean']:.2f} us (median {kern['median']:.2f}), {achieved:.0f} GB/s; "
+        f"append launch median {np.median(app_us):.2f} us")
+    keys_per_step = layers * B * Hkv * T
+    res = {
+        "workload": w.name, "preset": preset, "layers": layers, "bytes_per_key": bytes_per_key,
+        "step_ms": step_ms, "keys_per_s": keys_per_step / (step_ms * 1e-3),
+        "scores_per_s": keys_per_step * w.G / (step_ms * 1e-3),
+        "step_gbs": keys_per_step * bytes_per_key / (step_ms * 1e-3) / 1e9,
+        "step_ms_spread": spread(one_ms),
+        "attend_kernel": {"us": kern, "bytes_per_launch": bytes_per_launch, "gbs": achieved,
+                          "frac": achieved / HBM_PEAK_GBS, "keys_per_s": B * Hkv * T / (kern["mean"] * 1e-6),
+                          "scores_per_s": B * Hq * T / (kern["mean"] * 1e-6)},
+        "append_launch_us": spread(app_us),
+        "append_vectors": 2 * B * Hkv,
+        "bulk_quantize": {"vectors_per_launch": n_vec, "us_per_launch": bulk_s * 1e6, "vectors_per_s": n_vec / bulk_s,
+                          "gbs": bulk_b / bulk_s / 1e9, "frac": bulk_b / bulk_s / 1e9 / HBM_PEAK_GBS},
+    }
+    if keep_host:
+        # host copies of the first units of layer 0 for the oracle on the host cores
+        n_units = min(16, B * Hkv)
+        units = [(u // Hkv, u % Hkv) for u in range(n_units)]
+        res["_host"] = [{n: (None if t is None else t[b, h].cpu().numpy()) for n, t in caches[0].tensors().items()}
+                        for b, h in units]
+        res["_units"] = units
+        res["_q"] = Qh
+    del caches, k_new, v_new, ws, outs, qs_l
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_workload(name, preset, dev, launches=20):
     """Attention kernel (HIP events on its stream) and bulk quantize of the full context for one
     workload: one cache, inputs resident in HBM."""
     import torch
@@ -121,10 +287,7 @@ def time_workload(name, preset, dev, reps=5):
     dp = tq.upload_params(cb, dev)
     cache = tq.KVCache(cb, w.B, w.Hkv, w.T, device=dev, zero=False)
     zero = torch.zeros(w.B, dtype=torch.int32, device=dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    e1.record()
-    torch.cuda.synchronize()
+    e0, e1 = event_pair()
     q_ms = []
     tq.tq_profile_events(quant=(e0, e1))
     for _ in range(3):
@@ -134,25 +297,26 @@ def time_workload(name, preset, dev, reps=5):
     tq.tq_profile_events()
     del K, V
     seq = torch.full((w.B,), w.T, dtype=torch.int32, device=dev)
-    ws = torch.zeros(tq.attend_workspace_bytes(cb, dp, cache, w.Hq, w.T), dtype=torch.uint8, device=dev)
+    ws = torch.empty(tq.attend_workspace_bytes(cb, dp, cache, w.Hq, w.T), dtype=torch.uint8, device=dev)
     out = torch.empty((w.B, w.Hq, 128), dtype=torch.float32, device=dev)
     tq.tq_attend_decode(cb, dp, cache, Q, seq, w.T, out=out, workspace=ws)
     torch.cuda.synchronize()
-    a_ms = []
+    a_us = []
     tq.tq_profile_events(attend=(e0, e1))
-    for _ in range(reps):
+    for _ in range(launches):
         tq.tq_attend_decode(cb, dp, cache, Q, seq, w.T, out=out, workspace=ws)
         torch.cuda.synchronize()
-        a_ms.append(e0.elapsed_time(e1))
+        a_us.append(e0.elapsed_time(e1) * 1e3)
     tq.tq_profile_events()
-    a_s = float(np.median(a_ms)) * 1e-3
+    a = spread(a_us)
     q_s = float(np.median(q_ms[1:])) * 1e-3
     att_bytes = w.B * w.Hkv * w.T * cache.bytes_per_token
     qb = bulk_bytes(w.B, w.Hkv, w.T, kb, kq, vb)
     n_vec = 2 * w.B * w.Hkv * w.T
     res = {"workload": w.name, "preset": preset,
-           "attend": {"us": a_s * 1e6, "keys_per_s": w.B * w.Hkv * w.T / a_s, "gbs": att_bytes / a_s / 1e9,
-                      "frac": att_bytes / a_s / 1e9 / HBM_PEAK_GBS, "bytes": att_bytes},
+           "attend": {"us": a, "keys_per_s": w.B * w.Hkv * w.T / (a["mean"] * 1e-6),
+                      "gbs": att_bytes / (a["mean"] * 1e-6) / 1e9,
+                      "frac": att_bytes / (a["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS, "bytes": att_bytes},
            "bulk_quantize": {"us": q_s * 1e6, "vectors_per_s": n_vec / q_s, "gbs": qb / q_s / 1e9,
                              "frac": qb / q_s / 1e9 / HBM_PEAK_GBS, "vectors": n_vec}}
     del cache, ws, out
@@ -160,25 +324,34 @@ def time_workload(name, preset, dev, reps=5):
     return res
 
 
-def stream_read_gbs(dev, mib=2048):
-    """Read bandwidth of the box: row sums over a 2 GiB fp32 buffer (a streaming read that
-    writes almost nothing), 5 passes timed with events."""
+def read_ceiling(dev, mib=4096, grids=(1024, 2048, 4096, 8192), reps=5):
+    """The box's streaming read rate: this library's read probe (16-byte loads, one launch over a
+    4 GiB buffer, well beyond the 256 MB Infinity Cache) at several grid sizes; the best median
+    over `reps` launches per grid."""
     import torch
 
-    x = torch.ones(mib << 18, dtype=torch.float32, device=dev)
-    xv = x.view(4096, -1)
-    xv.sum(dim=1)
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(5):
-        xv.sum(dim=1)
-    t1.record()
-    torch.cuda.synchronize()
-    gbs = 5 * x.numel() * 4 / (t0.elapsed_time(t1) * 1e-3) / 1e9
-    del x
+    import kv_cache_vector_tq_amd as tq
+
+    buf = torch.zeros(mib << 20, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best, per_grid = 0.0, {}
+    for g in grids:
+        tq.tq_read_probe(buf, g, sink)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            tq.tq_read_probe(buf, g, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        gbs = buf.numel() / float(np.median(ts)) / 1e9
+        per_grid[str(g)] = gbs
+        best = max(best, gbs)
+    del buf
     torch.cuda.empty_cache()
-    return gbs
+    return best, per_grid
 
 
 def bf16_comparator(w, layers, dev, reps=3):
@@ -210,13 +383,11 @@ def bf16_comparator(w, layers, dev, reps=3):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) * 1e3 / (reps * layers)
 
-    # (a) baseline kernel
     Vts = [tq.bf16_value_chunks(v) for v in Vs]
     ws = torch.empty(tq.bf16_attend_workspace_bytes(B, Hkv, T, Hq, T), dtype=torch.uint8, device=dev)
     hip_us = timed(lambda: [tq.tq_bf16_attend_decode(Ks[l], Vts[l], q, seq, T, out=out, workspace=ws)
                             for l in range(layers)])
     del Vts
-    # (b) plain PyTorch, one bmm per kv-head group
     qT = q.view(B * Hkv, G, 128).transpose(1, 2).contiguous()  # [B*Hkv, 128, G]
     scale = 1.0 / math.sqrt(128)
 
@@ -244,18 +415,14 @@ def copy_probe(mib: int):
     print(json.dumps({"copy_probe_bytes": n, "copies": 5}), flush=True)
 
 
-def log(*a):
-    print("[bench]", *a, file=sys.stderr, flush=True)
-
-
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1 (no multi-GPU path "
+                                   "is built: the kernels run on one GPU's share of the work)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
-
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
@@ -268,235 +435,158 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = wl.workload(args.workload)
-    B, Hkv, Hq, T, G = w.B, w.Hkv, w.Hq, w.T, w.G
-    L = args.layers
     kb, kq, vb = wl.PRESETS[args.preset]
+    per_layer = w.B * w.Hkv * w.T * tq.tq_cache_layout(kb, kq, vb, 1, 1, 64)["bytes_per_token"]
+    layers = args.layers or (1 if per_layer > (1 << 30) else 32)
+    launches = max(20, args.kernel_launches)
 
-    # ---- inputs (seeded, synthetic) -------------------------------------------------------------
-    log("drawing inputs", w.name)
-    K, V = draw_kv(w, dev)
-    Qh = wl.host_tensor(w, wl.TENSOR_Q)
-    Q = torch.from_numpy(Qh).to(dev).to(K.dtype)
+    log("read probe")
+    read_gbs, read_grid = read_ceiling(dev)
+    log(f"stream read ceiling {read_gbs:.0f} GB/s {read_grid}")
 
-    cb = tq.tq_build_codebook(kb, kq, vb, seed=0)
-    dp = tq.upload_params(cb, dev)
-    caches = [tq.KVCache(cb, B, Hkv, T, device=dev, zero=False) for _ in range(L)]
-    bytes_per_key = caches[0].bytes_per_token
-    zero = torch.zeros(B, dtype=torch.int32, device=dev)
+    head = run_step(w.name, args.preset, dev, layers, args.steps, args.warmup, launches,
+                    keep_host=args.cpu_seconds > 0)
+    host = (head.pop("_host", None), head.pop("_units", None), head.pop("_q", None))
 
-    # ---- prefill: bulk quantize of T-1 tokens into every layer (timed per launch) ---------------
-    qs, qe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    qs.record()
-    qe.record()
-    torch.cuda.synchronize()
-    tq.tq_profile_events(quant=(qs, qe))
-    bulk_ms = []
-    Kp, Vp = K[:, :, : T - 1], V[:, :, : T - 1]
-    for l in range(L):
-        tq.tq_quantize_kv(cb, dp, caches[l], Kp, Vp, zero)
-        torch.cuda.synchronize()
-        bulk_ms.append(qs.elapsed_time(qe))
-    tq.tq_profile_events()
-    n_vec = 2 * B * Hkv * (T - 1)
-    bulk_b = bulk_bytes(B, Hkv, T - 1, kb, kq, vb)
-    bulk_s = float(np.median(bulk_ms[1:] if L > 1 else bulk_ms)) * 1e-3
-    log(f"bulk quantize: {n_vec} vectors in {bulk_s * 1e6:.1f} us")
-
-    # ---- one decode step over all layers ----------------------------------------------------------
-    k_new = [K[:, :, T - 1:T].contiguous() for _ in range(L)]
-    v_new = [V[:, :, T - 1:T].contiguous() for _ in range(L)]
-    qs_l = [Q.clone() for _ in range(L)]
-    outs = [torch.empty((B, Hq, 128), dtype=torch.float32, device=dev) for _ in range(L)]
-    start = torch.full((B,), T - 1, dtype=torch.int32, device=dev)
-    seq = torch.full((B,), T, dtype=torch.int32, device=dev)
-    ws = torch.zeros(tq.attend_workspace_bytes(cb, dp, caches[0], Hq, T), dtype=torch.uint8, device=dev)
-
-    # per layer: the new token's quantize-on-write, then attention (tq_decode_step: the query
-    # rotation rides in the quantize launch, so two launches per layer)
-    def step():
-        for l in range(L):
-            tq.tq_decode_step(cb, dp, caches[l], k_new[l], v_new[l], start, qs_l[l], seq, T, out=outs[l],
-                              workspace=ws)
-
-    step()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = t0.elapsed_time(t1) / args.steps
-    keys_per_step = L * B * Hkv * T
-    value = keys_per_step / (step_ms * 1e-3)
-    log(f"step {step_ms:.3f} ms ({L} layers), wall {wall:.3f} s for {args.steps} steps")
-    # spread of single steps, from further replays with an event pair around each (outside the
-    # timed region above, which `value` comes from)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    ev[0].record()
-    for i in range(args.steps):
-        graph.replay()
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    one_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
-    step_spread = {"median": float(np.median(one_ms)), "p10": float(np.percentile(one_ms, 10)),
-                   "p90": float(np.percentile(one_ms, 90)), "steps": args.steps}
-
-    # ---- dominant kernel: main attention kernel, HIP events on its stream ------------------------
-    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a0.record()
-    a1.record()
-    torch.cuda.synchronize()
-    tq.tq_profile_events(attend=(a0, a1))
-    kern_ms = []
-    for _ in range(args.kernel_reps):
-        for l in range(L):
-            tq.tq_attend_decode(cb, dp, caches[l], qs_l[l], seq, T, out=outs[l], workspace=ws)
-            torch.cuda.synchronize()
-            kern_ms.append(a0.elapsed_time(a1))
-    tq.tq_profile_events()
-    kern_s = float(np.mean(kern_ms)) * 1e-3
-    kern_us = np.array(kern_ms) * 1e3
-    kern_spread = {"median": float(np.median(kern_us)), "p10": float(np.percentile(kern_us, 10)),
-                   "p90": float(np.percentile(kern_us, 90)), "launches": len(kern_ms)}
-    bytes_per_launch = B * Hkv * T * bytes_per_key
-    achieved = bytes_per_launch / kern_s / 1e9
-    log(f"attention kernel: {kern_s * 1e6:.2f} us per launch, {achieved:.0f} GB/s")
-
-    # whole attention call (query prologue + main kernel) per layer, back to back over the layers
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(args.kernel_reps):
-        for l in range(L):
-            tq.tq_attend_decode(cb, dp, caches[l], qs_l[l], seq, T, out=outs[l], workspace=ws)
-    c1.record()
-    torch.cuda.synchronize()
-    call_us = c0.elapsed_time(c1) * 1e3 / (args.kernel_reps * L)
-    log(f"attention call (prologue + main): {call_us:.2f} us per layer")
-
-    # host copy of one (batch row, kv-head) of layer 0 for the oracle on the host cores
-    host = {n: (None if t is None else t[0, 0].cpu().numpy()) for n, t in caches[0].tensors().items()}
-
-    # ---- the other HBM-sized workloads (one cache each; the step's caches are freed first) -------
-    others = []
-    comparator = None
+    steps_extra, others, comparator = [], [], None
     if args.other_workloads:
-        del caches, k_new, v_new, K, V, ws, outs, qs_l, graph
-        torch.cuda.empty_cache()
-        bf16_us, torch_us = bf16_comparator(w, L, dev)
-        bf16_bytes = 2 * B * Hkv * T * 128 * 2
-        comparator = {"kind": "uncompressed bf16 decode attention, same shape: tq_bf16_attend_decode (this "
-                              "library's baseline kernel) and plain PyTorch (bmm, fp32 softmax, bmm)",
-                      "us_per_layer": bf16_us, "keys_per_s": B * Hkv * T / (bf16_us * 1e-6),
-                      "gbs": bf16_bytes / (bf16_us * 1e-6) / 1e9,
-                      "torch_us_per_layer": torch_us,
-                      "compressed_call_us_per_layer": call_us,
-                      "speedup_of_compressed_call": bf16_us / call_us}
+        for name, preset in EXTRA_STEPS:
+            if (name, preset) == (w.name, args.preset):
+                continue
+            steps_extra.append(run_step(name, preset, dev, 32, args.steps, args.warmup, 2 * 32))
+            log(json.dumps(steps_extra[-1]))
+        c2 = wl.workload("c2_llama8b_layer_t32k")
+        bf16_us, torch_us = bf16_comparator(c2, 32, dev)
+        bf16_bytes = 2 * c2.B * c2.Hkv * c2.T * 128 * 2
+        c2_call = next((s for s in steps_extra if s["preset"] == "turbo3"), None)
+        comparator = {"kind": "uncompressed bf16 decode attention at the Llama-3.1-8B layer shape (32 distinct "
+                              "layers): tq_bf16_attend_decode (this library's baseline kernel) and plain PyTorch "
+                              "(bmm, fp32 softmax, bmm)",
+                      "us_per_layer": bf16_us, "keys_per_s": c2.B * c2.Hkv * c2.T / (bf16_us * 1e-6),
+                      "gbs": bf16_bytes / (bf16_us * 1e-6) / 1e9, "torch_us_per_layer": torch_us}
+        if c2_call is not None:
+            per_layer_us = c2_call["step_ms"] * 1e3 / c2_call["layers"]
+            comparator["compressed_step_us_per_layer"] = per_layer_us
+            comparator["speedup_of_compressed_step"] = bf16_us / per_layer_us
         log(json.dumps(comparator))
         for name, preset in OTHER_WORKLOADS:
             log("timing", name, preset)
             others.append(time_workload(name, preset, dev))
             log(json.dumps(others[-1]))
-    read_gbs = stream_read_gbs(dev)
-    log(f"stream read ceiling {read_gbs:.0f} GB/s")
 
-    # ---- oracle on the host cores ----------------------------------------------------------------
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, host, Qh, args.preset, args.cpu_seconds)
+        cpu = cpu_baseline(w, args.preset, *host, args.cpu_seconds)
 
+    ka = head["attend_kernel"]
     line = {
         "metric": "compressed-KV decode attention keys/s + achieved HBM GB/s (% of peak) at 3/4 bit",
-        "value": value,
+        "value": head["keys_per_s"],
         "unit": "keys/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": step_ms,
+        "ms_per_step": head["step_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "f16 MFMA operands (query as an f16 hi+lo pair), fp32 accumulation; bf16 MFMA rotation",
         "data": "synthetic",
-        "config": {"workload": w.name, "preset": args.preset, "batch": B, "q_heads": Hq, "kv_heads": Hkv,
-                   "head_dim": 128, "context": T, "layers": L, "bytes_per_key": bytes_per_key,
-                   "step": "per layer: quantize-on-write of 1 new token (K+V) then decode attention (tq_decode_step)"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(w.name, args.preset),
-                     "kernel": "attend_kernel (main decode attention)", "bytes_per_launch": bytes_per_launch,
-                     "avg_launch_us": kern_s * 1e6},
+        "config": {"workload": w.name, "preset": args.preset, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": 128, "context": w.T, "layers": layers, "bytes_per_key": head["bytes_per_key"],
+                   "step": f"tq_decode_step: quantize-on-write of {w.B}x{w.Hkv} new K and V vectors (query rotation "
+                           f"in the same launch), then decode attention of {w.B * w.Hq} (batch row, q-head) pairs "
+                           f"over {w.T} keys"},
+        "roofline": {"bound": "hbm", "achieved": ka["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ka["frac"], "traffic": measured_traffic(w.name, args.preset),
+                     "kernel": "attend_kernel (main decode attention)", "bytes_per_launch": ka["bytes_per_launch"],
+                     "avg_launch_us": ka["us"]["mean"], "launches": ka["us"]["n"]},
         "cpu_baseline": cpu,
         "extra": {
-            "attend_frac_of_measured_read": achieved / read_gbs,
+            "headline": head,
             "measured_read_gbs": read_gbs,
+            "read_probe_gbs_by_grid": read_grid,
+            "attend_frac_of_measured_read": ka["gbs"] / read_gbs,
+            "steps": steps_extra,
             "workloads": others,
-            "attend_call_us_per_layer": call_us,
             "bf16_comparator": comparator,
-            "step_gbs": keys_per_step * bytes_per_key / (step_ms * 1e-3) / 1e9,
-            "step_ms_spread": step_spread,
-            "scores_per_s": keys_per_step * G / (step_ms * 1e-3),
-            "attend_launch_us_spread": kern_spread,
-            "attend_kernel_scores_per_s": B * Hq * T / kern_s,
-            "bulk_quantize": {"vectors_per_launch": n_vec, "us_per_launch": bulk_s * 1e6,
-                              "vectors_per_s": n_vec / bulk_s, "gbs": bulk_b / bulk_s / 1e9,
-                              "frac": bulk_b / bulk_s / 1e9 / HBM_PEAK_GBS},
+            "targets": {"attend_frac": 0.70, "quantize_frac": 0.60},
         },
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(w, host, Qh, preset, seconds):
-    """The oracle (fp64 NumPy) decoding one (batch row, kv-head) of one layer from its packed cache:
-    unpack the codes, then attention of the G q-heads over the full context.  Repeated for
-    about `seconds`; reported as keys/s (keys attended per second)."""
+def _oracle_unit_worker(job):
+    """One host core: the oracle (fp64 NumPy, one BLAS thread) decoding one (batch row, kv-head)
+    unit from its packed cache (unpack + attention of its G q-heads over T keys) until `seconds`
+    have passed, then quantizing 2048 keys + 2048 values of the same slice for seconds / 4."""
+    preset, unit_cache, q, T, workload, b, h, seconds = job
+    from threadpoolctl import threadpool_limits
+
     import tq_workloads as wl
     from oracle.pipeline import Oracle
 
+    with threadpool_limits(limits=1):
+        orc = Oracle(*wl.PRESETS[preset], seed=0)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            k = orc.unpack_keys(unit_cache["k_codes"], unit_cache["k_signs"], unit_cache["k_norm"],
+                                unit_cache["k_rnorm"], T)
+            v = orc.unpack_values(unit_cache["v_codes"], unit_cache["v_norm"], T)
+            orc.attend(q, k, v, T=T)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+        w = wl.workload(workload)
+        xk = wl.host_slice(w, b, h, wl.TENSOR_K, n=2048).astype(np.float64)
+        xv = wl.host_slice(w, b, h, wl.TENSOR_V, n=2048).astype(np.float64)
+        qreps, q0 = 0, time.perf_counter()
+        while True:
+            orc.quantize_keys(xk)
+            orc.quantize_values(xv)
+            qreps += 1
+            qel = time.perf_counter() - q0
+            if qel >= seconds / 4:
+                break
+    return reps, el, qreps, qel
+
+
+def cpu_baseline(w, preset, host_units, units, Qh, seconds):
+    """The oracle on the host cores: one worker process per core (at most 16, the GPU's share of
+    the box), each single-threaded, each decoding a different (batch row, kv-head) unit of the
+    workload from the GPU-written packed cache at full context, repeated for about `seconds`.
+    keys/s = keys attended by all workers / wall time."""
+    import concurrent.futures
+    import multiprocessing
+
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    orc = Oracle(*wl.PRESETS[preset], seed=0)
-    T, G = w.T, w.G
-    q = Qh[0, :G].astype(np.float64)
-    reps = 0
+        n_cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n_cores = os.cpu_count() or 1
+    workers = max(1, min(16, n_cores, len(host_units)))
+    jobs = []
+    for i in range(workers):
+        b, h = units[i]
+        jobs.append((preset, host_units[i], Qh[b, h * w.G:(h + 1) * w.G].astype(np.float64), w.T, w.name, b, h,
+                     seconds))
+    ctx = multiprocessing.get_context("spawn")
     t0 = time.perf_counter()
-    while True:
-        k = orc.unpack_keys(host["k_codes"], host["k_signs"], host["k_norm"], host["k_rnorm"], T)
-        v = orc.unpack_values(host["v_codes"], host["v_norm"], T)
-        orc.attend(q, k, v, T=T)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    # quantize-on-write: the oracle quantizing the first 2048 keys and values of the same slice
-    xk = wl.host_slice(w, 0, 0, wl.TENSOR_K, n=2048).astype(np.float64)
-    xv = wl.host_slice(w, 0, 0, wl.TENSOR_V, n=2048).astype(np.float64)
-    qreps = 0
-    q0 = time.perf_counter()
-    while True:
-        orc.quantize_keys(xk)
-        orc.quantize_values(xv)
-        qreps += 1
-        qel = time.perf_counter() - q0
-        if qel >= seconds / 4:
-            break
-    return {"value": reps * T / el, "unit": "keys/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} decode passes of one (batch row, kv-head) of one layer: unpack + attention of "
-                      f"{G} q-heads over {T} keys, fp64 NumPy ({el:.1f} s)",
-            "quantize_vectors_per_s": qreps * 4096 / qel,
-            "quantize_sample": f"{qreps} x (2048 keys + 2048 values) of the same slice ({qel:.1f} s)",
-            "cpu_model": host_cpu_model(), "host_cpus": os.cpu_count()}
+    with concurrent.futures.ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        res = list(ex.map(_oracle_unit_worker, jobs))
+    wall = time.perf_counter() - t0
+    keys = sum(r[0] for r in res) * w.T
+    att_rate = sum(r[0] * w.T / r[1] for r in res)
+    q_rate = sum(r[2] * 4096 / r[3] for r in res)
+    return {"value": att_rate, "unit": "keys/s", "cores": workers, "kind": "oracle",
+            "sample": f"{workers} worker processes (one BLAS thread each), each decoding a different (batch row, "
+                      f"kv-head) unit of {w.name} {preset} from the GPU-written cache: unpack + attention of "
+                      f"{w.G} q-heads over {w.T} keys, fp64 NumPy; {sum(r[0] for r in res)} unit passes, "
+                      f"{keys} keys in {wall:.1f} s of wall time (value = sum of per-worker rates)",
+            "quantize_vectors_per_s": q_rate,
+            "quantize_sample": "per worker: 2048 keys + 2048 values of its unit, repeated for "
+                               f"{seconds / 4:.1f} s (sum of per-worker rates)",
+            "cpu_model": host_cpu_model(), "host_cpus": n_cores}
 
 
 def host_cpu_model() -> str:

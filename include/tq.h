@@ -203,11 +203,12 @@ int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, const void* k,
  *   (rnorm = 1 when k_bits == 0); p = softmax(scale * score);
  *   out = R_eff^T sum_i p_i nv_i cv[codev_i]/sqrt(d)   (fp32 [B][Hq][128]).
  * scores_out: NULL or device fp32 [B][Hq][T_cap]; receives scale * score_i for i < seq_len[b].
- * workspace: device scratch of *workspace_bytes bytes (256-byte aligned).  Call with
- *   workspace == NULL to get the required size in *workspace_bytes (returns TQ_OK).  It must
- *   be zero-filled before its first use (it holds arrival counters); every call leaves the
- *   counters zero again, so a workspace is reused without clearing.  Calls that share a
- *   workspace must not run concurrently (same stream, or ordered).
+ * workspace: device scratch of *workspace_bytes bytes (256-byte aligned), owned by the caller.
+ *   Call with workspace == NULL to get the required size in *workspace_bytes (returns TQ_OK).
+ *   It needs no initial contents: every call first sets the arrival counters it keeps there
+ *   to zero (in its query-rotation launch), so a workspace can be reused across calls of any
+ *   shape, also after an earlier call that did not finish.  Calls that share a workspace must
+ *   not run concurrently (same stream, or otherwise ordered).
  * Environment (read once per process; both change the split, and so the workspace size and
  *   the fp32 summation order, not the result's bound): TQ_ATTN_MIN_BLOCKS (default 2) is the
  *   smallest number of 64-key blocks a wave streams when the context is split over
@@ -257,6 +258,15 @@ int tq_bf16_attend_decode(const void* k, const void* vt, int B, int Hkv, int T_c
  * pair.  The events are only recorded; the caller reads them after synchronizing.  Returns
  * TQ_OK. */
 int tq_profile_events(void* attend_start, void* attend_stop, void* quant_start, void* quant_stop);
+
+/* Read-bandwidth probe (for benchmarks; not part of the compressed path): one launch of a
+ * streaming kernel that reads the `bytes` bytes at device address src with 16-byte loads
+ * (grid workgroups of 256 lanes, 8 loads in flight per lane, each wave reading contiguous
+ * 1 KB runs) and folds them with xor.  sink: device uint32, written only if the fold equals
+ * 0xA5A5A5A5 (it keeps the loads alive; a zero-filled source never writes it).  src 16-byte
+ * aligned, bytes a positive multiple of 16, grid in 1..2^20.  Asynchronous on hip_stream.
+ * Errors: TQ_ERR_INVALID, TQ_ERR_DEVICE. */
+int tq_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid, void* hip_stream);
 
 /* Description of the last error on this thread ("" when none). */
 const char* tq_last_error(void);

@@ -22,7 +22,7 @@ __all__ = [
     "PRESETS", "Codebook", "DeviceParams", "KVCache", "TQError", "tq_build_codebook", "tq_cache_layout",
     "tq_decode_step", "tq_bf16_attend_decode", "bf16_value_chunks", "bf16_attend_workspace_bytes",
     "tq_quantize_kv", "tq_attend_decode", "tq_abi_version", "tq_profile_events", "upload_params",
-    "attend_workspace_bytes",
+    "attend_workspace_bytes", "tq_read_probe",
 ]
 
 
@@ -181,7 +181,7 @@ def tq_quantize_kv(codebook: Codebook, params: DeviceParams, cache: KVCache, k, 
 
 def attend_workspace_bytes(codebook: Codebook, params: DeviceParams, cache: KVCache, Hq: int,
                            max_seq_len: int) -> int:
-    """Bytes of attention workspace; allocate it zero-filled (torch.zeros) and reuse it."""
+    """Bytes of attention workspace (no initial contents needed; reusable across calls)."""
     n = ctypes.c_size_t(0)
     # a workspace query needs no device data; dummy non-NULL pointers satisfy the argument check
     check(lib.tq_attend_decode(ctypes.byref(codebook.cb), ctypes.byref(params.struct), ctypes.byref(cache.struct),
@@ -205,8 +205,7 @@ def tq_attend_decode(codebook: Codebook, params: DeviceParams, cache: KVCache, q
         out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     need = attend_workspace_bytes(codebook, params, cache, Hq, max_seq_len)
     if workspace is None or workspace.numel() < need:
-        # zero-filled once: the kernel keeps its arrival counters there and leaves them zero
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     n = ctypes.c_size_t(workspace.numel())
     check(lib.tq_attend_decode(ctypes.byref(codebook.cb), ctypes.byref(params.struct), ctypes.byref(cache.struct),
                                q.data_ptr(), _dtype_code(q), Hq, seq_len.data_ptr(), max_seq_len, float(scale),
@@ -238,7 +237,7 @@ def tq_decode_step(codebook: Codebook, params: DeviceParams, cache: KVCache, k, 
         out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
     need = attend_workspace_bytes(codebook, params, cache, Hq, max_seq_len)
     if workspace is None or workspace.numel() < need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     n = ctypes.c_size_t(workspace.numel())
     sb, sh, _, _ = ref.stride()
     check(lib.tq_decode_step(ctypes.byref(codebook.cb), ctypes.byref(params.struct), ctypes.byref(cache.struct),
@@ -288,3 +287,15 @@ def tq_bf16_attend_decode(k, vt, q, seq_len, max_seq_len: int, scale: float = 0.
                                     _stream(q.device)), "tq_bf16_attend_decode")
     return out
 
+
+
+def tq_read_probe(buf, grid: int, sink=None):
+    """Read-bandwidth probe: one launch reading all of `buf` (a contiguous device tensor whose
+    byte size is a multiple of 16) with 16-byte loads on `grid` workgroups of 256 lanes."""
+    import torch
+
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    check(lib.tq_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), int(grid),
+                            _stream(buf.device)), "tq_read_probe")
+    return sink

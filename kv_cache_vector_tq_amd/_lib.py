@@ -103,6 +103,8 @@ def _load():
     lib.tq_bf16_attend_decode.restype = ctypes.c_int
     lib.tq_bf16_attend_decode.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int, vp,
                                           ctypes.c_int, ctypes.c_float, vp, vp, P(ctypes.c_size_t), vp]
+    lib.tq_read_probe.restype = ctypes.c_int
+    lib.tq_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
     lib.tq_profile_events.restype = ctypes.c_int
     lib.tq_profile_events.argtypes = [vp, vp, vp, vp]
     return lib

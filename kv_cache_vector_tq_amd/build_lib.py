@@ -1,7 +1,10 @@
 """Builds libtq.so (HIP kernels for gfx950 plus the host C++ of the C ABI) in this directory.
 
-Usage: python kv_cache_vector_tq_amd/build_lib.py  (run by path: importing the package needs the built library).
-Each source is compiled on its own (in parallel) and then linked with hipcc.
+Usage: python kv_cache_vector_tq_amd/build_lib.py [--incremental] [-v]
+(run by path: importing the package needs the built library).
+Each source is compiled on its own (in parallel) and then linked with hipcc.  --incremental
+recompiles only sources whose object is older than the source or than any header of csrc/ and
+include/; the default recompiles everything.
 """
 from __future__ import annotations
 
@@ -16,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
 # the attention kernels are instantiated per key code width in translation units of their own
 SOURCES = (["tq_host.cpp", "tq_quantize.hip", "tq_attend.hip"] + [f"tq_attend_k{kb}.hip" for kb in range(5)] +
-           ["tq_bf16_attend.hip"])
+           ["tq_bf16_attend.hip", "tq_probe.hip"])
 ARCH = "gfx950"
 
 
@@ -36,13 +39,26 @@ def _flags():
     ]
 
 
-def build(verbose: bool = False) -> str:
+def _newest_header() -> float:
+    t = 0.0
+    for d in (CSRC, os.path.join(HERE, "..", "include")):
+        for f in os.listdir(d):
+            if f.endswith(".h"):
+                t = max(t, os.path.getmtime(os.path.join(d, f)))
+    return t
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
     hipcc = _hipcc()
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
+    headers = _newest_header()
 
     def compile_one(src):
         obj = os.path.join(objdir, src.rsplit(".", 1)[0] + ".o")
+        if incremental and os.path.exists(obj) and os.path.getmtime(obj) > max(
+                headers, os.path.getmtime(os.path.join(CSRC, src))):
+            return obj
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [hipcc] + _flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -65,5 +81,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    path = build(verbose="-v" in sys.argv)
+    path = build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv)
     print(path)

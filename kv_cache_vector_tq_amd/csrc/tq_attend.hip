@@ -193,7 +193,7 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
   static const int MGROUP_ASKED = env_int("TQ_ATTN_MGROUP", 16, 1, MGROUP);
   const int mgroup = std::max(MGROUP_ASKED, (n_slices + MAX_GROUPS - 1) / MAX_GROUPS);
   const int n_mgroups = (n_slices + mgroup - 1) / mgroup;
-  const size_t cnt_bytes = align256(static_cast<size_t>(B) * cache->Hkv * (MAX_GROUPS + 1) * sizeof(unsigned));
+  const size_t cnt_bytes = align256(static_cast<size_t>(B) * cache->Hkv * CNT_PER_UNIT * sizeof(unsigned));
   const size_t part_bytes = align256(static_cast<size_t>(B) * Hq * n_slices * PREC * sizeof(float));
   const size_t gpart_bytes =
       n_mgroups > 1 ? align256(static_cast<size_t>(B) * Hq * n_mgroups * PREC * sizeof(float)) : 0;
@@ -212,8 +212,7 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
   hipStream_t s = reinterpret_cast<hipStream_t>(hip_stream);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace) + qrec_bytes;  // after the query records
   float* qrec = reinterpret_cast<float*>(workspace);
-  unsigned* cnt_grp = reinterpret_cast<unsigned*>(ws);
-  unsigned* cnt_top = cnt_grp + static_cast<size_t>(B) * cache->Hkv * MAX_GROUPS;
+  unsigned* cnt = reinterpret_cast<unsigned*>(ws);  // CNT_PER_UNIT per unit, zeroed by the rotation launch
   float* part = reinterpret_cast<float*>(ws + cnt_bytes);
   float* gpart = n_mgroups > 1 ? reinterpret_cast<float*>(ws + cnt_bytes + part_bytes)
                                : nullptr;
@@ -224,12 +223,13 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
   if (step != nullptr) {
     // the step's new tokens and the query rotation in one launch (it validates the append on
     // the host and launches nothing when that fails)
-    const QueryRotationArgs rot{q, q_dtype == TQ_DTYPE_F32 ? 1 : 0, G, units, qrec, p->r_hi, p->r_lo, m_hi, m_lo};
+    const QueryRotationArgs rot{q,    q_dtype == TQ_DTYPE_F32 ? 1 : 0, G, units, qrec, p->r_hi, p->r_lo, m_hi, m_lo,
+                                cnt, CNT_PER_UNIT};
     rc = quantize_launch(cb, p, step->k, step->v, step->dtype, B, cache->Hkv, 1, step->stride_b, step->stride_h, D,
                          step->start_pos, cache, hip_stream, &rot);
     if (rc != TQ_OK) return rc;
   } else {
-    PrologueArgs pa{q, p->r_hi, p->r_lo, m_hi, m_lo, qrec, G, q_dtype == TQ_DTYPE_F32 ? 1 : 0};
+    PrologueArgs pa{q, p->r_hi, p->r_lo, m_hi, m_lo, qrec, G, q_dtype == TQ_DTYPE_F32 ? 1 : 0, cnt, CNT_PER_UNIT};
     if (cb->cfg.k_qjl)
       hipLaunchKernelGGL(prologue_kernel<true>, dim3(units, 4), dim3(64), 0, s, pa);
     else
@@ -251,8 +251,7 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
   ma.rt_lo = p->rt_lo;
   ma.part = part;
   ma.gpart = gpart;
-  ma.cnt_grp = cnt_grp;
-  ma.cnt_top = cnt_top;
+  ma.cnt = cnt;
   ma.out = out;
   ma.scores_out = scores_out;
   ma.Hkv = cache->Hkv;
@@ -305,3 +304,4 @@ extern "C" int tq_decode_step(const tq_codebook* cb, const tq_dev_params* p, con
   return tq::attend(cb, p, cache, q, q_dtype, Hq, seq_len, max_seq_len, scale, out, scores_out, workspace,
                     workspace_bytes, hip_stream, &step);
 }
+

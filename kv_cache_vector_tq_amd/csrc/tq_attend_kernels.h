@@ -31,8 +31,8 @@ struct MainArgs {
   const uint16_t* rt_lo;
   float* part;        // [B*Hq][n_slices][PREC]: rotated sums, m, l of each slice
   float* gpart;       // [B*Hq][n_groups][PREC]: the same per group of mgroup slices
-  unsigned* cnt_grp;  // [B*Hkv][MAX_GROUPS] arrival counters (zero between calls)
-  unsigned* cnt_top;  // [B*Hkv]
+  unsigned* cnt;      // [B*Hkv][MAX_GROUPS + 1] arrival counters: one per merge group, then the
+                      // top-level one; zeroed by the query rotation launched before this kernel
   float* out;         // [B*Hq][128]
   float* scores_out;  // NULL or [B*Hq][T_cap]
   int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices, mgroup;
@@ -70,6 +70,7 @@ constexpr int NT = 64 * NW;                      // threads per attention workgr
 constexpr int MGROUP = 32;                       // slices per first-level merge group
 constexpr int MAX_GROUPS = 32;                   // merge groups per (batch row, kv-head)
 constexpr int MAX_SLICES = MGROUP * MAX_GROUPS;  // context slices per (batch row, kv-head)
+constexpr int CNT_PER_UNIT = MAX_GROUPS + 1;     // arrival counters per (batch row, kv-head)
 
 // ---- code decoding ------------------------------------------------------------------------
 // An 8-code window of a lane's chunk becomes one f16x8 MFMA operand (element e = code at bits
@@ -647,15 +648,13 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   const int grp = blockIdx.x / mgroup;
   drain_stores();
   __syncthreads();
+  unsigned* const cnt_top = a.cnt + bh * CNT_PER_UNIT + MAX_GROUPS;
   if (tid == 0) {
-    // the last arrival resets its counter, so counters are zero again after every call
+    // counters start at zero (the query rotation launch zeroes them before every call)
     int stage = 0;
-    unsigned* cnt = ngrp == 1 ? a.cnt_top + bh : a.cnt_grp + bh * MAX_GROUPS + grp;
+    unsigned* cnt = ngrp == 1 ? cnt_top : a.cnt + bh * CNT_PER_UNIT + grp;
     const unsigned last = ngrp == 1 ? ns - 1 : min(mgroup, ns - mgroup * grp) - 1;
-    if (atomicAdd(cnt, 1u) == last) {
-      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      stage = ngrp == 1 ? 2 : 1;
-    }
+    if (atomicAdd(cnt, 1u) == last) stage = ngrp == 1 ? 2 : 1;
     ep->stage = stage;
   }
   __syncthreads();
@@ -723,10 +722,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   __syncthreads();
   if (tid == 0) {
     ep->stage = 0;
-    if (atomicAdd(a.cnt_top + bh, 1u) == static_cast<unsigned>(ngrp - 1)) {
-      __hip_atomic_store(a.cnt_top + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ep->stage = 2;
-    }
+    if (atomicAdd(cnt_top, 1u) == static_cast<unsigned>(ngrp - 1)) ep->stage = 2;
   }
   __syncthreads();
   if (ep->stage != 2) return;

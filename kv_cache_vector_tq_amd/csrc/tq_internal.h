@@ -35,6 +35,8 @@ struct QueryRotationArgs {
   const uint16_t* r_lo;
   const uint16_t* m_hi;  // NULL without the sketch
   const uint16_t* m_lo;
+  unsigned* cnt;  // arrival counters to zero, cnt_per_unit per unit
+  int cnt_per_unit;
 };
 
 // tq_quantize_kv with the query rotation of a decode step in the same launch (rot may be

@@ -111,6 +111,11 @@ struct PrologueArgs {
   const uint16_t* m_lo;
   float* qrec;  // [B*Hq][QREC]
   int G, q_f32;
+  // arrival counters of the attention kernel that follows: cnt_per_unit per (batch row,
+  // kv-head) unit, set to zero here (wave 0 of each unit's rotation) before every attention
+  // launch, so a workspace needs no initial contents
+  unsigned* cnt;
+  int cnt_per_unit;
 };
 
 template <bool QJL>
@@ -118,6 +123,7 @@ __device__ __forceinline__ void rotate_query_tile(const PrologueArgs& a, int uni
   const int col = lane & 15, g = lane >> 4;
   const int G = a.G;
   const int64_t head0 = static_cast<int64_t>(unit) * G;
+  if (tile == 0 && lane < a.cnt_per_unit) a.cnt[static_cast<int64_t>(unit) * a.cnt_per_unit + lane] = 0u;
   QOperands<QJL> qo;
   load_query_operands<QJL>(qo, a.q, a.q_f32 != 0, head0, G, a.r_hi, a.r_lo, a.m_hi, a.m_lo, tile, col, g);
   f32x4 d1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};

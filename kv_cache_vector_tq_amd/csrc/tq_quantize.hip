@@ -294,7 +294,8 @@ int quantize_launch(const tq_codebook* cb, const tq_dev_params* p, const void* k
   PrologueArgs pa{};
   QuantGrid qg{grid, nullptr, 0};
   if (rot != nullptr) {
-    pa = PrologueArgs{rot->q, rot->r_hi, rot->r_lo, rot->m_hi, rot->m_lo, rot->qrec, rot->G, rot->q_f32};
+    pa = PrologueArgs{rot->q,    rot->r_hi, rot->r_lo, rot->m_hi, rot->m_lo, rot->qrec,
+                      rot->G,    rot->q_f32, rot->cnt,  rot->cnt_per_unit};
     qg.pa = &pa;
     qg.rot_wgs = rot->units;
   }

@@ -51,28 +51,6 @@ def key_scores(q, R_eff, k, k_centroids=None, S_b=None):
     return acc * np.asarray(k["n"], dtype=np.float64)[None, :]
 
 
-def score_magnitudes(q, R_eff, k, k_centroids=None, S_b=None):
-    """Sum of the magnitudes of the terms of each unscaled score [H, T]:
-    n_i (sum_j |q1_j c[idx_ij]| / sqrt(d) + gamma_i kappa sum_j |q2_j|).
-    A score can be far smaller than this when its terms cancel; rounding errors of any
-    finite-precision evaluation scale with this sum, not with the score itself."""
-    q = np.asarray(q, dtype=np.float64)
-    d = R_eff.shape[0]
-    q1 = q @ R_eff.T
-    T = len(k["n"])
-    acc = np.zeros((q.shape[0], T))
-    if k_centroids is not None:
-        c = np.asarray(k_centroids, dtype=np.float32).astype(np.float64)
-        C = np.abs(c[k["idx"].astype(np.int64)]) / math.sqrt(d)
-        acc += np.abs(q1) @ C.T
-    if S_b is not None:
-        q2 = q1 @ S_b.T
-        gamma = k.get("gamma")
-        gamma = np.ones(T) if gamma is None else np.asarray(gamma, dtype=np.float64)
-        acc += np.abs(q2).sum(axis=1, keepdims=True) * (gamma * kappa(S_b.shape[0]))[None, :]
-    return acc * np.abs(np.asarray(k["n"], dtype=np.float64))[None, :]
-
-
 def attend(q, R_eff, k, v, k_centroids, v_centroids, S_b, scale=None, T=None):
     """Decode attention of queries q [H, d] (all of one kv-head) over the first T keys.
 

@@ -3,34 +3,55 @@ packed cache back, and compare it with the oracle under the band rules.
 
 Comparison rules (tolerances of the path):
   * codes: bit-exact, except elements whose rotated value z lies within 1e-5 * max(1, |t|)
-    of a threshold t; every mismatch must be such an element and the mismatch fraction
-    must stay below 1e-4 (in-band and mismatch fractions are both reported);
+    of a threshold t.  A mismatching element must be such an element, the two codes must be
+    neighbours (|got - ref| = 1), and z must lie in the band of the one threshold that
+    separates them (t[min(got, ref)]); the mismatch fraction must stay below 1e-4 (in-band
+    and mismatch fractions are both reported);
   * sign bits: the oracle takes the GPU's code for in-band elements, recomputes the
     residual and its sketch, and must then agree bit for bit except where |u_j| lies
     within 1e-5 * ||r|| of the decision point 0;
   * stored norms: relative 1e-6 (vector norms) and 1e-5 (residual norms);
-  * scores: |d score_i| <= 2e-3 max(max_k |score_k|, A_i) per (batch row, q-head), where
-    A_i is the sum of the magnitudes of the terms of score i (oracle.attention.
-    score_magnitudes); A_i only matters when a row's scores all nearly cancel, e.g. a
-    single key;
+  * scores: per (batch row, q-head), max_i |d score_i| <= 2e-3 max_k |score_k| (the row's
+    largest logit).  Only rows of fewer than 64 keys, whose few scores can all nearly
+    cancel, fall back to 2e-3 max(max_k |score_k|, A_i) with A_i the sum of the magnitudes
+    of the terms of score i (score_magnitudes below);
   * outputs: max |d out| <= 2e-3 max |out| per (batch row, q-head);
     both computed by the oracle on the GPU-written cache.
+
+Every comparison adds its figures to RECORDS; tests/conftest.py prints them at the end of
+the run (in-band and mismatch fractions, largest score error against the row maximum,
+largest output error).
 """
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 
 import tq_workloads as wl
 from oracle import layout
 from oracle.pipeline import Oracle
-from oracle.attention import score_magnitudes
-from oracle.quantize import sign_band, threshold_band
+from oracle.quantize import kappa, sign_band, threshold_band
 
 BAND = 1e-5
 MAX_MISMATCH = 1e-4
 SCORE_TOL = 2e-3
+# rows with at least this many keys are held to the strict per-row score bound
+STRICT_MIN_KEYS = 64
+
+# test id -> {figure: worst value}; printed by tests/conftest.py at the end of the session
+RECORDS: dict = {}
+
+
+def _test_id() -> str:
+    cur = os.environ.get("PYTEST_CURRENT_TEST", "interactive")
+    return cur.rsplit(" ", 1)[0]
+
+
+def record(figure: str, value: float, worst=max):
+    r = RECORDS.setdefault(_test_id(), {})
+    r[figure] = value if figure not in r else worst(r[figure], value)
 
 
 def torch_mod():
@@ -68,16 +89,33 @@ def unpack_values(orc: Oracle, hc: dict, b: int, h: int, T: int) -> dict:
             "idx": layout.unpack(hc["v_codes"][b, h], T, 128, orc.v_bits, "v")}
 
 
+def code_mismatches(got_idx, ref_idx, z, thresholds, rel=BAND):
+    """Checks the code rule and returns (mismatch mask, in-band mask).
+
+    Every mismatching element must have codes that are neighbours, and z must lie within
+    rel * max(1, |t|) of the threshold t = thresholds[min(got, ref)] that separates them
+    (code c covers [t[c-1], t[c]), so t[c] is the boundary between codes c and c + 1)."""
+    got = np.asarray(got_idx).astype(np.int64)
+    ref = np.asarray(ref_idx).astype(np.int64)
+    band = threshold_band(z, thresholds, rel)
+    mism = got != ref
+    if np.any(mism):
+        g, r, zz = got[mism], ref[mism], np.asarray(z, dtype=np.float64)[mism]
+        assert np.all(np.abs(g - r) == 1), "a code mismatch is not between neighbouring codes"
+        t = np.asarray(thresholds, dtype=np.float32).astype(np.float64)[np.minimum(g, r)]
+        assert np.all(np.abs(zz - t) <= rel * np.maximum(1.0, np.abs(t))), \
+            "a code mismatch lies outside the band of the threshold between the two codes"
+    return mism, band
+
+
 def compare_keys(orc: Oracle, x: np.ndarray, got: dict, stats: dict):
     """x: the exact input rows [T, d]; got: unpacked GPU keys for the same rows."""
     ref = orc.quantize_keys(x)
     assert np.allclose(got["n"], ref["n"], rtol=1e-6, atol=0), "key norms"
     force = None
     if orc.k_bits:
-        band = threshold_band(ref["z"], orc.kt, BAND)
-        mism = got["idx"] != ref["idx"]
+        mism, band = code_mismatches(got["idx"], ref["idx"], ref["z"], orc.kt)
         _acc(stats, "k_code", mism, band)
-        assert not np.any(mism & ~band), "key code mismatch outside the threshold band"
         force = (got["idx"], band)
     if orc.k_qjl:
         cond = orc.quantize_keys(x, *force) if force is not None else ref
@@ -93,10 +131,8 @@ def compare_keys(orc: Oracle, x: np.ndarray, got: dict, stats: dict):
 def compare_values(orc: Oracle, x: np.ndarray, got: dict, stats: dict):
     ref = orc.quantize_values(x)
     assert np.allclose(got["n"], ref["n"], rtol=1e-6, atol=0), "value norms"
-    band = threshold_band(ref["z"], orc.vt, BAND)
-    mism = got["idx"] != ref["idx"]
+    mism, band = code_mismatches(got["idx"], ref["idx"], ref["z"], orc.vt)
     _acc(stats, "v_code", mism, band)
-    assert not np.any(mism & ~band), "value code mismatch outside the threshold band"
     return ref
 
 
@@ -111,8 +147,48 @@ def finish_stats(stats: dict):
     for key, s in stats.items():
         s["mismatch_frac"] = s["mismatch"] / max(1, s["n"])
         s["in_band_frac"] = s["in_band"] / max(1, s["n"])
+        record(f"{key}_in_band_frac", s["in_band_frac"])
+        record(f"{key}_mismatch_frac", s["mismatch_frac"])
         assert s["mismatch_frac"] < MAX_MISMATCH, (key, s)
     return stats
+
+
+def score_magnitudes(q, R_eff, k, k_centroids=None, S_b=None):
+    """Sum of the magnitudes of the terms of each unscaled score [H, T]:
+    n_i (sum_j |q1_j c[idx_ij]| / sqrt(d) + gamma_i kappa sum_j |q2_j|), q1 = R_eff q,
+    q2 = S_b q1.  Any finite-precision evaluation of score i errs in proportion to this sum,
+    which can be far larger than the score itself when its terms cancel.  Used only for rows
+    of fewer than STRICT_MIN_KEYS keys (pinned in tests/test_parity_rules.py)."""
+    q = np.asarray(q, dtype=np.float64)
+    d = R_eff.shape[0]
+    q1 = q @ R_eff.T
+    T = len(k["n"])
+    acc = np.zeros((q.shape[0], T))
+    if k_centroids is not None:
+        c = np.asarray(k_centroids, dtype=np.float32).astype(np.float64)
+        C = np.abs(c[k["idx"].astype(np.int64)]) / math.sqrt(d)
+        acc += np.abs(q1) @ C.T
+    if S_b is not None:
+        q2 = q1 @ S_b.T
+        gamma = k.get("gamma")
+        gamma = np.ones(T) if gamma is None else np.asarray(gamma, dtype=np.float64)
+        acc += np.abs(q2).sum(axis=1, keepdims=True) * (gamma * kappa(S_b.shape[0]))[None, :]
+    return acc * np.abs(np.asarray(k["n"], dtype=np.float64))[None, :]
+
+
+def check_scores(got, logits, T, mags=None):
+    """The score rule on one group of rows: got, logits [H, >= T].  mags (the unscaled-score
+    magnitudes times the logit scale) is needed only when T < STRICT_MIN_KEYS.  Returns the
+    largest error against each row's largest |logit|."""
+    diff = np.abs(np.asarray(got, dtype=np.float64)[:, :T] - logits[:, :T])
+    rowmax = np.abs(logits[:, :T]).max(axis=1)
+    vs_rowmax = float((diff.max(axis=1) / np.maximum(rowmax, 1e-300)).max())
+    if T >= STRICT_MIN_KEYS:
+        assert vs_rowmax <= SCORE_TOL, ("scores against the row maximum", vs_rowmax)
+    else:
+        ref = np.maximum(rowmax[:, None], mags[:, :T])
+        assert np.all(diff <= SCORE_TOL * ref), ("scores (short row)", (diff / ref).max())
+    return vs_rowmax
 
 
 def compare_attention(orc: Oracle, q: np.ndarray, k: dict, v: dict, T: int, got_out: np.ndarray,
@@ -121,18 +197,17 @@ def compare_attention(orc: Oracle, q: np.ndarray, k: dict, v: dict, T: int, got_
     logits, out = orc.attend(q.astype(np.float64), k, v, T=T, scale=scale)
     err = {}
     if got_scores is not None:
-        sc = (1.0 / math.sqrt(128)) if scale is None else scale
-        kk = {key: np.asarray(val)[:T] for key, val in k.items()}
-        mag = sc * score_magnitudes(q.astype(np.float64), orc.R_eff, kk, orc.kc, orc.S_b)
-        ref = np.maximum(np.abs(logits).max(axis=1, keepdims=True), mag)
-        rel = np.abs(got_scores[:, :T] - logits) / ref
-        err["score"] = float(rel.max())
-        err["score_vs_rowmax"] = float((np.abs(got_scores[:, :T] - logits).max(axis=1)
-                                        / np.abs(logits).max(axis=1)).max())
-        assert np.all(rel <= SCORE_TOL), ("scores", rel.max(axis=1))
+        mags = None
+        if T < STRICT_MIN_KEYS:
+            sc = (1.0 / math.sqrt(128)) if scale is None else scale
+            kk = {key: np.asarray(val)[:T] for key, val in k.items()}
+            mags = sc * score_magnitudes(q.astype(np.float64), orc.R_eff, kk, orc.kc, orc.S_b)
+        err["score_vs_rowmax"] = check_scores(got_scores, logits, T, mags)
+        record("score_err_vs_rowmax", err["score_vs_rowmax"])
     d = np.abs(got_out - out).max(axis=1)
     ref = np.abs(out).max(axis=1)
     err["out"] = float((d / np.maximum(ref, 1e-300)).max())
+    record("out_err_vs_max", err["out"])
     assert np.all(d <= SCORE_TOL * ref), ("outputs", d / ref)
     return err
 
