@@ -236,6 +236,21 @@ int tq_decode_step(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_ca
                    int Hq, const int32_t* seq_len, int max_seq_len, float scale, float* out,
                    float* scores_out, void* workspace, size_t* workspace_bytes, void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): tq_attend_decode with its workspace taken from a
+ * fixed array of TQ_NOALLOC_SCRATCH_BYTES bytes of device memory that the library holds, one per
+ * GPU it runs on, until the process ends.  Arguments, outputs and errors as tq_attend_decode
+ * without workspace / workspace_bytes; it calls no allocating routine.  A call whose workspace
+ * would exceed TQ_NOALLOC_SCRATCH_BYTES fails with TQ_ERR_WORKSPACE before any launch (the
+ * workspace grows with B * Hq and with the context split; B * Hq up to about 8192 fits).  Every
+ * call on one GPU shares that GPU's array and leaves its contents there; each call first sets
+ * what must start at zero (the arrival counters).  Calls that overlap on one GPU (different
+ * streams, or threads without ordering) race on the array and give undefined results. */
+#define TQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int tq_attend_decode_noalloc(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache,
+                             const void* q, tq_dtype q_dtype, int Hq, const int32_t* seq_len, int max_seq_len,
+                             float scale, float* out, float* scores_out, void* hip_stream);
+
 /* Baseline for comparison: uncompressed bf16 decode attention at the same shapes (not part of
  * the compressed path).  p = softmax(scale * K q) (scale 0 selects 1/sqrt(128)),
  * out = sum_i p_i V_i, fp32 accumulation, for all (batch row, q-head); q-head h reads kv-head

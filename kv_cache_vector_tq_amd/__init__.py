@@ -22,7 +22,7 @@ __all__ = [
     "PRESETS", "Codebook", "DeviceParams", "KVCache", "TQError", "tq_build_codebook", "tq_cache_layout",
     "tq_decode_step", "tq_bf16_attend_decode", "bf16_value_chunks", "bf16_attend_workspace_bytes",
     "tq_quantize_kv", "tq_attend_decode", "tq_abi_version", "tq_profile_events", "upload_params",
-    "attend_workspace_bytes", "tq_read_probe",
+    "attend_workspace_bytes", "tq_read_probe", "tq_attend_decode_noalloc",
 ]
 
 
@@ -211,6 +211,27 @@ def tq_attend_decode(codebook: Codebook, params: DeviceParams, cache: KVCache, q
                                q.data_ptr(), _dtype_code(q), Hq, seq_len.data_ptr(), max_seq_len, float(scale),
                                out.data_ptr(), scores_out.data_ptr() if scores_out is not None else None,
                                workspace.data_ptr(), ctypes.byref(n), _stream(q.device)), "tq_attend_decode")
+    return out
+
+
+def tq_attend_decode_noalloc(codebook: Codebook, params: DeviceParams, cache: KVCache, q, seq_len,
+                             max_seq_len: int, scale: float = 0.0, out=None, scores_out=None):
+    """tq_attend_decode with the library's fixed device scratch as workspace (no allocation
+    inside the call; `out` must then be given by callers that cannot allocate)."""
+    import torch
+
+    if q.dim() != 3 or q.shape[-1] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, 128] tensor")
+    B, Hq, _ = q.shape
+    if B != cache.B:
+        raise ValueError("q batch does not match the cache")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    check(lib.tq_attend_decode_noalloc(ctypes.byref(codebook.cb), ctypes.byref(params.struct),
+                                       ctypes.byref(cache.struct), q.data_ptr(), _dtype_code(q), Hq,
+                                       seq_len.data_ptr(), max_seq_len, float(scale), out.data_ptr(),
+                                       scores_out.data_ptr() if scores_out is not None else None,
+                                       _stream(q.device)), "tq_attend_decode_noalloc")
     return out
 
 

@@ -305,3 +305,62 @@ extern "C" int tq_decode_step(const tq_codebook* cb, const tq_dev_params* p, con
                     workspace_bytes, hip_stream, &step);
 }
 
+// ---- attention for callers that cannot allocate -----------------------------------------------
+// The workspace of tq_attend_decode_noalloc is a fixed array in device memory, one per GPU the
+// library runs on, held until the process ends.  Host code never uses the array's name as an
+// address (on the host it names a stand-in, not device memory): each device's address is looked
+// up once, with that device current, and kept.
+namespace tq {
+namespace {
+
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(TQ_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device (looked up on the first call per device);
+// NULL with the error set when the lookup fails.
+void* scratch_address() {
+  static std::mutex mu;
+  static std::vector<void*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(TQ_ERR_DEVICE, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= static_cast<int>(addr.size())) addr.resize(dev + 1, nullptr);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      fail(TQ_ERR_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+      return nullptr;
+    }
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+}  // namespace tq
+
+extern "C" int tq_attend_decode_noalloc(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache,
+                                        const void* q, tq_dtype q_dtype, int Hq, const int32_t* seq_len,
+                                        int max_seq_len, float scale, float* out, float* scores_out,
+                                        void* hip_stream) {
+  tq::clear_error();
+  size_t need = 0;
+  // the size query validates every argument on the host and launches nothing
+  int rc = tq::attend(cb, p, cache, q, q_dtype, Hq, seq_len, max_seq_len, scale, out, scores_out, nullptr, &need,
+                      hip_stream, nullptr);
+  if (rc != TQ_OK) return rc;
+  if (need > tq::NOALLOC_SCRATCH_BYTES)
+    return tq::fail(TQ_ERR_WORKSPACE, "the call needs " + std::to_string(need) +
+                                          " bytes of workspace, more than the fixed scratch of " +
+                                          std::to_string(tq::NOALLOC_SCRATCH_BYTES) + " bytes");
+  void* ws = tq::scratch_address();
+  if (ws == nullptr) return TQ_ERR_DEVICE;
+  size_t have = tq::NOALLOC_SCRATCH_BYTES;
+  return tq::attend(cb, p, cache, q, q_dtype, Hq, seq_len, max_seq_len, scale, out, scores_out, ws, &have,
+                    hip_stream, nullptr);
+}
