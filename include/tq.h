@@ -83,7 +83,8 @@ typedef struct tq_codebook {
 } tq_codebook;
 
 /* Parameter matrices, row-major d x d, bf16 bit patterns, all derived from cfg->seed:
- *   r_hi, r_lo    the rotation R_eff = r_hi + r_lo (y = R_eff x);
+ *   r_hi, r_lo    the rotation: R_eff = r_hi + r_lo (Haar mode) or r_hi / sqrt(128) with
+ *                 r_lo = 0 (Hadamard mode); y = R_eff x;
  *   s_qjl         the sketch S_b (u = S_b r);
  *   rt_hi, rt_lo  r_hi and r_lo transposed (the unrotation R_eff^T of attention outputs);
  *   m_hi, m_lo    M = S_b R_eff (exact product, then m_hi = bf16(M), m_lo = bf16(M - m_hi)):
@@ -161,7 +162,11 @@ typedef struct tq_cache_sizes {
  *     словами", section on TurboQuant in llama.cpp): R = H diag(s) / sqrt(128) with
  *     H_ij = (-1)^popcount(i & j) and s_j = -1 when the top bit of the j-th output of the
  *     stream started at 2*seed is set, else +1;
- *   R_hi = bf16(R), R_lo = bf16(R - R_hi), bf16() = round to fp32 then to bf16, ties to even;
+ *   Haar mode: R_hi = bf16(R), R_lo = bf16(R - R_hi), bf16() = round to fp32 then to bf16, ties
+ *     to even, and the applied rotation is R_eff = R_hi + R_lo;
+ *   Hadamard mode: R_hi = H diag(s) (entries +-1, exact in bf16), R_lo = 0, and the applied
+ *     rotation is R_eff = R = R_hi / sqrt(128) exactly: the kernels apply one bf16 product pass
+ *     instead of two and fold 1/sqrt(128) into their fp32 scales;
  *   S_b = bf16(S), S = 128x128 N(0,1) from the stream started at 2*seed + 1.
  * Errors: TQ_ERR_INVALID (NULL cfg/cb), TQ_ERR_UNSUPPORTED (d != 128, k_bits outside 0..4,
  * v_bits outside 1..4, k_qjl not 0/1, k_bits == 0 with k_qjl == 0, or an unknown rotation). */

@@ -218,6 +218,8 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
                                : nullptr;
   if (scale == 0.f) scale = INV_SQRT_D;
 
+  // Hadamard mode: r_hi = H diag(s) = sqrt(d) R, one product pass; 1/sqrt(d) joins the scales
+  const int one_pass = cb->cfg.rotation == TQ_ROTATION_HADAMARD ? 1 : 0;
   const uint16_t* m_hi = cb->cfg.k_qjl ? p->m_hi : nullptr;
   const uint16_t* m_lo = cb->cfg.k_qjl ? p->m_lo : nullptr;
   if (step != nullptr) {
@@ -229,7 +231,8 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
                          step->start_pos, cache, hip_stream, &rot);
     if (rc != TQ_OK) return rc;
   } else {
-    PrologueArgs pa{q, p->r_hi, p->r_lo, m_hi, m_lo, qrec, G, q_dtype == TQ_DTYPE_F32 ? 1 : 0, cnt, CNT_PER_UNIT};
+    PrologueArgs pa{q,   p->r_hi,      p->r_lo, m_hi, m_lo, qrec, G, q_dtype == TQ_DTYPE_F32 ? 1 : 0,
+                    cnt, CNT_PER_UNIT, one_pass};
     if (cb->cfg.k_qjl)
       hipLaunchKernelGGL(prologue_kernel<true>, dim3(units, 4), dim3(64), 0, s, pa);
     else
@@ -262,6 +265,8 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
   ma.mgroup = mgroup;
   ma.scale = scale;
   ma.scale_log2 = scale * LOG2E;
+  ma.one_pass = one_pass;
+  ma.rot_scale = one_pass ? INV_SQRT_D : 1.0f;
   const float ks = table_scale(cb->k_centroids, cb->cfg.k_bits);
   // equal widths share the key table (built from the key centroids), so they share its factor
   const float vs = cb->cfg.k_bits == cb->cfg.v_bits ? ks : table_scale(cb->v_centroids, cb->cfg.v_bits);

@@ -42,6 +42,11 @@ struct MainArgs {
   float k_unscale;     // 1 / k_scale
   float v_cent[16];   // value centroids times v_scale
   float v_unscale;     // 1 / v_scale
+  // rotation: one_pass = 0: R_eff = rt_hi^T + rt_lo^T; one_pass = 1 (Hadamard): R_eff =
+  // rt_hi^T / sqrt(d) (rt_lo = 0), the query records hold sqrt(d) R_eff q, and rot_scale =
+  // 1/sqrt(d) scales the key-code term of the scores and the unrotated outputs
+  int one_pass;
+  float rot_scale;
 };
 
 // Launches the attention kernel for key code width KB (k_qjl selects the sign sketch), value
@@ -73,63 +78,61 @@ constexpr int MAX_SLICES = MGROUP * MAX_GROUPS;  // context slices per (batch ro
 constexpr int CNT_PER_UNIT = MAX_GROUPS + 1;     // arrival counters per (batch row, kv-head)
 
 // ---- code decoding ------------------------------------------------------------------------
-// An 8-code window of a lane's chunk becomes one f16x8 MFMA operand (element e = code at bits
-// B*e of the window) through wide LDS lookups (few LDS instructions per code):
+// Codes become f16 MFMA operands through lookup tables in LDS built at kernel start.  A table
+// Tab<B, K> maps a K-bit key (CPL = K / B consecutive B-bit codes, or K sign bits) to the CPL
+// f16 values, EBYTES = 2 CPL bytes per entry, one entry after the other:
 //   B = 1 and sign bits: an 8-bit key -> 8 values (16-byte entries, 256 entries);
 //   B = 2: an 8-bit key -> 4 codes (8-byte entries, 256 entries);
 //   B = 3: a 12-bit key -> 4 codes (8-byte entries, 4096 entries);
 //   B = 4: an 8-bit key -> 2 codes (4-byte entries, 256 entries).
-// Tables depend only on the bit width (codebooks do), so keys and values of the same width
-// share one table.
+// Keys and values of the same width share one table.  (Tables with one copy of each entry per
+// lane slot, which make a wave's random lookups free of LDS bank conflicts, were measured
+// without gain on the batch-16 128K-context and 1M-context workloads: the loop is bound by its
+// dependent chain, not by LDS bandwidth.)
 template <int B>
-struct Dec {
-  static constexpr int KEYBITS = (B == 3) ? 12 : 8;
-  static constexpr int CPL = (B == 1) ? 8 : (B == 4) ? 2 : 4;  // codes per lookup
-  static constexpr int EBYTES = 2 * CPL;
-  static constexpr int LDS_BYTES = (1 << KEYBITS) * EBYTES;
+struct Tab {
+  static constexpr int K = (B == 3) ? 12 : 8;            // key bits
+  static constexpr int CPL = K / B;                       // codes per lookup
+  static constexpr int EBYTES = 2 * CPL;                  // bytes per entry
+  static constexpr int SHIFT = EBYTES == 16 ? 4 : (EBYTES == 8 ? 3 : 2);
+  static constexpr int BYTES = (1 << K) * EBYTES;
 };
-constexpr int SIGN_TABLE_BYTES = 256 * 16;
 
 __device__ __forceinline__ uint32_t pack_f16x2(_Float16 a, _Float16 b) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
-template <int B>
-__device__ void build_code_table(uint8_t* tab, const float* cent, int tid) {
-  using T = Dec<B>;
-  typedef _Float16 entry_t __attribute__((ext_vector_type(T::CPL)));
-  _Float16 c16[1 << B];
+// Fills table Tab<B> at tab: entry e holds the f16 values of its CPL codes (code i = bits
+// B i .. B i + B - 1 of e), or for SIGN the values -1 / +1 of its 8 bits.  All NT threads of
+// the workgroup write 16-byte chunks.
+template <int B, bool SIGN>
+__device__ void build_table(uint8_t* tab, const float* cent, int tid) {
+  using T = Tab<B>;
+  constexpr int L = 1 << B;
+  _Float16 c16[L];
 #pragma unroll
-  for (int l = 0; l < (1 << B); ++l) c16[l] = static_cast<_Float16>(cent[l]);
-  if constexpr (B == 3) {
-    // entry e = tid + 256 k (k < 16) holds codes e & 7, (e >> 3) & 7, (e >> 6) & 7, e >> 9:
-    // the first two depend only on the lane (e & 63 = tid & 63), the third is
-    // c[w + 4 (k & 1)] for the wave w = tid >> 6, the fourth c[k >> 1]
-    const int lane = tid & 63, w = tid >> 6;
-    const uint32_t lo = pack_f16x2(c16[lane & 7], c16[(lane >> 3) & 7]);
-    const _Float16 x0 = c16[w], x1 = c16[w + 4];
+  for (int l = 0; l < L; ++l) c16[l] = SIGN ? static_cast<_Float16>(l ? 1.0f : -1.0f) : static_cast<_Float16>(cent[l]);
+  for (int c = tid; c < T::BYTES / 16; c += NT) {
+    uint16_t v[8];  // the 8 halves of chunk c
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-      *reinterpret_cast<u32x2*>(tab + (tid + 256 * k) * 8) = u32x2{lo, pack_f16x2((k & 1) ? x1 : x0, c16[k >> 1])};
-    return;
-  }
-  for (int e = tid; e < (1 << T::KEYBITS); e += 256) {
-    entry_t v;
+    for (int h = 0; h < 8; ++h) {
+      const int e = (8 * c + h) / T::CPL;  // entry
+      const int i = (8 * c + h) % T::CPL;  // code within the entry
+      const int code = (e >> (B * i)) & (L - 1);
+      _Float16 x = c16[0];
 #pragma unroll
-    for (int i = 0; i < T::CPL; ++i) v[i] = c16[(e >> (B * i)) & ((1 << B) - 1)];
-    *reinterpret_cast<entry_t*>(tab + e * T::EBYTES) = v;
+      for (int l = 1; l < L; ++l) x = code == l ? c16[l] : x;  // no dynamic register indexing
+      v[h] = __builtin_bit_cast(uint16_t, x);
+    }
+    u32x4 w;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) w[h] = static_cast<uint32_t>(v[2 * h]) | (static_cast<uint32_t>(v[2 * h + 1]) << 16);
+    *reinterpret_cast<u32x4*>(tab + 16 * c) = w;
   }
 }
 
-__device__ void build_sign_table(uint8_t* tab, int tid) {
-  f16x8 v;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = ((tid >> i) & 1) ? static_cast<_Float16>(1.0f) : static_cast<_Float16>(-1.0f);
-  *reinterpret_cast<f16x8*>(tab + tid * 16) = v;
-}
-
-// Bits P .. P+N-1 of the little-endian dword array dw, shifted left by S (a byte offset).
+// Bits P .. P+N-1 of the little-endian dword array dw, shifted left by S.
 template <int P, int N, int S>
 __device__ __forceinline__ uint32_t field(const uint32_t* dw) {
   constexpr int w = P >> 5, o = P & 31;
@@ -144,28 +147,24 @@ __device__ __forceinline__ uint32_t field(const uint32_t* dw) {
   }
 }
 
-// The 8 B-bit codes starting at bit P of dw -> f16x8, via the LDS table tab.
+// The 8 codes (B bits each, or sign bits for B = 1 in the sign table) starting at bit P of dw ->
+// f16x8, through table Tab<B> at tab.
 template <int B, int P>
 __device__ __forceinline__ f16x8 decode8(const uint32_t* dw, const uint8_t* tab) {
-  if constexpr (B == 1) {
-    return *reinterpret_cast<const f16x8*>(tab + field<P, 8, 4>(dw));
-  } else if constexpr (B == 2 || B == 3) {
-    constexpr int K = Dec<B>::KEYBITS;
-    const u32x2 a = *reinterpret_cast<const u32x2*>(tab + field<P, K, 3>(dw));
-    const u32x2 b = *reinterpret_cast<const u32x2*>(tab + field<P + K, K, 3>(dw));
-    return __builtin_bit_cast(f16x8, u32x4{a[0], a[1], b[0], b[1]});
+  using T = Tab<B>;
+  constexpr int K = T::K, S = T::SHIFT;
+  if constexpr (T::EBYTES == 16) {
+    return *reinterpret_cast<const f16x8*>(tab + field<P, K, S>(dw));
+  } else if constexpr (T::EBYTES == 8) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(tab + field<P, K, S>(dw));
+    const u32x2 y = *reinterpret_cast<const u32x2*>(tab + field<P + K, K, S>(dw));
+    return __builtin_bit_cast(f16x8, u32x4{x[0], x[1], y[0], y[1]});
   } else {
-    return __builtin_bit_cast(f16x8, u32x4{*reinterpret_cast<const uint32_t*>(tab + field<P, 8, 2>(dw)),
-                                           *reinterpret_cast<const uint32_t*>(tab + field<P + 8, 8, 2>(dw)),
-                                           *reinterpret_cast<const uint32_t*>(tab + field<P + 16, 8, 2>(dw)),
-                                           *reinterpret_cast<const uint32_t*>(tab + field<P + 24, 8, 2>(dw))});
+    return __builtin_bit_cast(f16x8, u32x4{*reinterpret_cast<const uint32_t*>(tab + field<P, K, S>(dw)),
+                                           *reinterpret_cast<const uint32_t*>(tab + field<P + K, K, S>(dw)),
+                                           *reinterpret_cast<const uint32_t*>(tab + field<P + 2 * K, K, S>(dw)),
+                                           *reinterpret_cast<const uint32_t*>(tab + field<P + 3 * K, K, S>(dw))});
   }
-}
-
-// 8 sign bits starting at bit P of dw -> f16x8 of +1 / -1.
-template <int P>
-__device__ __forceinline__ f16x8 decode_signs(const uint32_t* dw, const uint8_t* tab) {
-  return *reinterpret_cast<const f16x8*>(tab + field<P, 8, 4>(dw));
 }
 
 // Reductions over the 4 lanes of a column (lanes l, l^16, l^32, l^48) with the gfx950
@@ -182,6 +181,14 @@ __device__ __forceinline__ float col_sum(float v) {
   v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The value of the lane N columns further on within its row of 16 lanes (row rotation), an
+// operand modifier of the add that consumes it.
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  static_assert(N > 0 && N < 16, "rotation within a row");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
 }
 
 template <int I, int N, typename F>
@@ -297,16 +304,42 @@ template <int KB, bool QJL, int VB, int G>
 struct MainCfg {
   static constexpr int TPD = 16 / G;       // score tiles packed into one accumulator set
   static constexpr int NSETS = 4 / TPD;    // accumulator sets per 64-key block
+  // Score terms: the key-code part (C) and the sign part (S), each as the product with an f16
+  // hi and lo term of the (scaled) query coordinates: kinds 0 = C hi, 1 = C lo, 2 = S hi,
+  // 3 = S lo.  The 16 columns of a score MFMA hold NP = 16 / G parts of G q-heads each; the
+  // NT terms fill the parts of NA accumulators, term (a NP + k) % NT in part k of accumulator a
+  // (with fewer terms than parts they repeat), except that one accumulator with all four terms
+  // orders its parts C hi, S hi, C lo, S lo (see the score assembly).
+  static constexpr int NT = (KB > 0 ? 2 : 0) + (QJL ? 2 : 0);
+  static constexpr int NP = 16 / G;
+  static constexpr int NA = NT > NP ? NT / NP : 1;
+  static constexpr bool MIXED = NA == 1 && NT == 4;  // C and S terms share the accumulator
+  static constexpr int kind(int a, int k) {
+    if (MIXED) return k == 0 ? 0 : (k == 1 ? 2 : (k == 2 ? 1 : 3));
+    const int i = (a * NP + k) % NT;
+    return KB > 0 ? i : i + 2;
+  }
+  static constexpr bool has_c(int a) {
+    bool r = false;
+    for (int k = 0; k < NP; ++k) r = r || kind(a, k) < 2;
+    return r;
+  }
+  static constexpr bool has_s(int a) {
+    bool r = false;
+    for (int k = 0; k < NP; ++k) r = r || kind(a, k) >= 2;
+    return r;
+  }
   static constexpr bool SHARED = (KB == VB);  // one table serves keys and values
-  static constexpr int KTAB = KB > 0 ? Dec<(KB > 0 ? KB : 1)>::LDS_BYTES : 0;
-  static constexpr int STAB = QJL ? SIGN_TABLE_BYTES : 0;
-  static constexpr int VTAB = SHARED ? 0 : Dec<VB>::LDS_BYTES;
-  static constexpr int TABLES = KTAB + STAB + VTAB;
-  // the epilogue reuses the table space once every wave has left the block loop
-  static constexpr int MERGE = static_cast<int>(sizeof(Epi));
+  static constexpr int KTAB = KB > 0 ? Tab<(KB > 0 ? KB : 1)>::BYTES : 0;
+  static constexpr int STAB = QJL ? Tab<1>::BYTES : 0;
+  static constexpr int VTAB = SHARED ? 0 : Tab<VB>::BYTES;
+  static constexpr int KOFF = 0, SOFF = KTAB, VOFF = SHARED ? 0 : KTAB + STAB;
   // the G query records are staged behind the tables before the block loop (the epilogue,
   // which aliases both, comes after it)
   static constexpr int QSTAGE = G * QREC * 4;
+  static constexpr int TABLES = KTAB + STAB + VTAB;
+  // the epilogue reuses the table space once every wave has left the block loop
+  static constexpr int MERGE = static_cast<int>(sizeof(Epi));
   static constexpr int LDS = TABLES + QSTAGE > MERGE ? TABLES + QSTAGE : MERGE;
 };
 
@@ -316,9 +349,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   using C = MainCfg<KB, QJL, VB, G>;
   constexpr int TPD = C::TPD, NSETS = C::NSETS;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
-  uint8_t* ktab = smem;
-  uint8_t* stab = smem + C::KTAB;
-  uint8_t* vtab = C::SHARED ? smem : smem + C::KTAB + C::STAB;
+  constexpr int KBT = KB > 0 ? KB : 1;  // key code width of the (unused when KB = 0) key table
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, g = lane >> 4;
@@ -357,6 +388,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
     if constexpr (QJL) load_dwords<4>(d.sd, a.k_signs + (bh * nblk_cap + blk) * 1024 + lane * 16);
     load_dwords<4 * VB>(d.vd, a.v_codes + (bh * nblk_cap + blk) * (1024 * VB) + lane * 16 * VB);
   };
+  // Norms of the lane's kept keys (set s: tile s TPD + tcls, rows 4 g .. 4 g + 3).
   struct Norms {
     f32x4 kn[NSETS], kr[NSETS], vn[NSETS];
   };
@@ -369,16 +401,6 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
       d.vn[s] = *reinterpret_cast<const f32x4*>(a.v_norm + tok);
     }
   };
-  // score operands from the prologue's record of head hh: lane (col, g) holds
-  // q[hh][32 g + 8 kb + e] of every k-block kb as two f16 terms (hi + lo, the fp32 value to
-  // about 22 bits), scaled by 2^-e with e the exponent of the vector's largest magnitude (the
-  // 4 lanes of a column hold the 128 coordinates).  One f16 term alone leaves a relative
-  // error of 2^-12 per coordinate, which large logits carry into the softmax weights.
-  // logit * log2(e) = n (code_acc * c1 + rnorm * sign_acc * c2): the table holds centroids c,
-  // the key term is q1 . c / sqrt(d), the sign term carries sqrt(pi/2)/m.
-  // The G query records of this kv-head (contiguous) go through LDS: one 16-byte load per
-  // thread (two for G = 16), issued before the block loads, so that no wave's query waits
-  // behind other waves' block loads.
   constexpr int QWORDS = G * QREC / 4;
   constexpr int QPT = (QWORDS + NT - 1) / NT;
   float* const qst = reinterpret_cast<float*>(smem + C::TABLES);
@@ -388,29 +410,45 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
 #pragma unroll
     for (int k = 0; k < QPT; ++k) qw[k] = *reinterpret_cast<const f32x4*>(qsrc + 4 * min(tid + k * NT, QWORDS - 1));
   }
+  // The G query records of this kv-head (contiguous) go through LDS: one 16-byte load per
+  // thread (two for G = 16), issued before the block loads, so that no wave's query waits
+  // behind other waves' block loads.
   // Block loads are unconditional, from clamped (always in-bounds) block indices: a load under
   // a branch would make the compiler wait for every load in flight where the branches join,
   // which would serialize the prefetch with the current block's compute.
   Blk cur, nxt;
   load_block(min(blk_begin, nblk_cap - 1), cur);  // in flight while the tables are built
 
-  if (wave < 4) {  // the table builders take 256 threads
-    if constexpr (KB > 0) build_code_table<(KB > 0 ? KB : 1)>(ktab, a.k_cent, tid);
-    if constexpr (QJL) build_sign_table(stab, tid);
-    if constexpr (!C::SHARED) build_code_table<VB>(vtab, a.v_cent, tid);
-  }
+  if constexpr (KB > 0) build_table<KBT, false>(smem + C::KOFF, a.k_cent, tid);
+  if constexpr (QJL) build_table<1, true>(smem + C::SOFF, nullptr, tid);
+  if constexpr (!C::SHARED) build_table<VB, false>(smem + C::VOFF, a.v_cent, tid);
 #pragma unroll
   for (int k = 0; k < QPT; ++k)
     if (tid + k * NT < QWORDS) *reinterpret_cast<f32x4*>(qst + 4 * (tid + k * NT)) = qw[k];
   __syncthreads();  // tables and query records ready
-  f16x8 bq[4], bs[4], bql[4], bsl[4];
-  float c1, c2;
+  // Score operands.  For q-head hh = col % G: x1 = q1 c1 and x2 = q2 c2 with the constant factors
+  // of the score folded in (c1 = log2(e) scale / sqrt(d) / k_scale (/ sqrt(d) in one-pass
+  // rotation mode): the key term is q1 . c / sqrt(d); c2 = log2(e) scale sqrt(pi/2) / m: the sign
+  // term), each scaled by a power of two 2^-e that brings its largest magnitude into [0.5, 1) (the
+  // 4 lanes of a column hold the 128 coordinates), then split into two f16 terms (hi + lo, the
+  // fp32 value to about 22 bits: one f16 term alone leaves a relative error of 2^-12 per
+  // coordinate, which large logits carry into the softmax weights).  Lane (col, g) holds, for
+  // k-block kb, coordinates 32 g + 8 kb + e of the term of its part k = col / G in each
+  // accumulator (zero in the code operand for sign terms and the other way round); u1 and u2
+  // undo the two scalings.
+  const int part = col / G;
+  f16x8 bc[C::NA][4], bsg[C::NA][4];
+  float u1, u2;
   {
+    const float lscale = a.scale * LOG2E;
+    const float c1 = INV_SQRT_D * lscale * a.k_unscale * a.rot_scale, c2 = KAPPA * lscale;
     f32x4 qv1[8], qv2[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      qv1[i] = *reinterpret_cast<const f32x4*>(qst + hh * QREC + 32 * g + 4 * i);
-      qv2[i] = QJL ? *reinterpret_cast<const f32x4*>(qst + hh * QREC + D + 32 * g + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+      qv1[i] = KB > 0 ? *reinterpret_cast<const f32x4*>(qst + hh * QREC + 32 * g + 4 * i) * c1
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+      qv2[i] = QJL ? *reinterpret_cast<const f32x4*>(qst + hh * QREC + D + 32 * g + 4 * i) * c2
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float m1 = 0.f, m2 = 0.f;
 #pragma unroll
@@ -426,21 +464,30 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
     if (m1 > 0.f) frexpf(m1, &e1);
     if (m2 > 0.f) frexpf(m2, &e2);
     const float s1 = ldexpf(1.0f, -e1), s2 = ldexpf(1.0f, -e2);  // exact powers of two
-    auto lo16 = [](float x, _Float16 hi) { return static_cast<_Float16>(x - static_cast<float>(hi)); };
+    u1 = ldexpf(1.0f, e1);
+    u2 = ldexpf(1.0f, e2);
+    // this lane's term in each accumulator (part = col / G)
+    int kd[C::NA];
+    static_for<0, C::NA>([&](auto A_) {
+      kd[A_] = 0;
+      static_for<0, C::NP>([&](auto K_) {
+        if (part == decltype(K_)::value) kd[A_] = C::kind(decltype(A_)::value, decltype(K_)::value);
+      });
+    });
+    const _Float16 z16 = static_cast<_Float16>(0.0f);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float x1 = qv1[2 * kb + j / 4][j % 4] * s1, x2 = qv2[2 * kb + j / 4][j % 4] * s2;
-        const _Float16 h1 = static_cast<_Float16>(x1), h2 = static_cast<_Float16>(x2);
-        bq[kb][j] = h1;
-        bql[kb][j] = lo16(x1, h1);
-        bs[kb][j] = h2;
-        bsl[kb][j] = lo16(x2, h2);
+        const _Float16 h1 = static_cast<_Float16>(x1), l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
+        const _Float16 h2 = static_cast<_Float16>(x2), l2 = static_cast<_Float16>(x2 - static_cast<float>(h2));
+#pragma unroll
+        for (int ac = 0; ac < C::NA; ++ac) {
+          bc[ac][kb][j] = kd[ac] == 0 ? h1 : (kd[ac] == 1 ? l1 : z16);
+          bsg[ac][kb][j] = kd[ac] == 2 ? h2 : (kd[ac] == 3 ? l2 : z16);
+        }
       }
-    const float lscale = a.scale * LOG2E;
-    c1 = ldexpf(1.0f, e1) * INV_SQRT_D * lscale * a.k_unscale;
-    c2 = ldexpf(1.0f, e2) * KAPPA * lscale;
   }
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
@@ -448,42 +495,67 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
     load_norms(blk, nrm);
     load_block(min(blk + 1, blk_end - 1), nxt);
 
-    // ---- score MFMAs: tile t = keys 16 t .. 16 t + 15 of the block; each lane keeps the
-    // tile of its column class in every set (tile s TPD + tcls of set s) ----------------------
-    f32x4 cs[NSETS], ss[NSETS];
+    // ---- scores: tile t = keys 16 t .. 16 t + 15 of the block.  Per accumulator, the code and
+    // sign MFMAs (operands zero outside their own terms' columns) sum into one register set.
+    // The hi and lo parts are then summed across lanes (row rotations by G columns) and, for
+    // the shared accumulator of G = 4, the sign sum brought next to the code sum (parts C hi,
+    // S hi, C lo, S lo: rotating by 2 G gives C or S in every lane, rotating that by G the
+    // other one).  Each lane keeps the pair (p, q) of the tile of its column class in every set
+    // (tile s TPD + tcls of set s) ------------------------------------------------------------
+    f32x4 cp[NSETS], cq[NSETS];
     static_for<0, 4>([&](auto T_) {
       constexpr int t = decltype(T_)::value;
-      f32x4 dc = f32x4{0.f, 0.f, 0.f, 0.f}, ds = f32x4{0.f, 0.f, 0.f, 0.f};
-      f32x4 dcl = f32x4{0.f, 0.f, 0.f, 0.f}, dsl = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (KB > 0) {
-        static_for<0, 4>([&](auto KB_) {
-          constexpr int kb = decltype(KB_)::value;
-          const f16x8 ak = decode8<KB, 32 * KB * t + 8 * KB * kb>(cur.kd, ktab);
-          dc = mfma_f16(ak, bq[kb], dc);
-          dcl = mfma_f16(ak, bql[kb], dcl);
-        });
+      f32x4 v[C::NA];
+      static_for<0, C::NA>([&](auto A_) {
+        constexpr int ac = decltype(A_)::value;
+        f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (KB > 0 && C::has_c(ac)) {
+          static_for<0, 4>([&](auto KB_) {
+            constexpr int kb = decltype(KB_)::value;
+            d = mfma_f16(decode8<KBT, 32 * KB * t + 8 * KB * kb>(cur.kd, smem + C::KOFF), bc[ac][kb], d);
+          });
+        }
+        if constexpr (QJL && C::has_s(ac)) {
+          static_for<0, 4>([&](auto KB_) {
+            constexpr int kb = decltype(KB_)::value;
+            d = mfma_f16(decode8<1, 32 * t + 8 * kb>(cur.sd, smem + C::SOFF), bsg[ac][kb], d);
+          });
+        }
+        v[ac] = d;
+      });
+      f32x4 p, q = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (C::MIXED) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = v[0][i] + row_ror<2 * G>(v[0][i]);
+          q[i] = row_ror<G>(p[i]);
+        }
+      } else if constexpr (C::NP >= 2) {  // NA = 1 (one kind of term) or 2 (C, S): hi, lo parts
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = v[0][i] + row_ror<G>(v[0][i]);
+          if constexpr (C::NA == 2) q[i] = v[1][i] + row_ror<G>(v[1][i]);
+        }
+      } else {  // G = 16: one term per accumulator, in lane order C hi, C lo, S hi, S lo
+        p = v[0] + v[1];
+        if constexpr (C::NA == 4) q = v[2] + v[3];
       }
-      if constexpr (QJL) {
-        static_for<0, 4>([&](auto KB_) {
-          constexpr int kb = decltype(KB_)::value;
-          const f16x8 as = decode_signs<32 * t + 8 * kb>(cur.sd, stab);
-          ds = mfma_f16(as, bs[kb], ds);
-          dsl = mfma_f16(as, bsl[kb], dsl);
-        });
-      }
-      dc += dcl;
-      ds += dsl;
       constexpr int st_ = t / TPD, ct = t % TPD;
       if constexpr (ct == 0) {
-        cs[st_] = dc;
-        ss[st_] = ds;
+        cp[st_] = p;
+        cq[st_] = q;
       } else {
         if (tcls == ct) {
-          cs[st_] = dc;
-          ss[st_] = ds;
+          cp[st_] = p;
+          cq[st_] = q;
         }
       }
     });
+    // logit * log2(e) = n (u1 C + u2 rnorm S): C, S are p, q (or q, p in the odd parts of a
+    // shared accumulator); with one kind of term, p alone
+    const bool odd = C::MIXED && (part & 1);
+    const float a1 = odd ? 0.f : u1, a2 = odd ? u1 : 0.f;  // weights of p and q for C
+    const float b1 = odd ? u2 : 0.f, b2 = odd ? 0.f : u2;  // weights of p and q for S
 
     // ---- logits of this lane's keys: set s, row i -> key 16 (s TPD + tcls) + 4 g + i --------
     // lg = logit * log2(e); lgb = lg + an upper bound of log2(nv) (from the float exponent),
@@ -495,10 +567,14 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = blk * 64 + 16 * (s * TPD + tcls) + 4 * g + i;
-        float est = 0.f;
-        if constexpr (KB > 0) est = cs[s][i] * c1;
-        if constexpr (QJL) est = fmaf((KB > 0 ? nrm.kr[s][i] : 1.0f) * ss[s][i], c2, est);
-        const float l2 = nrm.kn[s][i] * est;
+        float sc;
+        if constexpr (C::NT == 4) {
+          const float r = nrm.kr[s][i];
+          sc = fmaf(cp[s][i], fmaf(r, b1, a1), cq[s][i] * fmaf(r, b2, a2));
+        } else {
+          sc = cp[s][i] * (KB > 0 ? u1 : u2);
+        }
+        const float l2 = nrm.kn[s][i] * sc;
         const bool valid = key < seq;
         if constexpr (SCORES) {
           if (valid) a.scores_out[((int64_t)b * Hq + kvh * G + hh) * a.T_cap + key] = l2 * (1.0f / LOG2E);
@@ -553,7 +629,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
       const f16x8 bp = __builtin_bit_cast(f16x8, bpw);
       static_for<0, 8>([&](auto MT) {
         constexpr int mt = decltype(MT)::value;
-        const f16x8 av = decode8<VB, 8 * VB * (2 * mt + kb2)>(cur.vd, vtab);
+        const f16x8 av = decode8<VB, 8 * VB * (2 * mt + kb2)>(cur.vd, smem + C::VOFF);
         acc[mt] = mfma_f16(av, bp, acc[mt]);
       });
     });
@@ -682,20 +758,27 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   f32x4 uh[3][2];
 #pragma unroll
   for (int t = 0; t < 3; ++t) uh[t][0] = uh[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto unrotate = [&](auto one_) {
+    constexpr bool ONE = decltype(one_)::value;  // R_lo^T = 0: one pass
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    float v[8];
-    const float* src = &ep->amat[col][32 * g + 8 * kb];
-    *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
-    *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
-    bf16x8 p[3];
-    split3_bf16(v, p[0], p[1], p[2]);
+    for (int kb = 0; kb < 4; ++kb) {
+      float v[8];
+      const float* src = &ep->amat[col][32 * g + 8 * kb];
+      *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
+      *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
+      bf16x8 p[3];
+      split3_bf16(v, p[0], p[1], p[2]);
 #pragma unroll
-    for (int t = 0; t < 3; ++t) {
-      uh[t][0] = mfma_bf16(p[t], th[kb], uh[t][0]);
-      uh[t][1] = mfma_bf16(p[t], tl[kb], uh[t][1]);
+      for (int t = 0; t < 3; ++t) {
+        uh[t][0] = mfma_bf16(p[t], th[kb], uh[t][0]);
+        if constexpr (!ONE) uh[t][1] = mfma_bf16(p[t], tl[kb], uh[t][1]);
+      }
     }
-  }
+  };
+  if (a.one_pass)  // uniform
+    unrotate(std::true_type{});
+  else
+    unrotate(std::false_type{});
   const f32x4 u = (uh[0][0] + uh[0][1]) + ((uh[1][0] + uh[1][1]) + (uh[2][0] + uh[2][1]));
   if (ngrp == 1) {
 #pragma unroll
@@ -704,7 +787,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
       if (h >= G) continue;
       const float L = ep->st[h][1];
       // value centroids enter as c v_scale / sqrt(d)
-      const float f = L > 0.f ? INV_SQRT_D * a.v_unscale / L : 0.f;
+      const float f = L > 0.f ? INV_SQRT_D * a.v_unscale * a.rot_scale / L : 0.f;
       a.out[(bh * G + h) * D + 16 * wave + col] = u[i] * f;
     }
     return;
@@ -729,7 +812,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   for (int h = wave; h < G; h += NW) {
     const Merged r = merge_records(a.gpart + (bh * G + h) * ngrp * PREC, ngrp, lane);
     // value centroids enter as c v_scale / sqrt(d)
-    const float f = r.L > 0.f ? INV_SQRT_D * a.v_unscale / r.L : 0.f;
+    const float f = r.L > 0.f ? INV_SQRT_D * a.v_unscale * a.rot_scale / r.L : 0.f;
     float* o = a.out + (bh * G + h) * D + 2 * lane;  // out is only 4-byte aligned
     o[0] = r.A0 * f;
     o[1] = r.A1 * f;
@@ -738,8 +821,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
 
 template <int KB, bool QJL, int VB, int G>
 hipError_t launch_main(const MainArgs& a, int n_slices, int B, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
-  using C = MainCfg<KB, QJL, VB, G>;
-  static_assert(C::LDS <= 65536, "attention LDS budget");
+  static_assert(MainCfg<KB, QJL, VB, G>::LDS <= 64 * 1024, "attention LDS budget");
   auto kern = a.scores_out != nullptr ? attend_kernel<KB, QJL, VB, G, true> : attend_kernel<KB, QJL, VB, G, false>;
   if (e0 != nullptr || e1 != nullptr)
     hipExtLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(NT), 0, s, e0, e1, 0, a);

@@ -258,11 +258,16 @@ int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, tq_host_params* out
     gaussian_fill(2ull * cfg->seed, G.data(), d * d);
     haar_rotation(G.data(), R.data(), d);
   }
+  // Haar: R_eff = R_hi + R_lo, the bf16 split of R.  Hadamard: R = H diag(s) / sqrt(d) with
+  // H diag(s) = +-1 exact in bf16, so R_hi = H diag(s), R_lo = 0 and R_eff = R exactly (the
+  // kernels apply 1/sqrt(d) as a scale).
+  const bool hadamard = cfg->rotation == TQ_ROTATION_HADAMARD;
   for (int i = 0; i < d; ++i)
     for (int j = 0; j < d; ++j) {
       const double r = R[static_cast<size_t>(i) * d + j];
-      const uint16_t hi = to_bf16(r), lo = to_bf16(r - from_bf16(hi));
-      Reff[static_cast<size_t>(i) * d + j] = from_bf16(hi) + from_bf16(lo);
+      const uint16_t hi = hadamard ? to_bf16(r < 0.0 ? -1.0 : 1.0) : to_bf16(r);
+      const uint16_t lo = hadamard ? uint16_t(0) : to_bf16(r - from_bf16(hi));
+      Reff[static_cast<size_t>(i) * d + j] = hadamard ? r : from_bf16(hi) + from_bf16(lo);
       if (out->r_hi) out->r_hi[i * d + j] = hi;
       if (out->r_lo) out->r_lo[i * d + j] = lo;
       if (out->rt_hi) out->rt_hi[j * d + i] = hi;
@@ -277,7 +282,7 @@ int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, tq_host_params* out
   if (out->m_hi || out->m_lo) {
     for (int i = 0; i < d; ++i)
       for (int j = 0; j < d; ++j) {
-        double m = 0.0;  // M = S_b R_eff, every product exact in fp64 (8 x 16 significant bits)
+        double m = 0.0;  // M = S_b R_eff (Haar: every product exact in fp64, 8 x 16 significant bits)
         for (int k = 0; k < d; ++k) m += Sb[static_cast<size_t>(i) * d + k] * Reff[static_cast<size_t>(k) * d + j];
         const uint16_t hi = to_bf16(m);
         if (out->m_hi) out->m_hi[i * d + j] = hi;

@@ -57,14 +57,14 @@ __device__ __forceinline__ void load_query_operands(QOperands<QJL>& o, const voi
   for (int i = 0; i < 8; ++i) o.raw[i] = *reinterpret_cast<const u32x4*>(base + 16 * min(i, last));
 }
 
-// Accumulates the products of one k-block for both output tiles: q1 += a (r_hi + r_lo),
-// q2 += a (m_hi + m_lo).
-template <bool QJL>
+// Accumulates the products of one k-block for both output tiles: q1 += a (r_hi + r_lo), or
+// a r_hi alone in one-pass mode (Hadamard: r_lo = 0); q2 += a (m_hi + m_lo).
+template <bool QJL, bool ONE>
 __device__ __forceinline__ void rotate_step(const QOperands<QJL>& o, int kb, bf16x8 a, f32x4* d1, f32x4* d2) {
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     d1[nt] = mfma_bf16(a, o.rh[nt][kb], d1[nt]);
-    d1[nt] = mfma_bf16(a, o.rl[nt][kb], d1[nt]);
+    if constexpr (!ONE) d1[nt] = mfma_bf16(a, o.rl[nt][kb], d1[nt]);
     if constexpr (QJL) {
       d2[nt] = mfma_bf16(a, o.mh[nt][kb], d2[nt]);
       d2[nt] = mfma_bf16(a, o.ml[nt][kb], d2[nt]);
@@ -72,8 +72,9 @@ __device__ __forceinline__ void rotate_step(const QOperands<QJL>& o, int kb, bf1
   }
 }
 
-// d1 += q (R_hi + R_lo), d2 += q (M_hi + M_lo) for the lane's output tiles (all k-blocks).
-template <bool QJL>
+// d1 += q (R_hi + R_lo) (q R_hi in one-pass mode), d2 += q (M_hi + M_lo) for the lane's output
+// tiles (all k-blocks).
+template <bool QJL, bool ONE>
 __device__ __forceinline__ void rotate_products(const QOperands<QJL>& o, bool q_f32, f32x4* d1, f32x4* d2) {
   const bf16x8 zero = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   if (q_f32) {
@@ -88,14 +89,14 @@ __device__ __forceinline__ void rotate_products(const QOperands<QJL>& o, bool q_
       }
       bf16x8 ph, pm, pl;
       split3_bf16(x, ph, pm, pl);
-      rotate_step<QJL>(o, kb, ph, d1, d2);
-      rotate_step<QJL>(o, kb, pm, d1, d2);
-      rotate_step<QJL>(o, kb, pl, d1, d2);
+      rotate_step<QJL, ONE>(o, kb, ph, d1, d2);
+      rotate_step<QJL, ONE>(o, kb, pm, d1, d2);
+      rotate_step<QJL, ONE>(o, kb, pl, d1, d2);
     }
   } else {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      rotate_step<QJL>(o, kb, o.valid ? __builtin_bit_cast(bf16x8, o.raw[kb]) : zero, d1, d2);
+      rotate_step<QJL, ONE>(o, kb, o.valid ? __builtin_bit_cast(bf16x8, o.raw[kb]) : zero, d1, d2);
   }
 }
 
@@ -116,6 +117,7 @@ struct PrologueArgs {
   // launch, so a workspace needs no initial contents
   unsigned* cnt;
   int cnt_per_unit;
+  int one_pass;  // Hadamard mode: q1 = q r_hi (one pass; the record holds sqrt(d) R q)
 };
 
 template <bool QJL>
@@ -128,7 +130,10 @@ __device__ __forceinline__ void rotate_query_tile(const PrologueArgs& a, int uni
   load_query_operands<QJL>(qo, a.q, a.q_f32 != 0, head0, G, a.r_hi, a.r_lo, a.m_hi, a.m_lo, tile, col, g);
   f32x4 d1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   f32x4 d2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  rotate_products<QJL>(qo, a.q_f32 != 0, d1, d2);
+  if (a.one_pass)
+    rotate_products<QJL, true>(qo, a.q_f32 != 0, d1, d2);
+  else
+    rotate_products<QJL, false>(qo, a.q_f32 != 0, d1, d2);
   // D layout: lane (col, g) holds head 4 g + i, output coordinate 32 tile + 16 nt + col
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

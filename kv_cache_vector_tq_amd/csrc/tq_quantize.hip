@@ -85,7 +85,7 @@ __device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& s
     const int start_lane = q.k.start_pos[b + static_cast<int>(__builtin_amdgcn_mbcnt_lo(0u, 0u))];
     const TileRef row0{tensor, b, h, 0, 0, 0, 1};
     load_rows<F32>(q, row0, tid, in);
-    load_rows_norms<F32>(sm, row0, in, tid);
+    load_rows_norms<F32>(sm, row0, in, tid, q.k.zscale);
     const int start = __builtin_amdgcn_readfirstlane(start_lane);
     if (start < 0 || start >= q.k.T_cap) return;  // uniform: the row is not written
     const TileRef cur{tensor, b, h, start, start / 64, start, start + 1};
@@ -108,7 +108,7 @@ __device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& s
     TileRef nxt;
     const bool more = find_tile(q, t + nwg, nwg, tn, nxt);
     lds_barrier();  // the previous tile is done with LDS
-    load_rows_norms<F32>(sm, cur, in, tid);
+    load_rows_norms<F32>(sm, cur, in, tid, q.k.zscale);
     uint32_t prev[4];
     load_prev<VB>(q, cur, tid, prev);  // used at the end of the tile
     // the next tile's rows are in flight while this tile computes
@@ -242,6 +242,8 @@ int quantize_args(const tq_codebook* cb, const tq_dev_params* p, const void* k, 
   a.T_cap = cache->T_cap;
   a.r_hi = p->r_hi;
   a.r_lo = p->r_lo;
+  a.one_pass = cb->cfg.rotation == TQ_ROTATION_HADAMARD ? 1 : 0;
+  a.zscale = a.one_pass ? 1.0f : SQRT_D;
   *ka = a;
   ka->x = k;
   ka->s_b = p->s_qjl;
@@ -294,8 +296,8 @@ int quantize_launch(const tq_codebook* cb, const tq_dev_params* p, const void* k
   PrologueArgs pa{};
   QuantGrid qg{grid, nullptr, 0};
   if (rot != nullptr) {
-    pa = PrologueArgs{rot->q,    rot->r_hi, rot->r_lo, rot->m_hi, rot->m_lo, rot->qrec,
-                      rot->G,    rot->q_f32, rot->cnt,  rot->cnt_per_unit};
+    pa = PrologueArgs{rot->q,    rot->r_hi, rot->r_lo, rot->m_hi,         rot->m_lo, rot->qrec,
+                      rot->G,    rot->q_f32, rot->cnt,  rot->cnt_per_unit, q.k.one_pass};
     qg.pa = &pa;
     qg.rot_wgs = rot->units;
   }

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "tq_common.h"
 
@@ -24,6 +25,11 @@ struct QuantArgs {
   float* rnorm;
   float centroids[16];
   float thresholds[16];
+  // rotation: one_pass = 0: R_eff = r_hi + r_lo (two bf16 passes), z = sqrt(d) R_eff x / n;
+  // one_pass = 1 (Hadamard): r_hi = H diag(s) (+-1), R_eff = r_hi / sqrt(d), so z = r_hi x / n
+  // (one pass).  zscale = sqrt(d) or 1: z = zscale * acc / n.
+  int one_pass;
+  float zscale;
 };
 
 // One quantize launch: keys and values of the same call.
@@ -90,7 +96,7 @@ struct Smem {
   uint8_t sgn[64 * IDX_STRIDE];
   float norm[64];
   float rnorm[64];
-  float zs[64];  // sqrt(d) / norm (0 for a zero row)
+  float zs[64];  // zscale / norm (0 for a zero row)
 };
 
 // Rotation (hi, lo) and sketch operands of one wave: lane (col, grp) holds row
@@ -132,7 +138,8 @@ __device__ __forceinline__ void load_prev(const QuantLaunch& q, const TileRef& r
 // LDS, and each row's norm n and sqrt(d) / n are computed.  Rows outside [lo_slot, hi_slot)
 // are zero.
 template <bool F32>
-__device__ __forceinline__ void load_rows_norms(Smem& sm, const TileRef& tr, const TileIn<F32>& in, int tid) {
+__device__ __forceinline__ void load_rows_norms(Smem& sm, const TileRef& tr, const TileIn<F32>& in, int tid,
+                                                float zscale) {
   const int p0 = tr.blk * 64, lo_slot = tr.lo_slot, hi_slot = tr.hi_slot;
   float* s_tile = sm.tile;
   float* s_norm = sm.norm;
@@ -187,7 +194,7 @@ __device__ __forceinline__ void load_rows_norms(Smem& sm, const TileRef& tr, con
     if (q == 0) {
       const float n = mx > 0.f ? ldexpf(sqrtf(ss), ex) : 0.f;
       s_norm[row] = n;
-      sm.zs[row] = n > 0.f ? SQRT_D / n : 0.f;
+      sm.zs[row] = n > 0.f ? zscale / n : 0.f;
     }
   }
 }
@@ -225,13 +232,15 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   const bool partial = partial_tile(tr);  // uniform over the workgroup
 
 
-  // ---- rotation: acc[mt][nt] = X[16 mt.., :] R_eff[32 wave + 16 nt.., :]^T ---------------
+  // ---- rotation: acc[mt][nt] = X[16 mt.., :] R[32 wave + 16 nt.., :]^T, R = r_hi + r_lo, or
+  // r_hi alone in one-pass mode -----------------------------------------------------------------
   f32x4 acc[4][2];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  {
+  auto rotate = [&](auto one_) {
+    constexpr bool ONE = decltype(one_)::value;
     const auto& rh = op.rh;
     const auto& rl = op.rl;
 #pragma unroll
@@ -250,11 +259,11 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             acc[mt][nt] = mfma_bf16(xh, rh[nt][kb], acc[mt][nt]);
-            acc[mt][nt] = mfma_bf16(xh, rl[nt][kb], acc[mt][nt]);
+            if constexpr (!ONE) acc[mt][nt] = mfma_bf16(xh, rl[nt][kb], acc[mt][nt]);
             acc[mt][nt] = mfma_bf16(xm, rh[nt][kb], acc[mt][nt]);
-            acc[mt][nt] = mfma_bf16(xm, rl[nt][kb], acc[mt][nt]);
+            if constexpr (!ONE) acc[mt][nt] = mfma_bf16(xm, rl[nt][kb], acc[mt][nt]);
             acc[mt][nt] = mfma_bf16(xl, rh[nt][kb], acc[mt][nt]);
-            acc[mt][nt] = mfma_bf16(xl, rl[nt][kb], acc[mt][nt]);
+            if constexpr (!ONE) acc[mt][nt] = mfma_bf16(xl, rl[nt][kb], acc[mt][nt]);
           }
         } else {
           const bf16x8 xv =
@@ -262,12 +271,16 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             acc[mt][nt] = mfma_bf16(xv, rh[nt][kb], acc[mt][nt]);
-            acc[mt][nt] = mfma_bf16(xv, rl[nt][kb], acc[mt][nt]);
+            if constexpr (!ONE) acc[mt][nt] = mfma_bf16(xv, rl[nt][kb], acc[mt][nt]);
           }
         }
       }
     }
-  }
+  };
+  if (a.one_pass)  // uniform
+    rotate(std::true_type{});
+  else
+    rotate(std::false_type{});
   lds_barrier();  // the input tile is dead from here on; its space holds residuals
 
   // ---- scale, scalar code, residual (sub-tiles without a token of the call are skipped; the

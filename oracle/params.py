@@ -21,9 +21,12 @@ implementations produce the same matrices:
   (H_ij = (-1)^popcount(i & j)), s_j = -1 when the top bit of the j-th output of the
   rotation stream is set, else +1.  y = R x flips signs, then applies the Walsh-Hadamard
   transform; R is exactly orthogonal.
-* Precision contract: R_hi = bf16(R), R_lo = bf16(R - R_hi) (difference in fp64);
-  R_eff = R_hi + R_lo is the matrix both sides apply.  bf16(v) rounds v to fp32 (ties to
-  even) and then to bf16 (ties to even).
+* Precision contract (Haar mode): R_hi = bf16(R), R_lo = bf16(R - R_hi) (difference in
+  fp64); R_eff = R_hi + R_lo is the matrix both sides apply.  bf16(v) rounds v to fp32 (ties
+  to even) and then to bf16 (ties to even).
+* Precision contract (Hadamard mode): H diag(s) has entries +-1, exact in bf16, so the
+  rotation needs no split: R_hi holds H diag(s), R_lo is zero, and R_eff = R exactly (the
+  factor 1/sqrt(d) is a scale, applied by each side in its own arithmetic).
 * Sketch: S (m x d, m = d) i.i.d. N(0,1) from the sketch stream; S_b = bf16(S) is the
   matrix both sides apply.
 """
@@ -122,14 +125,20 @@ def build_params(seed: int, d: int = 128, m: int = None, rotation: str = "haar")
         R = haar_from_gaussian(G)
     elif rotation == "hadamard":
         G = None
-        R = sylvester_hadamard(d) * hadamard_signs((2 * seed) & MASK64, d)[None, :] / math.sqrt(d)
+        Hs = sylvester_hadamard(d) * hadamard_signs((2 * seed) & MASK64, d)[None, :]
+        R = Hs / math.sqrt(d)
     else:
         raise ValueError(f"rotation must be one of {ROTATIONS}")
-    r_hi = bf16_bits(R)
-    r_lo = bf16_bits(R - bf16_value(r_hi))
+    if rotation == "hadamard":
+        r_hi = bf16_bits(Hs)
+        r_lo = np.zeros((d, d), dtype=np.uint16)
+        R_eff = R
+    else:
+        r_hi = bf16_bits(R)
+        r_lo = bf16_bits(R - bf16_value(r_hi))
+        R_eff = bf16_value(r_hi) + bf16_value(r_lo)
     S = gaussian_matrix((2 * seed + 1) & MASK64, m, d)
     s_b = bf16_bits(S)
-    R_eff = bf16_value(r_hi) + bf16_value(r_lo)
     return {
         "G": G, "R": R, "S": S,
         "r_hi": r_hi, "r_lo": r_lo, "s_b": s_b,

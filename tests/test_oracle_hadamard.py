@@ -54,17 +54,21 @@ def test_rotation_is_sign_flip_then_walsh_hadamard(seed):
     np.testing.assert_array_equal(p["R"][0] * math.sqrt(D), s)
 
 
-def test_orthogonality_exact_and_after_the_bf16_split():
-    p = build_params(0, rotation="hadamard")
-    assert np.abs(p["R"].T @ p["R"] - np.eye(D)).max() < 1e-14
-    E = p["R_eff"].T @ p["R_eff"]
-    # every entry of R_eff has the same magnitude, so distinct columns stay exactly orthogonal
-    assert np.all(E[~np.eye(D, dtype=bool)] == 0.0)
-    assert np.abs(np.diag(E) - 1.0).max() < 1e-5
-    # the bf16 pair: hi is 1/sqrt(d) rounded to bf16, lo the bf16 of the remainder
-    hi = bf16_value(p["r_hi"])
-    assert np.all(np.abs(hi) == np.abs(hi[0, 0]))
-    assert abs(abs(hi[0, 0]) - 1 / math.sqrt(D)) < 2 ** -9 / math.sqrt(D)
+@pytest.mark.parametrize("seed", [0, 9])
+def test_applied_rotation_is_exact_and_needs_no_split(seed):
+    # H diag(s) has entries +-1, exact in bf16: the stored hi term is H diag(s) itself (bf16
+    # patterns 0x3F80 / 0xBF80), the lo term is zero, and the applied rotation is R exactly
+    p = build_params(seed, rotation="hadamard")
+    g = SplitMix64(2 * seed)
+    s = np.array([-1.0 if (g.next() >> 63) else 1.0 for _ in range(D)])
+    Hs = kronecker_hadamard(D) * s[None, :]
+    np.testing.assert_array_equal(p["r_hi"], np.where(Hs > 0, 0x3F80, 0xBF80).astype(np.uint16))
+    np.testing.assert_array_equal(p["r_lo"], np.zeros((D, D), dtype=np.uint16))
+    np.testing.assert_array_equal(bf16_value(p["r_hi"]), Hs)
+    np.testing.assert_array_equal(p["R_eff"], p["R"])
+    # orthogonal to fp64 rounding: (H diag(s))^T (H diag(s)) = d I exactly, and R = that / sqrt(d)
+    np.testing.assert_array_equal(Hs.T @ Hs, D * np.eye(D))
+    assert np.abs(p["R_eff"].T @ p["R_eff"] - np.eye(D)).max() < 1e-15
 
 
 def test_sketch_and_codebooks_do_not_depend_on_the_rotation():
