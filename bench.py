@@ -324,6 +324,50 @@ def time_workload(name, preset, dev, launches=20):
     return res
 
 
+def time_prefill(name, preset, dev, T_p, reps=3):
+    """Prefill of a T_p-token prompt into one layer's packed cache: the bulk quantize-on-write of
+    its keys and values, then causal attention of its T_p queries (all q-heads) over the packed
+    cache (tq_attend_prefill), each timed with HIP events on its stream."""
+    import torch
+
+    import kv_cache_vector_tq_amd as tq
+    import tq_workloads as wl
+
+    w = wl.workload(name)
+    kb, kq, vb = wl.PRESETS[preset]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.cfg_seed)
+    K = torch.randn((w.B, w.Hkv, T_p, 128), generator=gen, device=dev).to(torch.bfloat16)
+    V = torch.randn((w.B, w.Hkv, T_p, 128), generator=gen, device=dev).to(torch.bfloat16)
+    Q = torch.randn((w.B, w.Hq, T_p, 128), generator=gen, device=dev).to(torch.bfloat16)
+    cb = tq.tq_build_codebook(kb, kq, vb, seed=0)
+    dp = tq.upload_params(cb, dev)
+    cache = tq.KVCache(cb, w.B, w.Hkv, T_p, device=dev, zero=False)
+    zero = torch.zeros(w.B, dtype=torch.int32, device=dev)
+    out = torch.empty((w.B, w.Hq, T_p, 128), dtype=torch.float32, device=dev)
+    e0, e1 = event_pair()
+    q_us, a_us = [], []
+    for _ in range(reps):
+        tq.tq_profile_events(quant=(e0, e1))
+        tq.tq_quantize_kv(cb, dp, cache, K, V, zero)
+        torch.cuda.synchronize()
+        q_us.append(e0.elapsed_time(e1) * 1e3)
+        tq.tq_profile_events(attend=(e0, e1))
+        tq.tq_attend_prefill(cb, dp, cache, Q, zero, T_p, out=out)
+        torch.cuda.synchronize()
+        a_us.append(e0.elapsed_time(e1) * 1e3)
+    tq.tq_profile_events()
+    qs, as_ = float(np.median(q_us)), float(np.median(a_us))
+    pairs = w.B * w.Hq * T_p * (T_p + 1) / 2  # (query, visible key) pairs over all q-heads
+    res = {"workload": f"{w.name} prompt of {T_p} tokens", "preset": preset, "prompt_tokens": T_p,
+           "bulk_quantize_us": qs, "prefill_attention_us": as_, "prompt_tokens_per_s": w.B * T_p / ((qs + as_) * 1e-6),
+           "scores_per_s": pairs / (as_ * 1e-6),
+           "bulk_quantize_gbs": bulk_bytes(w.B, w.Hkv, T_p, kb, kq, vb) / (qs * 1e-6) / 1e9}
+    del K, V, Q, cache, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def read_ceiling(dev, mib=4096, grids=(1024, 2048, 4096, 8192), reps=5):
     """The box's streaming read rate: this library's read probe (16-byte loads, one launch over a
     4 GiB buffer, well beyond the 256 MB Infinity Cache) at several grid sizes; the best median
@@ -448,8 +492,12 @@ def main():
                     keep_host=args.cpu_seconds > 0)
     host = (head.pop("_host", None), head.pop("_units", None), head.pop("_q", None))
 
-    steps_extra, others, comparator = [], [], None
+    steps_extra, others, comparator, prefill = [], [], None, []
     if args.other_workloads:
+        for T_p in (4096, 32768):
+            log("prefill", T_p)
+            prefill.append(time_prefill("c2_llama8b_layer_t32k", "turbo3", dev, T_p))
+            log(json.dumps(prefill[-1]))
         for name, preset in EXTRA_STEPS:
             if (name, preset) == (w.name, args.preset):
                 continue
@@ -509,6 +557,7 @@ def main():
             "attend_frac_of_measured_read": ka["gbs"] / read_gbs,
             "steps": steps_extra,
             "workloads": others,
+            "prefill": prefill,
             "bf16_comparator": comparator,
             "targets": {"attend_frac": 0.70, "quantize_frac": 0.60},
         },

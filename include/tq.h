@@ -241,6 +241,27 @@ int tq_decode_step(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_ca
                    int Hq, const int32_t* seq_len, int max_seq_len, float scale, float* out,
                    float* scores_out, void* workspace, size_t* workspace_bytes, void* hip_stream);
 
+/* Prefill attention: causal attention of a prompt's queries straight from the packed cache
+ * (pages: "Когда в марте 2026 года Google опубликовала статью...", paragraph "Теперь про цифры",
+ * quantization overhead at prefill; "Google TurboQuant простыми словами", section "Как
+ * попробовать TurboQuant прямо сейчас", prefill throughput with the compressed cache).  The
+ * prompt's keys and values are first written with tq_quantize_kv; then query t of row b, at
+ * position q_start[b] + t, attends keys 0 .. q_start[b] + t with the score, softmax and value sum
+ * of tq_attend_decode (keys at positions >= max_seq_len are never read: limits are clamped to it).
+ * q: device [B][Hq][T_q][128] in q_dtype, contiguous, 16-byte aligned; q-head h reads kv-head
+ *   h / (Hq / Hkv), Hq / Hkv in {4, 8, 16}.
+ * q_start: device int32 [B] (negative values count as 0).
+ * max_seq_len: host bound (1 .. T_cap) on q_start[b] + T_q.
+ * scale: logit scale; 0 selects 1/sqrt(128).
+ * out: device fp32 [B][Hq][T_q][128] (4-byte aligned).
+ * One launch; no workspace: each workgroup takes max(8, G) / G consecutive queries of all G q-heads
+ * of a kv-head, rotates them itself and writes their outputs.
+ * Errors: TQ_ERR_INVALID (NULL or misaligned arguments, bad shapes), TQ_ERR_UNSUPPORTED (group size,
+ *   config or dtype), TQ_ERR_DEVICE (launch failure). */
+int tq_attend_prefill(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache, const void* q,
+                      tq_dtype q_dtype, int Hq, int T_q, const int32_t* q_start, int max_seq_len, float scale,
+                      float* out, void* hip_stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc): tq_attend_decode with its workspace taken from a
  * fixed array of TQ_NOALLOC_SCRATCH_BYTES bytes of device memory that the library holds, one per

@@ -22,7 +22,7 @@ __all__ = [
     "PRESETS", "Codebook", "DeviceParams", "KVCache", "TQError", "tq_build_codebook", "tq_cache_layout",
     "tq_decode_step", "tq_bf16_attend_decode", "bf16_value_chunks", "bf16_attend_workspace_bytes",
     "tq_quantize_kv", "tq_attend_decode", "tq_abi_version", "tq_profile_events", "upload_params",
-    "attend_workspace_bytes", "tq_read_probe", "tq_attend_decode_noalloc",
+    "attend_workspace_bytes", "tq_read_probe", "tq_attend_decode_noalloc", "tq_attend_prefill",
 ]
 
 
@@ -232,6 +232,26 @@ def tq_attend_decode_noalloc(codebook: Codebook, params: DeviceParams, cache: KV
                                        seq_len.data_ptr(), max_seq_len, float(scale), out.data_ptr(),
                                        scores_out.data_ptr() if scores_out is not None else None,
                                        _stream(q.device)), "tq_attend_decode_noalloc")
+    return out
+
+
+def tq_attend_prefill(codebook: Codebook, params: DeviceParams, cache: KVCache, q, q_start, max_seq_len: int,
+                      scale: float = 0.0, out=None):
+    """Causal prefill attention: q [B, Hq, T_q, 128] (bf16/fp32, contiguous), query t of row b at
+    position q_start[b] + t (int32 device tensor [B]) attends keys 0 .. q_start[b] + t of the cache.
+    Returns out [B, Hq, T_q, 128] fp32."""
+    import torch
+
+    if q.dim() != 4 or q.shape[-1] != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, T_q, 128] tensor")
+    B, Hq, T_q, _ = q.shape
+    if B != cache.B:
+        raise ValueError("q batch does not match the cache")
+    if out is None:
+        out = torch.empty((B, Hq, T_q, HEAD_DIM), dtype=torch.float32, device=q.device)
+    check(lib.tq_attend_prefill(ctypes.byref(codebook.cb), ctypes.byref(params.struct), ctypes.byref(cache.struct),
+                                q.data_ptr(), _dtype_code(q), Hq, T_q, q_start.data_ptr(), max_seq_len,
+                                float(scale), out.data_ptr(), _stream(q.device)), "tq_attend_prefill")
     return out
 
 

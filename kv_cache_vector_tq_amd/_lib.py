@@ -99,6 +99,9 @@ def _load():
     lib.tq_attend_decode_noalloc.restype = ctypes.c_int
     lib.tq_attend_decode_noalloc.argtypes = [P(TQCodebook), P(TQDevParams), P(TQKVCache), vp, ctypes.c_int,
                                              ctypes.c_int, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp]
+    lib.tq_attend_prefill.restype = ctypes.c_int
+    lib.tq_attend_prefill.argtypes = [P(TQCodebook), P(TQDevParams), P(TQKVCache), vp, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, vp, ctypes.c_int, ctypes.c_float, vp, vp]
     lib.tq_decode_step.restype = ctypes.c_int
     lib.tq_decode_step.argtypes = [P(TQCodebook), P(TQDevParams), P(TQKVCache), vp, vp, ctypes.c_int,
                                    ctypes.c_int64, ctypes.c_int64, vp, vp, ctypes.c_int, ctypes.c_int, vp,

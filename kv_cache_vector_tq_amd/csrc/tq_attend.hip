@@ -42,15 +42,15 @@ bool supported(const tq_config& c, int G) {
   return keys && c.v_bits >= 1 && c.v_bits <= 4 && (G == 4 || G == 8 || G == 16);
 }
 
-hipError_t dispatch_main(const MainArgs& a, const tq_config& c, int G, int n_slices, int B, hipStream_t s,
+hipError_t dispatch_main(const MainArgs& a, const tq_config& c, int G, int n_slices, int B, bool pre, hipStream_t s,
                          hipEvent_t e0, hipEvent_t e1) {
   const bool qjl = c.k_qjl != 0;
   switch (c.k_bits) {
-    case 0: return attn::dispatch_k0(a, qjl, c.v_bits, G, n_slices, B, s, e0, e1);
-    case 1: return attn::dispatch_k1(a, qjl, c.v_bits, G, n_slices, B, s, e0, e1);
-    case 2: return attn::dispatch_k2(a, qjl, c.v_bits, G, n_slices, B, s, e0, e1);
-    case 3: return attn::dispatch_k3(a, qjl, c.v_bits, G, n_slices, B, s, e0, e1);
-    case 4: return attn::dispatch_k4(a, qjl, c.v_bits, G, n_slices, B, s, e0, e1);
+    case 0: return attn::dispatch_k0(a, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 1: return attn::dispatch_k1(a, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 2: return attn::dispatch_k2(a, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 3: return attn::dispatch_k3(a, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 4: return attn::dispatch_k4(a, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }
@@ -149,6 +149,40 @@ float table_scale(const float* cent, int bits) {
   return best;
 }
 
+// Kernel arguments shared by decode and prefill attention: cache arrays, decode tables (centroids
+// times their f16 grid factors), logit scale and rotation mode.  scale 0 selects 1/sqrt(d).
+MainArgs main_args(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache, int max_seq_len,
+                   float scale) {
+  MainArgs ma{};
+  if (scale == 0.f) scale = INV_SQRT_D;
+  const int one_pass = cb->cfg.rotation == TQ_ROTATION_HADAMARD ? 1 : 0;
+  ma.k_codes = cache->k_codes;
+  ma.k_signs = cache->k_signs;
+  ma.k_norm = cache->k_norm;
+  ma.k_rnorm = cache->k_rnorm;
+  ma.v_codes = cache->v_codes;
+  ma.v_norm = cache->v_norm;
+  ma.rt_hi = p->rt_hi;
+  ma.rt_lo = p->rt_lo;
+  ma.Hkv = cache->Hkv;
+  ma.T_cap = cache->T_cap;
+  ma.max_seq_len = max_seq_len;
+  ma.scale = scale;
+  ma.scale_log2 = scale * LOG2E;
+  ma.one_pass = one_pass;
+  ma.rot_scale = one_pass ? INV_SQRT_D : 1.0f;
+  const float ks = table_scale(cb->k_centroids, cb->cfg.k_bits);
+  // equal widths share the key table (built from the key centroids), so they share its factor
+  const float vs = cb->cfg.k_bits == cb->cfg.v_bits ? ks : table_scale(cb->v_centroids, cb->cfg.v_bits);
+  for (int l = 0; l < 16; ++l) {
+    ma.k_cent[l] = static_cast<float>(static_cast<double>(cb->k_centroids[l]) * ks);
+    ma.v_cent[l] = static_cast<float>(static_cast<double>(cb->v_centroids[l]) * vs);
+  }
+  ma.k_unscale = static_cast<float>(1.0 / static_cast<double>(ks));
+  ma.v_unscale = static_cast<float>(1.0 / static_cast<double>(vs));
+  return ma;
+}
+
 // tq_attend_decode; with step != NULL the query rotation runs inside the quantize launch of
 // the step's new tokens instead of a launch of its own.
 int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache, const void* q, tq_dtype q_dtype,
@@ -241,48 +275,24 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
     if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("query prologue launch: ") + hipGetErrorString(e));
   }
 
-  MainArgs ma{};
-  ma.k_codes = cache->k_codes;
-  ma.k_signs = cache->k_signs;
-  ma.k_norm = cache->k_norm;
-  ma.k_rnorm = cache->k_rnorm;
-  ma.v_codes = cache->v_codes;
-  ma.v_norm = cache->v_norm;
+  MainArgs ma = main_args(cb, p, cache, max_seq_len, scale);
   ma.seq_len = seq_len;
   ma.qrec = qrec;
-  ma.rt_hi = p->rt_hi;
-  ma.rt_lo = p->rt_lo;
   ma.part = part;
   ma.gpart = gpart;
   ma.cnt = cnt;
   ma.out = out;
   ma.scores_out = scores_out;
-  ma.Hkv = cache->Hkv;
-  ma.T_cap = cache->T_cap;
-  ma.max_seq_len = max_seq_len;
   ma.blocks_per_wave = bpw;
   ma.n_slices = n_slices;
   ma.mgroup = mgroup;
-  ma.scale = scale;
-  ma.scale_log2 = scale * LOG2E;
-  ma.one_pass = one_pass;
-  ma.rot_scale = one_pass ? INV_SQRT_D : 1.0f;
-  const float ks = table_scale(cb->k_centroids, cb->cfg.k_bits);
-  // equal widths share the key table (built from the key centroids), so they share its factor
-  const float vs = cb->cfg.k_bits == cb->cfg.v_bits ? ks : table_scale(cb->v_centroids, cb->cfg.v_bits);
-  for (int l = 0; l < 16; ++l) {
-    ma.k_cent[l] = static_cast<float>(static_cast<double>(cb->k_centroids[l]) * ks);
-    ma.v_cent[l] = static_cast<float>(static_cast<double>(cb->v_centroids[l]) * vs);
-  }
-  ma.k_unscale = static_cast<float>(1.0 / static_cast<double>(ks));
-  ma.v_unscale = static_cast<float>(1.0 / static_cast<double>(vs));
   const ProfileEvents& pe = profile_events();
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (pe.attend_start && pe.attend_stop) {
     e0 = reinterpret_cast<hipEvent_t>(pe.attend_start);
     e1 = reinterpret_cast<hipEvent_t>(pe.attend_stop);
   }
-  const hipError_t e = dispatch_main(ma, cb->cfg, G, n_slices, B, s, e0, e1);
+  const hipError_t e = dispatch_main(ma, cb->cfg, G, n_slices, B, false, s, e0, e1);
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("attention launch: ") + hipGetErrorString(e));
   return TQ_OK;
 }
@@ -368,4 +378,54 @@ extern "C" int tq_attend_decode_noalloc(const tq_codebook* cb, const tq_dev_para
   size_t have = tq::NOALLOC_SCRATCH_BYTES;
   return tq::attend(cb, p, cache, q, q_dtype, Hq, seq_len, max_seq_len, scale, out, scores_out, ws, &have,
                     hip_stream, nullptr);
+}
+
+// ---- prefill attention ------------------------------------------------------------------------
+extern "C" int tq_attend_prefill(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache,
+                                 const void* q, tq_dtype q_dtype, int Hq, int T_q, const int32_t* q_start,
+                                 int max_seq_len, float scale, float* out, void* hip_stream) {
+  using namespace tq;
+  clear_error();
+  if (cb == nullptr || p == nullptr || cache == nullptr || q == nullptr || q_start == nullptr || out == nullptr)
+    return fail(TQ_ERR_INVALID, "cb, p, cache, q, q_start and out must not be NULL");
+  int rc = check_config(cb->cfg);
+  if (rc != TQ_OK) return rc;
+  rc = check_cache(cb->cfg, *cache);
+  if (rc != TQ_OK) return rc;
+  if (Hq < 1 || Hq % cache->Hkv != 0) return fail(TQ_ERR_INVALID, "Hq must be a positive multiple of Hkv");
+  const int G = Hq / cache->Hkv;
+  if (!supported(cb->cfg, G)) return fail(TQ_ERR_UNSUPPORTED, "attention supports Hq/Hkv in {4, 8, 16}");
+  if (T_q < 1) return fail(TQ_ERR_INVALID, "T_q must be >= 1");
+  if (max_seq_len < 1 || max_seq_len > cache->T_cap) return fail(TQ_ERR_INVALID, "max_seq_len must be in 1..T_cap");
+  if (q_dtype != TQ_DTYPE_BF16 && q_dtype != TQ_DTYPE_F32) return fail(TQ_ERR_UNSUPPORTED, "query dtype");
+  if (p->r_hi == nullptr || p->r_lo == nullptr || p->rt_hi == nullptr || p->rt_lo == nullptr ||
+      (cb->cfg.k_qjl && (p->m_hi == nullptr || p->m_lo == nullptr)))
+    return fail(TQ_ERR_INVALID, "device parameter matrices missing");
+  if (!aligned(q, 16) || !aligned(out, 4)) return fail(TQ_ERR_INVALID, "q must be 16-byte and out 4-byte aligned");
+  const int qpg = (G > 8 ? G : 8) / G;  // query positions per unit (max(8, G) columns of (position, q-head))
+  const int64_t NG = (static_cast<int64_t>(T_q) + qpg - 1) / qpg;
+  if (NG * cache->Hkv > (1ll << 30)) return fail(TQ_ERR_INVALID, "too many queries in one call");
+  MainArgs ma = main_args(cb, p, cache, max_seq_len, scale);
+  ma.out = out;
+  ma.q_start = q_start;
+  ma.q = q;
+  ma.q_f32 = q_dtype == TQ_DTYPE_F32 ? 1 : 0;
+  ma.r_hi = p->r_hi;
+  ma.r_lo = p->r_lo;
+  ma.m_hi = cb->cfg.k_qjl ? p->m_hi : nullptr;
+  ma.m_lo = cb->cfg.k_qjl ? p->m_lo : nullptr;
+  ma.T_q = T_q;
+  ma.NG = static_cast<int>(NG);
+  ma.n_slices = 1;
+  ma.mgroup = 1;
+  const ProfileEvents& pe = profile_events();
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (pe.attend_start && pe.attend_stop) {
+    e0 = reinterpret_cast<hipEvent_t>(pe.attend_start);
+    e1 = reinterpret_cast<hipEvent_t>(pe.attend_stop);
+  }
+  const hipError_t e =
+      dispatch_main(ma, cb->cfg, G, 1, cache->B, true, reinterpret_cast<hipStream_t>(hip_stream), e0, e1);
+  if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("prefill attention launch: ") + hipGetErrorString(e));
+  return TQ_OK;
 }

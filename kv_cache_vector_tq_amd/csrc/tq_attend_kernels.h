@@ -47,13 +47,24 @@ struct MainArgs {
   // 1/sqrt(d) scales the key-code term of the scores and the unrotated outputs
   int one_pass;
   float rot_scale;
+  // prefill (causal attention of a prompt's queries): query t of row b sits at position
+  // q_start[b] + t and attends keys 0 .. q_start[b] + t; units of 16 / G consecutive queries
+  // times the G q-heads of a kv-head, NG units per (row, kv-head); the kernel rotates its
+  // queries itself (q [B][Hq][T_q][128], q_f32) and writes out [B][Hq][T_q][128]
+  const int32_t* q_start;
+  const void* q;
+  const uint16_t* r_hi;  // R_hi, R_lo, M_hi, M_lo (query rotation)
+  const uint16_t* r_lo;
+  const uint16_t* m_hi;
+  const uint16_t* m_lo;
+  int q_f32, T_q, NG;
 };
 
 // Launches the attention kernel for key code width KB (k_qjl selects the sign sketch), value
 // width vb and group size G; defined in tq_attend_k<KB>.hip.
 #define TQ_ATTN_DISPATCH(KB)                                                                       \
-  hipError_t dispatch_k##KB(const MainArgs& a, bool qjl, int vb, int G, int n_slices, int B, hipStream_t s, \
-                            hipEvent_t e0, hipEvent_t e1)
+  hipError_t dispatch_k##KB(const MainArgs& a, bool qjl, int vb, int G, int n_slices, int B, bool pre,          \
+                            hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 TQ_ATTN_DISPATCH(0);
 TQ_ATTN_DISPATCH(1);
 TQ_ATTN_DISPATCH(2);
@@ -344,28 +355,50 @@ struct MainCfg {
 };
 
 // Streams the 64-key blocks of one slice.  SCORES: also write the logits (parity runs).
-template <int KB, bool QJL, int VB, int G, bool SCORES>
+// PRE: prefill - every lane column class is its own query (GC = max(8, G) columns: GC / G
+// consecutive positions times the G q-heads), each with its causal limit; one workgroup per
+// unit, whose 8 waves split the unit's blocks; queries are rotated in the kernel; outputs are
+// written directly.  (Eight columns rather than sixteen keep the hi and lo query terms in the
+// columns of one accumulator, which halves the query operands held in registers.)
+template <int KB, bool QJL, int VB, int G, bool SCORES, bool PRE>
 __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
-  using C = MainCfg<KB, QJL, VB, G>;
+  constexpr int GC = PRE ? (G > 8 ? G : 8) : G;  // query columns per unit
+  constexpr int QPG = GC / G;                     // prefill: query positions per unit
+  using C = MainCfg<KB, QJL, VB, GC>;
   constexpr int TPD = C::TPD, NSETS = C::NSETS;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
   constexpr int KBT = KB > 0 ? KB : 1;  // key code width of the (unused when KB = 0) key table
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int col = lane & 15, g = lane >> 4;
-  const int tcls = col / G;   // which tile of a set this lane's column belongs to
-  const int hh = col % G;     // q-head within the group
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int tcls = col / GC;   // which tile of a set this lane's column belongs to
+  const int hh = col % GC;     // query column within the unit
   const int Hq = a.Hkv * G;
-  const int64_t bh = (int64_t)b * a.Hkv + kvh;
+  const int b = blockIdx.z;
+  // decode: unit (b, kv-head blockIdx.y), slice blockIdx.x; prefill: unit blockIdx.x = kv-head
+  // NG + (NG - 1 - query group) (the longest causal ranges start first)
+  const int kvh = PRE ? static_cast<int>(blockIdx.x) / a.NG : static_cast<int>(blockIdx.y);
+  const int qgrp = PRE ? a.NG - 1 - static_cast<int>(blockIdx.x) % a.NG : 0;
+  const int64_t cu = (int64_t)b * a.Hkv + kvh;           // (row, kv-head) of the cache
+  const int64_t bh = PRE ? cu * a.NG + qgrp : cu;         // unit of the partial records
   const int nblk_cap = a.T_cap / 64;
 
-  int seq = a.seq_len[b];
-  seq = seq < 1 ? 1 : (seq > a.max_seq_len ? a.max_seq_len : seq);
+  int seq, lim = 0;
+  if constexpr (PRE) {
+    const int qs = max(a.q_start[b], 0);
+    const int t_col = qgrp * QPG + hh / G;  // the lane column's query position in the unit
+    const int t_last = min(a.T_q, qgrp * QPG + QPG) - 1;
+    seq = min(qs + t_last + 1, a.max_seq_len);
+    lim = t_col < a.T_q ? min(qs + t_col + 1, a.max_seq_len) : 0;  // keys 0 .. lim - 1 visible
+  } else {
+    seq = a.seq_len[b];
+    seq = seq < 1 ? 1 : (seq > a.max_seq_len ? a.max_seq_len : seq);
+  }
   const int nblk = (seq + 63) / 64;
-  const int slice = blockIdx.x * NW + wave;
-  const int blk_begin = slice * a.blocks_per_wave;
-  const int blk_end = min(blk_begin + a.blocks_per_wave, nblk);
+  const int bpw = PRE ? (nblk + NW - 1) / NW : a.blocks_per_wave;
+  const int slice = PRE ? wave : static_cast<int>(blockIdx.x) * NW + wave;
+  const int blk_begin = slice * bpw;
+  const int blk_end = min(blk_begin + bpw, nblk);
 
   // online softmax per lane column: m_run (log2 domain), l_run = sum 2^(lg - m_run);
   // acc = sum P' V with P' = 2^(lg - m_run) nv / s_run and s_run >= every such product
@@ -384,9 +417,9 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   };
   auto load_block = [&](int blk, Blk& d) {
     if constexpr (KB > 0)
-      load_dwords<4 * KB>(d.kd, a.k_codes + (bh * nblk_cap + blk) * (1024 * KB) + lane * 16 * KB);
-    if constexpr (QJL) load_dwords<4>(d.sd, a.k_signs + (bh * nblk_cap + blk) * 1024 + lane * 16);
-    load_dwords<4 * VB>(d.vd, a.v_codes + (bh * nblk_cap + blk) * (1024 * VB) + lane * 16 * VB);
+      load_dwords<4 * KB>(d.kd, a.k_codes + (cu * nblk_cap + blk) * (1024 * KB) + lane * 16 * KB);
+    if constexpr (QJL) load_dwords<4>(d.sd, a.k_signs + (cu * nblk_cap + blk) * 1024 + lane * 16);
+    load_dwords<4 * VB>(d.vd, a.v_codes + (cu * nblk_cap + blk) * (1024 * VB) + lane * 16 * VB);
   };
   // Norms of the lane's kept keys (set s: tile s TPD + tcls, rows 4 g .. 4 g + 3).
   struct Norms {
@@ -395,17 +428,17 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   auto load_norms = [&](int blk, Norms& d) {
 #pragma unroll
     for (int s = 0; s < NSETS; ++s) {
-      const int64_t tok = bh * a.T_cap + blk * 64 + 16 * (s * TPD + tcls) + 4 * g;
+      const int64_t tok = cu * a.T_cap + blk * 64 + 16 * (s * TPD + tcls) + 4 * g;
       d.kn[s] = *reinterpret_cast<const f32x4*>(a.k_norm + tok);
       if constexpr (QJL && KB > 0) d.kr[s] = *reinterpret_cast<const f32x4*>(a.k_rnorm + tok);
       d.vn[s] = *reinterpret_cast<const f32x4*>(a.v_norm + tok);
     }
   };
-  constexpr int QWORDS = G * QREC / 4;
-  constexpr int QPT = (QWORDS + NT - 1) / NT;
+  constexpr int QWORDS = GC * QREC / 4;
+  constexpr int QPT = PRE ? 1 : (QWORDS + NT - 1) / NT;
   float* const qst = reinterpret_cast<float*>(smem + C::TABLES);
   f32x4 qw[QPT];
-  {
+  if constexpr (!PRE) {
     const float* qsrc = a.qrec + ((int64_t)b * Hq + kvh * G) * QREC;
 #pragma unroll
     for (int k = 0; k < QPT; ++k) qw[k] = *reinterpret_cast<const f32x4*>(qsrc + 4 * min(tid + k * NT, QWORDS - 1));
@@ -422,9 +455,20 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   if constexpr (KB > 0) build_table<KBT, false>(smem + C::KOFF, a.k_cent, tid);
   if constexpr (QJL) build_table<1, true>(smem + C::SOFF, nullptr, tid);
   if constexpr (!C::SHARED) build_table<VB, false>(smem + C::VOFF, a.v_cent, tid);
+  if constexpr (PRE) {
+    // waves 0..3 rotate the unit's 16 queries, 32 output coordinates each, into the records
+    if (wave < 4) {
+      const int cq = col % GC;  // lanes of columns >= GC rotate a copy (not stored)
+      const int t = qgrp * QPG + cq / G;
+      const int64_t qrow = ((int64_t)b * Hq + kvh * G + cq % G) * a.T_q + min(t, a.T_q - 1);
+      rotate_queries<QJL>(a.q, a.q_f32 != 0, qrow, t < a.T_q, a.one_pass, a.r_hi, a.r_lo, a.m_hi, a.m_lo, qst,
+                          GC, wave, lane);
+    }
+  } else {
 #pragma unroll
-  for (int k = 0; k < QPT; ++k)
-    if (tid + k * NT < QWORDS) *reinterpret_cast<f32x4*>(qst + 4 * (tid + k * NT)) = qw[k];
+    for (int k = 0; k < QPT; ++k)
+      if (tid + k * NT < QWORDS) *reinterpret_cast<f32x4*>(qst + 4 * (tid + k * NT)) = qw[k];
+  }
   __syncthreads();  // tables and query records ready
   // Score operands.  For q-head hh = col % G: x1 = q1 c1 and x2 = q2 c2 with the constant factors
   // of the score folded in (c1 = log2(e) scale / sqrt(d) / k_scale (/ sqrt(d) in one-pass
@@ -436,7 +480,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   // k-block kb, coordinates 32 g + 8 kb + e of the term of its part k = col / G in each
   // accumulator (zero in the code operand for sign terms and the other way round); u1 and u2
   // undo the two scalings.
-  const int part = col / G;
+  const int part = col / GC;
   f16x8 bc[C::NA][4], bsg[C::NA][4];
   float u1, u2;
   {
@@ -482,18 +526,17 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
         const float x1 = qv1[2 * kb + j / 4][j % 4] * s1, x2 = qv2[2 * kb + j / 4][j % 4] * s2;
         const _Float16 h1 = static_cast<_Float16>(x1), l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
         const _Float16 h2 = static_cast<_Float16>(x2), l2 = static_cast<_Float16>(x2 - static_cast<float>(h2));
-#pragma unroll
-        for (int ac = 0; ac < C::NA; ++ac) {
-          bc[ac][kb][j] = kd[ac] == 0 ? h1 : (kd[ac] == 1 ? l1 : z16);
-          bsg[ac][kb][j] = kd[ac] == 2 ? h2 : (kd[ac] == 3 ? l2 : z16);
-        }
+        static_for<0, C::NA>([&](auto A_) {
+          constexpr int ac = decltype(A_)::value;
+          // operands only for the accumulators that take that kind of term
+          if constexpr (C::has_c(ac)) bc[ac][kb][j] = kd[ac] == 0 ? h1 : (kd[ac] == 1 ? l1 : z16);
+          if constexpr (C::has_s(ac)) bsg[ac][kb][j] = kd[ac] == 2 ? h2 : (kd[ac] == 3 ? l2 : z16);
+        });
       }
   }
 
-  for (int blk = blk_begin; blk < blk_end; ++blk) {
-    Norms nrm;
-    load_norms(blk, nrm);
-    load_block(min(blk + 1, blk_end - 1), nxt);
+  // One block: scores, online softmax, value sums.  `d` holds the block's codes, `nrm` its norms.
+  auto process = [&](const Blk& cur, const Norms& nrm, int blk) {
 
     // ---- scores: tile t = keys 16 t .. 16 t + 15 of the block.  Per accumulator, the code and
     // sign MFMAs (operands zero outside their own terms' columns) sum into one register set.
@@ -527,14 +570,14 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
       if constexpr (C::MIXED) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = v[0][i] + row_ror<2 * G>(v[0][i]);
-          q[i] = row_ror<G>(p[i]);
+          p[i] = v[0][i] + row_ror<2 * GC>(v[0][i]);
+          q[i] = row_ror<GC>(p[i]);
         }
       } else if constexpr (C::NP >= 2) {  // NA = 1 (one kind of term) or 2 (C, S): hi, lo parts
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = v[0][i] + row_ror<G>(v[0][i]);
-          if constexpr (C::NA == 2) q[i] = v[1][i] + row_ror<G>(v[1][i]);
+          p[i] = v[0][i] + row_ror<GC>(v[0][i]);
+          if constexpr (C::NA == 2) q[i] = v[1][i] + row_ror<GC>(v[1][i]);
         }
       } else {  // G = 16: one term per accumulator, in lane order C hi, C lo, S hi, S lo
         p = v[0] + v[1];
@@ -575,7 +618,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
           sc = cp[s][i] * (KB > 0 ? u1 : u2);
         }
         const float l2 = nrm.kn[s][i] * sc;
-        const bool valid = key < seq;
+        const bool valid = key < (PRE ? lim : seq);
         if constexpr (SCORES) {
           if (valid) a.scores_out[((int64_t)b * Hq + kvh * G + hh) * a.T_cap + key] = l2 * (1.0f / LOG2E);
         }
@@ -633,7 +676,21 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
         acc[mt] = mfma_f16(av, bp, acc[mt]);
       });
     });
-    cur = nxt;
+  };
+  // Two blocks per iteration with the buffers swapping roles, so that the prefetched block never
+  // has to be copied into the current one.
+  for (int blk = blk_begin; blk < blk_end; blk += 2) {
+    {
+      Norms nrm;
+      load_norms(blk, nrm);
+      load_block(min(blk + 1, blk_end - 1), nxt);
+      process(cur, nrm, blk);
+    }
+    if (blk + 1 >= blk_end) break;  // uniform
+    Norms nrm;
+    load_norms(blk + 1, nrm);
+    load_block(min(blk + 2, blk_end - 1), cur);
+    process(nxt, nrm, blk + 1);
   }
 
   // Operands of R_eff^T for the unrotation, in case this workgroup becomes a merger: rows
@@ -686,46 +743,61 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   __syncthreads();  // the handed-over records are consumed
   if (wave < 4) put_record(wave * 16 + col);
   __syncthreads();
-  // record r = 16 w + c G + h belongs to q-head h; wave 0 finds each head's maximum and the
-  // record weights over the lanes with the same h (xor offsets that keep r mod G)
+  // record r = 16 w + c GC + h belongs to query column h; wave 0 finds each column's maximum and
+  // the record weights over the lanes with the same h (xor offsets that keep r mod GC)
   if (tid < 64) {
     const float* rec = ep->rec[tid];
     const float m = rec[128];
     float M = m;
 #pragma unroll
-    for (int o = G; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    for (int o = GC; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
     const float e = exp2f(m - M);
     ep->w64[tid] = rec[130] * e;
     float l = rec[129] * e;
 #pragma unroll
-    for (int o = G; o < 64; o <<= 1) l += __shfl_xor(l, o);
-    if (tid < G) st_dev2(a.part + ((bh * G + tid) * a.n_slices + blockIdx.x) * PREC + 128, M, l);
+    for (int o = GC; o < 64; o <<= 1) l += __shfl_xor(l, o);
+    if (tid < GC) {
+      if constexpr (PRE) {
+        ep->st[tid][0] = M;
+        ep->st[tid][1] = l;
+      } else {
+        st_dev2(a.part + ((bh * GC + tid) * a.n_slices + blockIdx.x) * PREC + 128, M, l);
+      }
+    }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * D / 2; idx += NT) {
+  // prefill: the weighted sums of the workgroup are the unit's result (amat aliases no record)
+  for (int idx = tid; idx < GC * D / 2; idx += NT) {
     const int h = idx / (D / 2), j = 2 * (idx % (D / 2));
     float A0 = 0.f, A1 = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
       for (int c = 0; c < TPD; ++c) {
-        const int r = 16 * w + c * G + h;
+        const int r = 16 * w + c * GC + h;
         A0 = fmaf(ep->rec[r][j], ep->w64[r], A0);
         A1 = fmaf(ep->rec[r][j + 1], ep->w64[r], A1);
       }
-    st_dev2(a.part + ((bh * G + h) * a.n_slices + blockIdx.x) * PREC + j, A0, A1);
+    if constexpr (PRE) {
+      ep->amat[h][j] = A0;
+      ep->amat[h][j + 1] = A1;
+    } else {
+      st_dev2(a.part + ((bh * GC + h) * a.n_slices + blockIdx.x) * PREC + j, A0, A1);
+    }
   }
 
   // ---- merge over the slices: the last workgroup of each group of MGROUP slices merges the
   // group and applies R_eff^T, the last group merger merges the groups ---------------------
-  const int ns = a.n_slices;
+  const int ns = PRE ? 1 : a.n_slices;
   const int mgroup = a.mgroup;
-  const int ngrp = (ns + mgroup - 1) / mgroup;
-  const int grp = blockIdx.x / mgroup;
+  const int ngrp = PRE ? 1 : (ns + mgroup - 1) / mgroup;
+  const int grp = PRE ? 0 : static_cast<int>(blockIdx.x) / mgroup;
   drain_stores();
   __syncthreads();
-  unsigned* const cnt_top = a.cnt + bh * CNT_PER_UNIT + MAX_GROUPS;
-  if (tid == 0) {
+  unsigned* const cnt_top = PRE ? nullptr : a.cnt + bh * CNT_PER_UNIT + MAX_GROUPS;
+  if constexpr (PRE) {
+    // the workgroup holds the whole unit: unrotate and write its outputs below
+  } else if (tid == 0) {
     // counters start at zero (the query rotation launch zeroes them before every call)
     int stage = 0;
     unsigned* cnt = ngrp == 1 ? cnt_top : a.cnt + bh * CNT_PER_UNIT + grp;
@@ -734,12 +806,12 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
     ep->stage = stage;
   }
   __syncthreads();
-  if (ep->stage == 0) return;
+  if (!PRE && ep->stage == 0) return;
   // This workgroup merges: it applies R_eff^T to what it merged (the unrotation is linear, so
   // merging unrotated group results is the same as unrotating the merge).  Merge the slices of
   // this group (or all slices with a single group) into ep->amat, ep->st; wave w takes q-heads
   // w, w + 4, ...
-  {
+  if constexpr (!PRE) {
     const int first = ngrp == 1 ? 0 : mgroup * grp;
     const int count = ngrp == 1 ? ns : min(mgroup, ns - mgroup * grp);
     for (int h = wave; h < G; h += NW) {
@@ -784,11 +856,19 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * g + i;
-      if (h >= G) continue;
+      if (h >= GC) continue;
       const float L = ep->st[h][1];
       // value centroids enter as c v_scale / sqrt(d)
       const float f = L > 0.f ? INV_SQRT_D * a.v_unscale * a.rot_scale / L : 0.f;
-      a.out[(bh * G + h) * D + 16 * wave + col] = u[i] * f;
+      float* dst;
+      if constexpr (PRE) {  // column h: query qgrp QPG + h / G of q-head kvh G + h % G
+        const int t = qgrp * QPG + h / G;
+        if (t >= a.T_q) continue;
+        dst = a.out + (((int64_t)b * Hq + kvh * G + h % G) * a.T_q + t) * D;
+      } else {
+        dst = a.out + (bh * G + h) * D;
+      }
+      dst[16 * wave + col] = u[i] * f;
     }
     return;
   }
@@ -820,34 +900,40 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
 }
 
 template <int KB, bool QJL, int VB, int G>
-hipError_t launch_main(const MainArgs& a, int n_slices, int B, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+hipError_t launch_main(const MainArgs& a, int n_slices, int B, bool pre, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   static_assert(MainCfg<KB, QJL, VB, G>::LDS <= 64 * 1024, "attention LDS budget");
-  auto kern = a.scores_out != nullptr ? attend_kernel<KB, QJL, VB, G, true> : attend_kernel<KB, QJL, VB, G, false>;
+  static_assert(MainCfg<KB, QJL, VB, (G > 8 ? G : 8)>::LDS <= 64 * 1024, "prefill LDS budget");
+  auto kern = pre ? attend_kernel<KB, QJL, VB, G, false, true>
+                  : (a.scores_out != nullptr ? attend_kernel<KB, QJL, VB, G, true, false>
+                                             : attend_kernel<KB, QJL, VB, G, false, false>);
+  // decode: (slices, kv-heads, rows); prefill: (kv-heads x query groups, 1, rows)
+  const dim3 grid = pre ? dim3(a.Hkv * a.NG, 1, B) : dim3(n_slices, a.Hkv, B);
   if (e0 != nullptr || e1 != nullptr)
-    hipExtLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(NT), 0, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL(kern, grid, dim3(NT), 0, s, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL(kern, dim3(n_slices, a.Hkv, B), dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
 template <int KB, bool QJL, int VB>
-hipError_t dispatch_g(const MainArgs& a, int G, int n_slices, int B, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+hipError_t dispatch_g(const MainArgs& a, int G, int n_slices, int B, bool pre, hipStream_t s, hipEvent_t e0,
+                      hipEvent_t e1) {
   switch (G) {
-    case 4: return launch_main<KB, QJL, VB, 4>(a, n_slices, B, s, e0, e1);
-    case 8: return launch_main<KB, QJL, VB, 8>(a, n_slices, B, s, e0, e1);
-    case 16: return launch_main<KB, QJL, VB, 16>(a, n_slices, B, s, e0, e1);
+    case 4: return launch_main<KB, QJL, VB, 4>(a, n_slices, B, pre, s, e0, e1);
+    case 8: return launch_main<KB, QJL, VB, 8>(a, n_slices, B, pre, s, e0, e1);
+    case 16: return launch_main<KB, QJL, VB, 16>(a, n_slices, B, pre, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
 template <int KB, bool QJL>
-hipError_t dispatch_v(const MainArgs& a, int VB, int G, int n_slices, int B, hipStream_t s, hipEvent_t e0,
+hipError_t dispatch_v(const MainArgs& a, int VB, int G, int n_slices, int B, bool pre, hipStream_t s, hipEvent_t e0,
                       hipEvent_t e1) {
   switch (VB) {
-    case 1: return dispatch_g<KB, QJL, 1>(a, G, n_slices, B, s, e0, e1);
-    case 2: return dispatch_g<KB, QJL, 2>(a, G, n_slices, B, s, e0, e1);
-    case 3: return dispatch_g<KB, QJL, 3>(a, G, n_slices, B, s, e0, e1);
-    case 4: return dispatch_g<KB, QJL, 4>(a, G, n_slices, B, s, e0, e1);
+    case 1: return dispatch_g<KB, QJL, 1>(a, G, n_slices, B, pre, s, e0, e1);
+    case 2: return dispatch_g<KB, QJL, 2>(a, G, n_slices, B, pre, s, e0, e1);
+    case 3: return dispatch_g<KB, QJL, 3>(a, G, n_slices, B, pre, s, e0, e1);
+    case 4: return dispatch_g<KB, QJL, 4>(a, G, n_slices, B, pre, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }

@@ -26,12 +26,14 @@ template <bool QJL>
 struct QOperands {
   bf16x8 rh[2][4], rl[2][4], mh[QJL ? 2 : 1][4], ml[QJL ? 2 : 1][4];
   u32x4 raw[8];
-  bool valid;  // col < G
+  bool valid;  // the lane's column holds a query
 };
 
+// qrow: row (in units of 128 elements) of q that holds the lane's query; valid: whether the
+// lane's column holds a query at all (the operand is zero otherwise).
 template <bool QJL>
-__device__ __forceinline__ void load_query_operands(QOperands<QJL>& o, const void* q, bool q_f32, int64_t head0,
-                                                    int G, const uint16_t* r_hi, const uint16_t* r_lo,
+__device__ __forceinline__ void load_query_operands(QOperands<QJL>& o, const void* q, bool q_f32, int64_t qrow,
+                                                    bool valid, const uint16_t* r_hi, const uint16_t* r_lo,
                                                     const uint16_t* m_hi, const uint16_t* m_lo, int wave, int col,
                                                     int g) {
 #pragma unroll
@@ -50,8 +52,8 @@ __device__ __forceinline__ void load_query_operands(QOperands<QJL>& o, const voi
   // unconditional loads from clamped, in-bounds addresses (no branch that would force an
   // early wait); lanes of rows >= G and the unused chunks of a bf16 query are masked on use
   const int esz = q_f32 ? 4 : 2;
-  o.valid = col < G;
-  const uint8_t* base = reinterpret_cast<const uint8_t*>(q) + ((head0 + (o.valid ? col : 0)) * D + 32 * g) * esz;
+  o.valid = valid;
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(q) + (qrow * D + 32 * g) * esz;
   const int last = q_f32 ? 7 : 3;  // last 16-byte chunk of this lane's 32 coordinates
 #pragma unroll
   for (int i = 0; i < 8; ++i) o.raw[i] = *reinterpret_cast<const u32x4*>(base + 16 * min(i, last));
@@ -120,32 +122,44 @@ struct PrologueArgs {
   int one_pass;  // Hadamard mode: q1 = q r_hi (one pass; the record holds sqrt(d) R q)
 };
 
+// Output coordinates 32 tile .. 32 tile + 31 of the records of up to 16 queries (one per lane
+// column: row qrow of q, `valid` as in load_query_operands); record h (q1[128] then q2[128]) at
+// recs + h QREC, for h < nrec.  recs may be global or LDS memory.
 template <bool QJL>
-__device__ __forceinline__ void rotate_query_tile(const PrologueArgs& a, int unit, int tile, int lane) {
+__device__ __forceinline__ void rotate_queries(const void* q, bool q_f32, int64_t qrow, bool valid, int one_pass,
+                                               const uint16_t* r_hi, const uint16_t* r_lo, const uint16_t* m_hi,
+                                               const uint16_t* m_lo, float* recs, int nrec, int tile, int lane) {
   const int col = lane & 15, g = lane >> 4;
-  const int G = a.G;
-  const int64_t head0 = static_cast<int64_t>(unit) * G;
-  if (tile == 0 && lane < a.cnt_per_unit) a.cnt[static_cast<int64_t>(unit) * a.cnt_per_unit + lane] = 0u;
   QOperands<QJL> qo;
-  load_query_operands<QJL>(qo, a.q, a.q_f32 != 0, head0, G, a.r_hi, a.r_lo, a.m_hi, a.m_lo, tile, col, g);
+  load_query_operands<QJL>(qo, q, q_f32, qrow, valid, r_hi, r_lo, m_hi, m_lo, tile, col, g);
   f32x4 d1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   f32x4 d2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  if (a.one_pass)
-    rotate_products<QJL, true>(qo, a.q_f32 != 0, d1, d2);
+  if (one_pass)
+    rotate_products<QJL, true>(qo, q_f32, d1, d2);
   else
-    rotate_products<QJL, false>(qo, a.q_f32 != 0, d1, d2);
-  // D layout: lane (col, g) holds head 4 g + i, output coordinate 32 tile + 16 nt + col
+    rotate_products<QJL, false>(qo, q_f32, d1, d2);
+  // D layout: lane (col, g) holds query 4 g + i, output coordinate 32 tile + 16 nt + col
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * g + i;
-    if (h >= G) continue;
-    float* rec = a.qrec + (head0 + h) * QREC;
+    if (h >= nrec) continue;
+    float* rec = recs + h * QREC;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       rec[32 * tile + 16 * nt + col] = d1[nt][i];
       rec[D + 32 * tile + 16 * nt + col] = QJL ? d2[nt][i] : 0.f;
     }
   }
+}
+
+template <bool QJL>
+__device__ __forceinline__ void rotate_query_tile(const PrologueArgs& a, int unit, int tile, int lane) {
+  const int col = lane & 15;
+  const int G = a.G;
+  const int64_t head0 = static_cast<int64_t>(unit) * G;
+  if (tile == 0 && lane < a.cnt_per_unit) a.cnt[static_cast<int64_t>(unit) * a.cnt_per_unit + lane] = 0u;
+  rotate_queries<QJL>(a.q, a.q_f32 != 0, head0 + (col < G ? col : 0), col < G, a.one_pass, a.r_hi, a.r_lo, a.m_hi,
+                      a.m_lo, a.qrec + head0 * QREC, G, tile, lane);
 }
 
 }  // namespace

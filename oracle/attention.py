@@ -68,3 +68,35 @@ def attend(q, R_eff, k, v, k_centroids, v_centroids, S_b, scale=None, T=None):
     V = np.asarray(v["n"], dtype=np.float64)[:T, None] * cv[np.asarray(v["idx"])[:T].astype(np.int64)] / math.sqrt(d)
     o_rot = p @ V
     return logits, o_rot @ R_eff
+
+
+def attend_prefill(q, R_eff, k, v, k_centroids, v_centroids, S_b, positions, scale=None):
+    """Causal (prefill) attention of a prompt's queries straight from the packed codes.
+
+    Pages: "Когда в марте 2026 года Google опубликовала статью..." (ai-news.ru), paragraph
+    "Теперь про цифры" (quantization overhead at prefill) and "Google TurboQuant простыми
+    словами", section "Как попробовать TurboQuant прямо сейчас" (prefill throughput with the
+    compressed cache): the prompt's keys and values are quantized on write and its queries
+    attend the compressed cache.  The plainest reading of attention over a prompt is causal:
+    the query at absolute position p attends keys 0..p, with the decode score of each key.
+
+    q          [H, Tq, d] queries (all of one kv-head)
+    positions  [Tq] absolute positions of the queries (key i is visible when i <= position)
+    Returns (logits [H, Tq, T] with -inf at masked keys, out [H, Tq, d]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    H, Tq, d = q.shape
+    positions = np.asarray(positions, dtype=np.int64)
+    T = int(positions.max()) + 1
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    kk = {key: np.asarray(val)[:T] for key, val in k.items()}
+    logits = scale * key_scores(q.reshape(H * Tq, d), R_eff, kk, k_centroids, S_b).reshape(H, Tq, T)
+    visible = np.arange(T)[None, None, :] <= positions[None, :, None]
+    logits = np.where(visible, logits, -np.inf)
+    mx = logits.max(axis=2, keepdims=True)
+    w = np.exp(logits - mx)
+    p = w / w.sum(axis=2, keepdims=True)
+    cv = np.asarray(v_centroids, dtype=np.float32).astype(np.float64)
+    V = np.asarray(v["n"], dtype=np.float64)[:T, None] * cv[np.asarray(v["idx"])[:T].astype(np.int64)] / math.sqrt(d)
+    o_rot = p @ V
+    return logits, o_rot @ R_eff

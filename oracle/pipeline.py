@@ -12,7 +12,7 @@ import math
 import numpy as np
 
 from . import layout
-from .attention import attend, key_scores
+from .attention import attend, attend_prefill, key_scores
 from .lloyd_max import codebook_f32
 from .params import build_params
 from .quantize import quantize
@@ -71,6 +71,9 @@ class Oracle:
     # ---- decode attention ---------------------------------------------------
     def attend(self, q, k, v, T=None, scale=None):
         return attend(q, self.R_eff, k, v, self.kc, self.vc, self.S_b, scale=scale, T=T)
+
+    def attend_prefill(self, q, k, v, positions, scale=None):
+        return attend_prefill(q, self.R_eff, k, v, self.kc, self.vc, self.S_b, positions, scale=scale)
 
     def scores(self, q, k):
         return key_scores(q, self.R_eff, k, self.kc, self.S_b) / math.sqrt(self.d)

@@ -541,3 +541,73 @@ def test_deterministic():
         if a is not None:
             np.testing.assert_array_equal(a, outs[1][0][name])
     np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+def _prefill_case(preset, B, Hkv, G, T_cap, T_q, starts, dtype, seed, check_units=None, sample=None):
+    """Bulk-quantize T_cap tokens, run causal prefill attention of T_q queries per row starting at
+    position starts[b], and compare the checked (row, kv-head) units with the oracle on the
+    GPU-written cache (every query, or the query indices in `sample`)."""
+    cb, dp, cache = _setup(preset, B, Hkv, T_cap)
+    rng = np.random.default_rng(seed)
+    K = rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32) * 2
+    V = rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32)
+    Q = rng.standard_normal((B, Hkv * G, T_q, 128)).astype(np.float32)
+    if dtype == "bf16":
+        K, V, Q = wl.round_to_bf16(K), wl.round_to_bf16(V), wl.round_to_bf16(Q)
+    say("prefill", preset, B, Hkv, G, T_cap, T_q, starts, "quantize")
+    tq.tq_quantize_kv(cb, dp, cache, H.to_device(K, dtype), H.to_device(V, dtype),
+                      torch.zeros(B, dtype=torch.int32, device="cuda"))
+    del K, V
+    say("prefill", preset, "attend")
+    out = tq.tq_attend_prefill(cb, dp, cache, H.to_device(Q, dtype), torch.tensor(starts, dtype=torch.int32,
+                                                                                  device="cuda"), T_cap)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    orc = H.make_oracle(preset)
+    units = check_units or [(b, h) for b in range(B) for h in range(Hkv)]
+    idx = np.arange(T_q) if sample is None else np.asarray(sample)
+    worst = 0.0
+    for b, h in units:
+        hc = {n: (None if t is None else t[b:b + 1, h:h + 1].cpu().numpy()) for n, t in cache.tensors().items()}
+        pos = starts[b] + idx
+        T = int(pos.max()) + 1
+        kg = H.unpack_keys(orc, hc, 0, 0, T)
+        vg = H.unpack_values(orc, hc, 0, 0, T)
+        hs = slice(h * G, (h + 1) * G)
+        _, ref = orc.attend_prefill(Q[b, hs][:, idx].astype(np.float64), kg, vg, pos)
+        got = out[b, hs][:, idx]
+        d = np.abs(got - ref).max(axis=2)
+        mag = np.abs(ref).max(axis=2)
+        err = float((d / np.maximum(mag, 1e-300)).max())
+        worst = max(worst, err)
+        H.record("out_err_vs_max", err)
+        assert np.all(d <= H.SCORE_TOL * mag), ("prefill outputs", (b, h), err)
+    say("prefill", preset, "max rel err", worst)
+
+
+@pytest.mark.parametrize("preset,G,dtype,T_q,starts", [("turbo3", 4, "bf16", 300, [0, 100]),
+                                                       ("turbo4", 8, "f32", 257, [0, 37]),
+                                                       ("qjl1", 16, "bf16", 130, [5, 0]),
+                                                       ((2, 0, 3), 4, "bf16", 70, [1, 64]),
+                                                       ("turbo3", 4, "bf16", 1, [0, 400])])
+def test_prefill_matches_oracle(preset, G, dtype, T_q, starts):
+    """Causal prefill attention over the packed cache (tq_attend_prefill): ragged prompt lengths,
+    prompts that start after an earlier context, a single query, every query column compared
+    with the oracle's causal attention on the GPU-written cache."""
+    _prefill_case(preset, 2, 2, G, 512, T_q, starts, dtype, seed=60 + T_q)
+
+
+def test_prefill_4k_prompt():
+    """A 4096-token prompt at the Llama-3.1-8B layer shape (32 q-heads, 8 kv-heads), every query of
+    two kv-heads checked."""
+    _prefill_case("turbo3", 1, 8, 4, 4096, 4096, [0], "bf16", seed=71, check_units=[(0, 0), (0, 7)])
+
+
+def test_prefill_32k_prompt_sampled():
+    """A 32768-token prompt at the Llama-3.1-8B layer shape, queries sampled (first and last 64,
+    block edges and 200 random positions) for two kv-heads."""
+    T = 32768
+    rng = np.random.default_rng(5)
+    sample = np.unique(np.concatenate([np.arange(64), np.arange(T - 64, T), [4095, 4096, 16383, 16384],
+                                       rng.integers(0, T, 200)]))
+    _prefill_case("turbo3", 1, 8, 4, T, T, [0], "bf16", seed=72, check_units=[(0, 0), (0, 5)], sample=sample)

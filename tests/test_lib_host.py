@@ -227,3 +227,32 @@ def test_bf16_baseline_checks():
     small = ctypes.c_size_t(need - 1)
     assert _lib.lib.tq_bf16_attend_decode(*a, 1 << 20, ctypes.byref(small), None) == _lib.TQ_ERR_WORKSPACE
 
+
+
+def _prefill_rc(cb, cache, q=1 << 12, Hq=8, T_q=100, start=1 << 13, max_seq=4096, out=1 << 14, dtype=None,
+                params=None):
+    if params is None:
+        params = _lib.TQDevParams(1 << 15, 1 << 16, 1 << 17, 1 << 18, 1 << 19, 1 << 20, 1 << 21)
+    return _lib.lib.tq_attend_prefill(ctypes.byref(cb.cb), ctypes.byref(params), ctypes.byref(cache.struct), q,
+                                      _lib.TQ_DTYPE_BF16 if dtype is None else dtype, Hq, T_q, start, max_seq, 0.0,
+                                      out, None)
+
+
+def test_prefill_argument_checks():
+    """Every argument error of tq_attend_prefill is detected on the host (no launch)."""
+    cb = tq.tq_build_codebook(2, 1, 3)
+    cache = _FakeCache(cb, B=2, Hkv=2, T_cap=4096)
+    assert _prefill_rc(cb, cache, q=None) == _lib.TQ_ERR_INVALID
+    assert _prefill_rc(cb, cache, start=None) == _lib.TQ_ERR_INVALID
+    assert _prefill_rc(cb, cache, out=None) == _lib.TQ_ERR_INVALID
+    assert _prefill_rc(cb, cache, q=(1 << 12) + 8) == _lib.TQ_ERR_INVALID     # q not 16-byte aligned
+    assert _prefill_rc(cb, cache, out=(1 << 14) + 2) == _lib.TQ_ERR_INVALID   # out not 4-byte aligned
+    assert _prefill_rc(cb, cache, T_q=0) == _lib.TQ_ERR_INVALID
+    assert _prefill_rc(cb, cache, Hq=7) == _lib.TQ_ERR_INVALID                # not a multiple of Hkv
+    assert _prefill_rc(cb, cache, Hq=6) == _lib.TQ_ERR_UNSUPPORTED            # group of 3
+    assert _prefill_rc(cb, cache, max_seq=0) == _lib.TQ_ERR_INVALID
+    assert _prefill_rc(cb, cache, max_seq=4097) == _lib.TQ_ERR_INVALID
+    assert _prefill_rc(cb, cache, dtype=7) == _lib.TQ_ERR_UNSUPPORTED
+    no_m = _lib.TQDevParams(1 << 15, 1 << 16, 1 << 17, 1 << 18, 1 << 19, None, 1 << 21)
+    assert _prefill_rc(cb, cache, params=no_m) == _lib.TQ_ERR_INVALID         # sketch keys need M
+    assert tq.TQError  # the binding raises on these codes

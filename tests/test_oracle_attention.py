@@ -101,3 +101,44 @@ def test_logits_track_unquantized_logits(preset, min_corr):
     exact = Q @ K.T / math.sqrt(128)
     corr = [np.corrcoef(logits[h], exact[h])[0, 1] for h in range(8)]
     assert min(corr) > min_corr
+
+
+# ---- prefill (causal) attention ---------------------------------------------------------------
+
+@pytest.mark.parametrize("preset", [(2, 1, 3), (3, 1, 4), (0, 1, 3), (2, 0, 3)])
+def test_prefill_matches_dense_masked_attention(preset):
+    # softmax over the visible keys of q . k~ / sqrt(d), written out with an explicit loop over
+    # query positions and the dequantized vectors (independent of the vectorized mask)
+    o, K, V, Q = _setup(preset, 40, 3, seed=5)
+    Qp = np.random.default_rng(6).standard_normal((3, 12, 128))
+    positions = np.array([0, 1, 5, 13, 20, 21, 22, 30, 31, 37, 38, 39])
+    kq, vq = o.quantize_keys(K), o.quantize_values(V)
+    logits, out = o.attend_prefill(Qp, kq, vq, positions)
+    Kd = dequantize(kq, o.R_eff, o.kc, o.S_b)
+    Vd = dequantize(vq, o.R_eff, o.vc, None)
+    for h in range(3):
+        for j, pos in enumerate(positions):
+            s = Qp[h, j] @ Kd[:pos + 1].T / math.sqrt(128)
+            p = np.exp(s - s.max())
+            p /= p.sum()
+            np.testing.assert_allclose(logits[h, j, :pos + 1], s, rtol=1e-12, atol=1e-12 * np.abs(s).max())
+            assert np.all(np.isneginf(logits[h, j, pos + 1:]))
+            np.testing.assert_allclose(out[h, j], p @ Vd[:pos + 1], rtol=1e-11, atol=1e-12 * np.abs(out[h, j]).max())
+
+
+def test_prefill_rows_reduce_to_decode_and_first_value():
+    o, K, V, Q = _setup((2, 1, 3), 64, 4, seed=8)
+    kq, vq = o.quantize_keys(K), o.quantize_values(V)
+    Qp = np.random.default_rng(9).standard_normal((4, 64, 128))
+    _, out = o.attend_prefill(Qp, kq, vq, np.arange(64))
+    # the last query sees every key: decode attention over all 64 keys
+    _, dec = o.attend(Qp[:, -1], kq, vq)
+    np.testing.assert_allclose(out[:, -1], dec, rtol=1e-12, atol=1e-13)
+    # the first query sees only key 0: its value, whatever the query
+    vhat = dequantize(vq, o.R_eff, o.vc, None)[0]
+    for h in range(4):
+        np.testing.assert_allclose(out[h, 0], vhat, rtol=1e-12, atol=1e-13)
+    # a query at position p equals decode attention over keys 0..p
+    for p_ in (7, 31, 50):
+        _, dp = o.attend(Qp[:, p_], kq, vq, T=p_ + 1)
+        np.testing.assert_allclose(out[:, p_], dp, rtol=1e-12, atol=1e-13)
