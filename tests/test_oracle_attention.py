@@ -29,7 +29,7 @@ def _dense(o, Q, kq, vq, scale=None):
     return logits, p @ Vd
 
 
-@pytest.mark.parametrize("preset", [(2, 1, 3), (3, 1, 4), (0, 1, 3), (2, 0, 3)])
+@pytest.mark.parametrize("preset", [(2, 1, 3), (3, 1, 4), (0, 1, 3), (2, 0, 3), (8, 0, 4), (5, 1, 3)])
 @pytest.mark.parametrize("T", [1, 7, 64])
 def test_matches_dense_dequantized_attention(preset, T):
     o, K, V, Q = _setup(preset, T, 4, seed=T)
@@ -91,7 +91,8 @@ def test_packed_cache_round_trip_gives_same_attention():
     np.testing.assert_allclose(o2, o1, rtol=1e-5, atol=1e-6 * np.abs(o1).max())
 
 
-@pytest.mark.parametrize("preset,min_corr", [((3, 1, 4), 0.95), ((2, 1, 3), 0.88), ((2, 0, 3), 0.9)])
+@pytest.mark.parametrize("preset,min_corr", [((3, 1, 4), 0.95), ((2, 1, 3), 0.88), ((2, 0, 3), 0.9),
+                                               ((8, 0, 4), 0.999), ((6, 1, 4), 0.995)])
 def test_logits_track_unquantized_logits(preset, min_corr):
     # Not a pin (the pages give no accuracy figure for a stated workload): a sanity floor
     # on the correlation of the estimated logits with exact fp64 logits on the raw keys.

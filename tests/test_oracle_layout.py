@@ -34,7 +34,7 @@ def test_hand_derived_positions(case):
     np.testing.assert_array_equal(back.astype(np.int64), codes)
 
 
-@pytest.mark.parametrize("kind,bits", [("k", 1), ("k", 2), ("k", 3), ("k", 4), ("s", 1),
+@pytest.mark.parametrize("kind,bits", [("k", 1), ("k", 2), ("k", 3), ("k", 4), ("k", 5), ("k", 7), ("k", 8), ("s", 1),
                                        ("v", 1), ("v", 2), ("v", 3), ("v", 4)])
 @pytest.mark.parametrize("T", [1, 64, 150])
 def test_round_trip(kind, bits, T):
@@ -49,7 +49,7 @@ def test_round_trip(kind, bits, T):
     np.testing.assert_array_equal(back, codes if kind == "s" else codes.astype(np.uint8))
 
 
-@pytest.mark.parametrize("kind,bits", [("k", 2), ("k", 3), ("v", 3), ("v", 4), ("s", 1)])
+@pytest.mark.parametrize("kind,bits", [("k", 2), ("k", 3), ("k", 6), ("k", 8), ("v", 3), ("v", 4), ("s", 1)])
 def test_layout_is_a_bijection(kind, bits):
     # every bit of a full block is used exactly once
     T = 64

@@ -24,7 +24,7 @@ def _figures():
     return out
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_threshold_count_is_nearest_centroid(bits):
     c, t, _ = codebook_f32(bits)
     rng = np.random.default_rng(bits)
@@ -72,7 +72,7 @@ def test_zero_vector():
     assert q["n"][1] == 1.0 and q["gamma"][1] > 0
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 6, 8])
 def test_empirical_mse_on_unit_vectors(bits):
     # Normalized squared error ||x - xhat||^2 / ||x||^2 of random unit vectors (d = 128)
     # through the whole value path: within [-3 %, +0.5 %] of the Gaussian optimum D_b
