@@ -122,6 +122,10 @@ def lloyd_max_gaussian(bits: int, tol: float = 1e-15):
             c = c + delta
             if float(np.max(np.abs(delta))) < NEWTON_TOL:
                 break
+        # N(0,1) is symmetric, so is its quantizer: the fp64 noise of the solve (~1e-13) is
+        # averaged out of the mirror pairs, which puts the middle threshold exactly at 0 (a
+        # zero coordinate then takes code 2^(b-1), as with the narrow tables)
+        c = 0.5 * (c - c[::-1])
     t = 0.5 * (c[:-1] + c[1:])
     return c, t, gaussian_mse(c, t), steps
 

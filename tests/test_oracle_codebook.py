@@ -65,9 +65,9 @@ def test_thresholds_are_midpoints_and_symmetric(bits):
     L = len(c)
     assert np.all(np.diff(c) > 0)
     np.testing.assert_allclose(t, 0.5 * (c[:-1] + c[1:]), rtol=0, atol=0)
-    # the law is symmetric, so is its quantizer (to the fp64 noise of the fixed-point solve)
-    np.testing.assert_allclose(c, -c[::-1], atol=1e-12)
-    assert abs(t[L // 2 - 1]) < 1e-12
+    # the law is symmetric, so is its quantizer, exactly: a zero coordinate takes code L / 2
+    np.testing.assert_array_equal(c, -c[::-1])
+    assert t[L // 2 - 1] == 0.0
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 6, 8])
