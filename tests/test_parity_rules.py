@@ -150,3 +150,46 @@ def test_short_rows_use_the_term_magnitudes():
     H.check_scores(got, logits, 8, mags)
     with pytest.raises(AssertionError, match="short row"):
         H.check_scores(logits + 2.1e-3 * ref, logits, 8, mags)
+
+
+@pytest.mark.parametrize("bits", [1, 3, 4, 6, 8])
+def test_threshold_band_tests_the_neighbouring_thresholds_only(bits):
+    # the band test looks at the two thresholds around z; written out from its definition
+    # (every threshold, one by one) it marks exactly the same elements, including planted
+    # values just inside and just outside the bands
+    from oracle.lloyd_max import codebook_f32
+    from oracle.quantize import threshold_band
+    _, t, _ = codebook_f32(bits)
+    t64 = t.astype(np.float64)
+    rng = np.random.default_rng(bits)
+    z = rng.standard_normal((400, 128)) * 1.5
+    pick = rng.integers(0, len(t64), 20000)
+    z.ravel()[:20000] = t64[pick] * (1 + rng.uniform(-3e-5, 3e-5, 20000)) + rng.uniform(-3e-5, 3e-5, 20000)
+    ref = np.zeros(z.shape, dtype=bool)
+    for tl in t64:
+        ref |= np.abs(z - tl) <= 1e-5 * max(1.0, abs(tl))
+    got = threshold_band(z, t)
+    np.testing.assert_array_equal(got, ref)
+    assert 0 < got.sum() < 20000
+
+
+def test_sign_band_floor():
+    # signs of wide-code keys: the band is 1e-5 max(||r||, ||y|| / 8); a flipped sign whose
+    # |u| exceeds it is still rejected, and for 3-bit keys (||r|| > ||y|| / 8) the floor does
+    # not widen the band
+    o = Oracle(8, 1, 4)
+    x = np.random.default_rng(4).standard_normal((64, 128))
+    ref = o.quantize_keys(x)
+    got = {"n": ref["n"].copy(), "idx": ref["idx"].copy(), "gamma": ref["gamma"].copy(), "sign": ref["sign"].copy()}
+    H.compare_keys(o, x, got, {})
+    u = ref["u"]
+    r_norm = np.linalg.norm(ref["r"], axis=1)
+    assert np.all(r_norm < 1 / 8)  # the floor applies to every row
+    i, j = np.unravel_index(np.argmin(np.where(np.abs(u) > 2e-5 / 8, np.abs(u), np.inf)), u.shape)
+    bad = dict(got, sign=got["sign"].copy())
+    bad["sign"][i, j] = not bad["sign"][i, j]
+    with pytest.raises(AssertionError, match="sign bit mismatch outside the band"):
+        H.compare_keys(o, x, bad, {})
+    o3 = Oracle(2, 1, 3)
+    r3 = o3.quantize_keys(x)
+    assert np.all(np.linalg.norm(r3["r"], axis=1) > 1 / 8)
