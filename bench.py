@@ -34,7 +34,8 @@ HBM_PEAK_GBS = 8000.0
 HEADLINE = ("c3_batch16_t128k", "turbo3")
 # workloads whose 32-layer decode step is timed as well (caches of one layer fit the 256 MB
 # Infinity Cache, so 32 distinct layers are cycled)
-EXTRA_STEPS = [("c2_llama8b_layer_t32k", "turbo3"), ("c2_llama8b_layer_t32k", "turbo4")]
+EXTRA_STEPS = [("c2_llama8b_layer_t32k", "turbo3"), ("c2_llama8b_layer_t32k", "turbo4"),
+               ("c2_llama8b_layer_t32k", "k8v4")]
 OTHER_WORKLOADS = [("c4_llama70b_layer_b8_t128k", "qjl1"), ("c5_moe_attn_t1m", "turbo3"),
                    ("c5_moe_attn_t1m", "turbo4")]
 
@@ -45,7 +46,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE[0])
-    ap.add_argument("--preset", default=HEADLINE[1], choices=["turbo2", "turbo3", "turbo4", "qjl1"])
+    ap.add_argument("--preset", default=HEADLINE[1], choices=["turbo2", "turbo3", "turbo4", "qjl1", "k8v4"])
     ap.add_argument("--layers", type=int, default=0,
                     help="distinct layer caches cycled per step (0: 1 when a layer's cache exceeds 1 GiB, else 32)")
     ap.add_argument("--kernel-launches", type=int, default=30,

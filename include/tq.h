@@ -36,7 +36,8 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 3
+#define TQ_ABI_VERSION 4
+#define TQ_MAX_K_LEVELS 256 /* key codes of up to 8 bits */
 #define TQ_HEAD_DIM 128
 #define TQ_BLOCK_TOKENS 64
 
@@ -54,11 +55,12 @@ typedef enum { TQ_DTYPE_BF16 = 0, TQ_DTYPE_F32 = 1 } tq_dtype;
 #define TQ_ROTATION_HAAR 0     /* seeded Haar-random orthogonal matrix */
 #define TQ_ROTATION_HADAMARD 1 /* randomized Walsh-Hadamard: H diag(s) / sqrt(d) */
 
-/* Cache configuration.  k_bits: scalar code bits per key coordinate (0..4; 0 = keys keep
+/* Cache configuration.  k_bits: scalar code bits per key coordinate (0..8; 0 = keys keep
  * only the sign sketch); k_qjl: 1 = keys carry the 1-bit sign sketch of their residual;
  * v_bits: value code bits (1..4); rotation: TQ_ROTATION_*; seed: fixes the rotation and the
  * sketch.  Presets: turbo2 = (1, 1, 2), turbo3 = (2, 1, 3), turbo4 = (3, 1, 4), sign-only
- * keys = (0, 1, 3). */
+ * keys = (0, 1, 3); keys wider than values, e.g. K8V4 = (8, 0, 4) (overview page, paragraph on
+ * K/V asymmetry: keys need more bits than values). */
 typedef struct tq_config {
   int32_t d;
   int32_t k_bits;
@@ -69,13 +71,16 @@ typedef struct tq_config {
 } tq_config;
 
 /* Static Lloyd-Max tables for N(0,1), stored as fp32 copies of fp64 values: 2^bits levels
- * (ascending) and 2^bits - 1 decision thresholds (midpoints).  A coordinate z of the
- * rotated, sqrt(d)-scaled unit vector gets code #{l : z >= threshold[l]}.  *_mse is the
- * fp64 Gaussian distortion of the table. */
+ * (ascending) and 2^bits - 1 decision thresholds (midpoints); entries past those are 0.  A
+ * coordinate z of the rotated, sqrt(d)-scaled unit vector gets code #{l : z >= threshold[l]}.
+ * *_mse is the fp64 Gaussian distortion of the table.  The tables are the fixed point of
+ * Lloyd's conditions (levels = conditional means of their cells, thresholds = midpoints),
+ * found by Lloyd's iteration and, for codes of 5 bits and more, finished by Newton's method
+ * on the same equations. */
 typedef struct tq_codebook {
   tq_config cfg;
-  float k_centroids[16];
-  float k_thresholds[16];
+  float k_centroids[TQ_MAX_K_LEVELS];
+  float k_thresholds[TQ_MAX_K_LEVELS];
   float v_centroids[16];
   float v_thresholds[16];
   double k_mse;
@@ -122,7 +127,7 @@ typedef struct tq_dev_params {
  *   v_norm  [B][Hkv][T_cap] fp32  value norms
  * Inside a 64-token block the bits follow this fixed arrangement (64 chunks; chunk L has
  * c = L % 16, g = L / 16; bit k is bit k % 8 of byte k / 8):
- *   key codes (b bits): chunk L = 16 b bytes holds tokens 16 t + c (t = 0..3) and
+ *   key codes (b bits, 1..8): chunk L = 16 b bytes holds tokens 16 t + c (t = 0..3) and
  *     coordinates 32 g + j (j = 0..31); code (t, j) starts at bit 32 b t + b j.
  *   sign bits: chunk L = 16 bytes; bit 32 t + j is the sign of sketch row 32 g + j of
  *     token 16 t + c.
@@ -168,7 +173,7 @@ typedef struct tq_cache_sizes {
  *     rotation is R_eff = R = R_hi / sqrt(128) exactly: the kernels apply one bf16 product pass
  *     instead of two and fold 1/sqrt(128) into their fp32 scales;
  *   S_b = bf16(S), S = 128x128 N(0,1) from the stream started at 2*seed + 1.
- * Errors: TQ_ERR_INVALID (NULL cfg/cb), TQ_ERR_UNSUPPORTED (d != 128, k_bits outside 0..4,
+ * Errors: TQ_ERR_INVALID (NULL cfg/cb), TQ_ERR_UNSUPPORTED (d != 128, k_bits outside 0..8,
  * v_bits outside 1..4, k_qjl not 0/1, k_bits == 0 with k_qjl == 0, or an unknown rotation). */
 int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, tq_host_params* out);
 
@@ -197,7 +202,7 @@ int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, const void* k,
 
 /* One decode step of attention for all (batch row, q-head) straight from the packed cache.
  * q: device [B][Hq][128] in q_dtype.  q-head h reads kv-head h / (Hq / Hkv); Hq / Hkv must
- *   be 4, 8 or 16.  Every configuration tq_build_codebook accepts is supported (keys of 0..4
+ *   be 4, 8 or 16.  Every configuration tq_build_codebook accepts is supported (keys of 0..8
  *   code bits with or without the sign sketch, values of 1..4 bits).
  * seq_len: device int32 [B], keys 0 .. seq_len[b]-1 are attended (1 <= seq_len[b] <= max_seq_len;
  *   values outside that range are clamped into it on the device).

@@ -19,6 +19,7 @@ TQ_ERR_DEVICE = -4
 TQ_DTYPE_BF16 = 0
 TQ_DTYPE_F32 = 1
 HEAD_DIM = 128
+MAX_K_LEVELS = 256
 BLOCK_TOKENS = 64
 
 ERROR_NAMES = {
@@ -40,7 +41,7 @@ ROTATIONS = {"haar": TQ_ROTATION_HAAR, "hadamard": TQ_ROTATION_HADAMARD}
 
 class TQCodebook(ctypes.Structure):
     _fields_ = [("cfg", TQConfig),
-                ("k_centroids", ctypes.c_float * 16), ("k_thresholds", ctypes.c_float * 16),
+                ("k_centroids", ctypes.c_float * MAX_K_LEVELS), ("k_thresholds", ctypes.c_float * MAX_K_LEVELS),
                 ("v_centroids", ctypes.c_float * 16), ("v_thresholds", ctypes.c_float * 16),
                 ("k_mse", ctypes.c_double), ("v_mse", ctypes.c_double)]
 

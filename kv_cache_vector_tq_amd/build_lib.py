@@ -17,9 +17,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtq.so")
-# the attention kernels are instantiated per key code width in translation units of their own
-SOURCES = (["tq_host.cpp", "tq_quantize.hip", "tq_attend.hip"] + [f"tq_attend_k{kb}.hip" for kb in range(5)] +
-           ["tq_bf16_attend.hip", "tq_probe.hip"])
+# the quantize and attention kernels are instantiated per key code width (0..8 bits) in
+# translation units of their own
+SOURCES = (["tq_host.cpp", "tq_quantize.hip", "tq_attend.hip"] + [f"tq_quantize_k{kb}.hip" for kb in range(9)] +
+           [f"tq_attend_k{kb}.hip" for kb in range(9)] + ["tq_bf16_attend.hip", "tq_probe.hip"])
 ARCH = "gfx950"
 
 

@@ -15,8 +15,8 @@
 //     coordinates): q1, q2 of the G q-heads (MFMA), stored as fp32 records;
 //  2. main: one workgroup of 8 waves (one workgroup per CU, two waves per SIMD) per (batch
 //     row, kv-head, context slice); each wave streams the 64-key blocks of its sub-slice.
-//     Codes are turned into f16 MFMA operands by table lookups in LDS (4 or 8 codes per
-//     lookup); keys sit on the M side of the score MFMAs (one key read serves all G q-heads
+//     Codes are turned into f16 MFMA operands by table lookups in LDS (2 to 8 codes per
+//     lookup; one per lookup for 5..8-bit keys); keys sit on the M side of the score MFMAs (one key read serves all G q-heads
 //     of the group), the softmax weights of a score tile feed the value MFMA directly from
 //     the accumulator layout, and the value sum stays in the rotated domain.  The 8 waves
 //     merge their online-softmax states in LDS and write one partial per (q-head, slice).
@@ -36,21 +36,26 @@ namespace tq {
 namespace {
 
 bool supported(const tq_config& c, int G) {
-  // every configuration tq_build_codebook accepts: keys of 0..4 bits (0 only with the sketch),
+  // every configuration tq_build_codebook accepts: keys of 0..8 bits (0 only with the sketch),
   // values of 1..4 bits
-  const bool keys = c.k_bits >= 0 && c.k_bits <= 4 && (c.k_qjl == 1 || c.k_bits > 0);
+  const bool keys = c.k_bits >= 0 && c.k_bits <= 8 && (c.k_qjl == 1 || c.k_bits > 0);
   return keys && c.v_bits >= 1 && c.v_bits <= 4 && (G == 4 || G == 8 || G == 16);
 }
 
-hipError_t dispatch_main(const MainArgs& a, const tq_config& c, int G, int n_slices, int B, bool pre, hipStream_t s,
-                         hipEvent_t e0, hipEvent_t e1) {
+// kcw: the scaled key centroids (all 2^k_bits of them; read for k_bits > 4).
+hipError_t dispatch_main(const MainArgs& a, const float* kcw, const tq_config& c, int G, int n_slices, int B, bool pre,
+                         hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const bool qjl = c.k_qjl != 0;
   switch (c.k_bits) {
-    case 0: return attn::dispatch_k0(a, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
-    case 1: return attn::dispatch_k1(a, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
-    case 2: return attn::dispatch_k2(a, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
-    case 3: return attn::dispatch_k3(a, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
-    case 4: return attn::dispatch_k4(a, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 0: return attn::dispatch_k0(a, kcw, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 1: return attn::dispatch_k1(a, kcw, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 2: return attn::dispatch_k2(a, kcw, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 3: return attn::dispatch_k3(a, kcw, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 4: return attn::dispatch_k4(a, kcw, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 5: return attn::dispatch_k5(a, kcw, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 6: return attn::dispatch_k6(a, kcw, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 7: return attn::dispatch_k7(a, kcw, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
+    case 8: return attn::dispatch_k8(a, kcw, qjl, c.v_bits, G, n_slices, B, pre, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }
@@ -105,7 +110,8 @@ double f16_rel_error(float x) {
   return std::fabs(r - f) / f;
 }
 
-// A centroid table holds f16(s c_l).  A common factor s (undone in fp32: with the logit scale
+// A centroid table holds f16(s c_l) (5..8-bit key tables: the exact f16 pair of s c_l).  A
+// common factor s (undone in fp32: with the logit scale
 // for keys, with the output normalisation for values) is chosen so that the few distinct
 // centroid magnitudes all sit nearly on the f16 grid: s = m / (smallest magnitude) with m an
 // 11-bit integer, the m with the smallest largest rounding error.  For 2-bit codes that error
@@ -113,6 +119,17 @@ double f16_rel_error(float x) {
 // table shared by keys and values (equal bit widths) serves both.  Cached per codebook.
 float table_scale(const float* cent, int bits) {
   if (bits == 0) return 1.0f;
+  if (bits > 4) {
+    // wide key tables hold each level as an exact f16 pair (hi, lo): the factor is the power of
+    // two that puts the largest level in [2^14, 2^15), so that the lo terms of even the
+    // smallest levels stay normal f16 numbers
+    float mx = 0.f;
+    for (int l = 0; l < (1 << bits); ++l) mx = std::max(mx, std::fabs(cent[l]));
+    if (mx == 0.f) return 1.0f;
+    int e = 0;
+    std::frexp(mx, &e);  // mx in [2^(e-1), 2^e)
+    return std::ldexp(1.0f, 15 - e);
+  }
   static std::mutex mu;
   static std::vector<std::pair<std::vector<float>, float>> cache;
   std::vector<float> key(cent, cent + (1 << bits));
@@ -151,8 +168,9 @@ float table_scale(const float* cent, int bits) {
 
 // Kernel arguments shared by decode and prefill attention: cache arrays, decode tables (centroids
 // times their f16 grid factors), logit scale and rotation mode.  scale 0 selects 1/sqrt(d).
+// kcw receives all 2^k_bits scaled key centroids (MainArgs holds the first 16).
 MainArgs main_args(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cache, int max_seq_len,
-                   float scale) {
+                   float scale, float* kcw) {
   MainArgs ma{};
   if (scale == 0.f) scale = INV_SQRT_D;
   const int one_pass = cb->cfg.rotation == TQ_ROTATION_HADAMARD ? 1 : 0;
@@ -178,6 +196,8 @@ MainArgs main_args(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_ca
     ma.k_cent[l] = static_cast<float>(static_cast<double>(cb->k_centroids[l]) * ks);
     ma.v_cent[l] = static_cast<float>(static_cast<double>(cb->v_centroids[l]) * vs);
   }
+  for (int l = 0; l < (cb->cfg.k_bits > 0 ? 1 << cb->cfg.k_bits : 0); ++l)
+    kcw[l] = static_cast<float>(static_cast<double>(cb->k_centroids[l]) * ks);
   ma.k_unscale = static_cast<float>(1.0 / static_cast<double>(ks));
   ma.v_unscale = static_cast<float>(1.0 / static_cast<double>(vs));
   return ma;
@@ -275,7 +295,8 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
     if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("query prologue launch: ") + hipGetErrorString(e));
   }
 
-  MainArgs ma = main_args(cb, p, cache, max_seq_len, scale);
+  float kcw[TQ_MAX_K_LEVELS];
+  MainArgs ma = main_args(cb, p, cache, max_seq_len, scale, kcw);
   ma.seq_len = seq_len;
   ma.qrec = qrec;
   ma.part = part;
@@ -292,7 +313,7 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
     e0 = reinterpret_cast<hipEvent_t>(pe.attend_start);
     e1 = reinterpret_cast<hipEvent_t>(pe.attend_stop);
   }
-  const hipError_t e = dispatch_main(ma, cb->cfg, G, n_slices, B, false, s, e0, e1);
+  const hipError_t e = dispatch_main(ma, kcw, cb->cfg, G, n_slices, B, false, s, e0, e1);
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("attention launch: ") + hipGetErrorString(e));
   return TQ_OK;
 }
@@ -405,7 +426,8 @@ extern "C" int tq_attend_prefill(const tq_codebook* cb, const tq_dev_params* p, 
   const int qpg = (G > 8 ? G : 8) / G;  // query positions per unit (max(8, G) columns of (position, q-head))
   const int64_t NG = (static_cast<int64_t>(T_q) + qpg - 1) / qpg;
   if (NG * cache->Hkv > (1ll << 30)) return fail(TQ_ERR_INVALID, "too many queries in one call");
-  MainArgs ma = main_args(cb, p, cache, max_seq_len, scale);
+  float kcw[TQ_MAX_K_LEVELS];
+  MainArgs ma = main_args(cb, p, cache, max_seq_len, scale, kcw);
   ma.out = out;
   ma.q_start = q_start;
   ma.q = q;
@@ -425,7 +447,7 @@ extern "C" int tq_attend_prefill(const tq_codebook* cb, const tq_dev_params* p, 
     e1 = reinterpret_cast<hipEvent_t>(pe.attend_stop);
   }
   const hipError_t e =
-      dispatch_main(ma, cb->cfg, G, 1, cache->B, true, reinterpret_cast<hipStream_t>(hip_stream), e0, e1);
+      dispatch_main(ma, kcw, cb->cfg, G, 1, cache->B, true, reinterpret_cast<hipStream_t>(hip_stream), e0, e1);
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("prefill attention launch: ") + hipGetErrorString(e));
   return TQ_OK;
 }

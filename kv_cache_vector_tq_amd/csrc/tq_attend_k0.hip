@@ -4,7 +4,7 @@
 namespace tq {
 namespace attn {
 
-TQ_ATTN_DISPATCH(0) { return qjl ? dispatch_v<0, true>(a, vb, G, n_slices, B, pre, s, e0, e1) : hipErrorInvalidValue; }
+TQ_ATTN_DISPATCH(0) { return dispatch_width<0>(a, kcw, qjl, vb, G, n_slices, B, pre, s, e0, e1); }
 
 }  // namespace attn
 }  // namespace tq

@@ -4,7 +4,7 @@
 namespace tq {
 namespace attn {
 
-TQ_ATTN_DISPATCH(1) { return qjl ? dispatch_v<1, true>(a, vb, G, n_slices, B, pre, s, e0, e1) : dispatch_v<1, false>(a, vb, G, n_slices, B, pre, s, e0, e1); }
+TQ_ATTN_DISPATCH(1) { return dispatch_width<1>(a, kcw, qjl, vb, G, n_slices, B, pre, s, e0, e1); }
 
 }  // namespace attn
 }  // namespace tq

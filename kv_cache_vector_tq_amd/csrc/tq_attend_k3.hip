@@ -4,7 +4,7 @@
 namespace tq {
 namespace attn {
 
-TQ_ATTN_DISPATCH(3) { return qjl ? dispatch_v<3, true>(a, vb, G, n_slices, B, pre, s, e0, e1) : dispatch_v<3, false>(a, vb, G, n_slices, B, pre, s, e0, e1); }
+TQ_ATTN_DISPATCH(3) { return dispatch_width<3>(a, kcw, qjl, vb, G, n_slices, B, pre, s, e0, e1); }
 
 }  // namespace attn
 }  // namespace tq

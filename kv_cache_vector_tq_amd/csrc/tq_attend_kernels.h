@@ -62,14 +62,26 @@ struct MainArgs {
 
 // Launches the attention kernel for key code width KB (k_qjl selects the sign sketch), value
 // width vb and group size G; defined in tq_attend_k<KB>.hip.
+// kcw: host array of the 2^KB scaled key centroids when KB > 4 (unused otherwise).
 #define TQ_ATTN_DISPATCH(KB)                                                                       \
-  hipError_t dispatch_k##KB(const MainArgs& a, bool qjl, int vb, int G, int n_slices, int B, bool pre,          \
-                            hipStream_t s, hipEvent_t e0, hipEvent_t e1)
+  hipError_t dispatch_k##KB(const MainArgs& a, const float* kcw, bool qjl, int vb, int G, int n_slices, int B, \
+                            bool pre, hipStream_t s, hipEvent_t e0, hipEvent_t e1)
 TQ_ATTN_DISPATCH(0);
 TQ_ATTN_DISPATCH(1);
 TQ_ATTN_DISPATCH(2);
 TQ_ATTN_DISPATCH(3);
 TQ_ATTN_DISPATCH(4);
+TQ_ATTN_DISPATCH(5);
+TQ_ATTN_DISPATCH(6);
+TQ_ATTN_DISPATCH(7);
+TQ_ATTN_DISPATCH(8);
+
+// Key centroids of 5..8-bit codes (times the table factor): too many for MainArgs, they are a
+// kernel argument of their own (1 KB at 8 bits); narrower widths carry a one-entry placeholder.
+template <int KB>
+struct KeyCent {
+  float c[KB > 4 ? (1 << KB) : 1];
+};
 
 }  // namespace attn
 
@@ -88,6 +100,14 @@ constexpr int MAX_GROUPS = 32;                   // merge groups per (batch row,
 constexpr int MAX_SLICES = MGROUP * MAX_GROUPS;  // context slices per (batch row, kv-head)
 constexpr int CNT_PER_UNIT = MAX_GROUPS + 1;     // arrival counters per (batch row, kv-head)
 
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // ---- code decoding ------------------------------------------------------------------------
 // Codes become f16 MFMA operands through lookup tables in LDS built at kernel start.  A table
 // Tab<B, K> maps a K-bit key (CPL = K / B consecutive B-bit codes, or K sign bits) to the CPL
@@ -95,17 +115,21 @@ constexpr int CNT_PER_UNIT = MAX_GROUPS + 1;     // arrival counters per (batch 
 //   B = 1 and sign bits: an 8-bit key -> 8 values (16-byte entries, 256 entries);
 //   B = 2: an 8-bit key -> 4 codes (8-byte entries, 256 entries);
 //   B = 3: a 12-bit key -> 4 codes (8-byte entries, 4096 entries);
-//   B = 4: an 8-bit key -> 2 codes (4-byte entries, 256 entries).
+//   B = 4: an 8-bit key -> 2 codes (4-byte entries, 256 entries);
+//   B = 5..8: one code -> its value as an exact pair of f16 terms hi + lo (4-byte entries,
+//     2^B entries); the score takes a product with each term.  (One f16 term alone leaves the
+//     many distinct levels of a wide table a relative error up to 2^-12 each, which no common
+//     factor can remove and which reaches the logits; the pair holds each level to ~2^-24.)
 // Keys and values of the same width share one table.  (Tables with one copy of each entry per
 // lane slot, which make a wave's random lookups free of LDS bank conflicts, were measured
 // without gain on the batch-16 128K-context and 1M-context workloads: the loop is bound by its
 // dependent chain, not by LDS bandwidth.)
 template <int B>
 struct Tab {
-  static constexpr int K = (B == 3) ? 12 : 8;            // key bits
-  static constexpr int CPL = K / B;                       // codes per lookup
-  static constexpr int EBYTES = 2 * CPL;                  // bytes per entry
-  static constexpr int SHIFT = EBYTES == 16 ? 4 : (EBYTES == 8 ? 3 : 2);
+  static constexpr int K = B > 4 ? B : ((B == 3) ? 12 : 8);  // key bits
+  static constexpr int CPL = K / B;                           // codes per lookup
+  static constexpr int EBYTES = B > 4 ? 4 : 2 * CPL;          // bytes per entry
+  static constexpr int SHIFT = EBYTES == 16 ? 4 : (EBYTES == 8 ? 3 : (EBYTES == 4 ? 2 : 1));
   static constexpr int BYTES = (1 << K) * EBYTES;
 };
 
@@ -121,6 +145,21 @@ template <int B, bool SIGN>
 __device__ void build_table(uint8_t* tab, const float* cent, int tid) {
   using T = Tab<B>;
   constexpr int L = 1 << B;
+  if constexpr (T::CPL == 1) {  // one code per entry: entry e is (hi, lo) with hi + lo = cent[e]
+    static_assert(!SIGN && T::EBYTES == 4 && T::BYTES % 16 == 0, "wide key tables");
+    for (int c = tid; c < T::BYTES / 16; c += NT) {
+      u32x4 w;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float x = cent[4 * c + h];
+        const _Float16 hi = static_cast<_Float16>(x);
+        // x - hi is exact in fp32 (hi is x rounded to 11 significant bits)
+        w[h] = pack_f16x2(hi, static_cast<_Float16>(x - static_cast<float>(hi)));
+      }
+      *reinterpret_cast<u32x4*>(tab + 16 * c) = w;
+    }
+    return;
+  }
   _Float16 c16[L];
 #pragma unroll
   for (int l = 0; l < L; ++l) c16[l] = SIGN ? static_cast<_Float16>(l ? 1.0f : -1.0f) : static_cast<_Float16>(cent[l]);
@@ -178,6 +217,25 @@ __device__ __forceinline__ f16x8 decode8(const uint32_t* dw, const uint8_t* tab)
   }
 }
 
+// Wide codes (B = 5..8): the 8 codes starting at bit P of dw -> the hi and lo f16 terms of their
+// values, one 4-byte lookup per code; hi takes the low halves of the entries, lo the high ones.
+template <int B, int P>
+__device__ __forceinline__ void decode8_pair(const uint32_t* dw, const uint8_t* tab, f16x8& hi, f16x8& lo) {
+  using T = Tab<B>;
+  static_assert(T::CPL == 1 && T::EBYTES == 4, "wide key tables");
+  constexpr int K = T::K, S = T::SHIFT;
+  u32x4 h, l;
+  static_for<0, 4>([&](auto I_) {
+    constexpr int i = decltype(I_)::value;
+    const uint32_t e0 = *reinterpret_cast<const uint32_t*>(tab + field<P + 2 * i * K, K, S>(dw));
+    const uint32_t e1 = *reinterpret_cast<const uint32_t*>(tab + field<P + (2 * i + 1) * K, K, S>(dw));
+    h[i] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);  // e0 bytes 0-1, e1 bytes 0-1
+    l[i] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);  // e0 bytes 2-3, e1 bytes 2-3
+  });
+  hi = __builtin_bit_cast(f16x8, h);
+  lo = __builtin_bit_cast(f16x8, l);
+}
+
 // Reductions over the 4 lanes of a column (lanes l, l^16, l^32, l^48) with the gfx950
 // row-swap instructions (VALU, no LDS round trip): each swap returns this lane's value and
 // its partner's, in some order, so max / sum of the pair is the pairwise reduction.
@@ -200,14 +258,6 @@ template <int N>
 __device__ __forceinline__ float row_ror(float v) {
   static_assert(N > 0 && N < 16, "rotation within a row");
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
-}
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
 }
 
 template <int N>
@@ -361,7 +411,7 @@ struct MainCfg {
 // written directly.  (Eight columns rather than sixteen keep the hi and lo query terms in the
 // columns of one accumulator, which halves the query operands held in registers.)
 template <int KB, bool QJL, int VB, int G, bool SCORES, bool PRE>
-__global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
+__global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent<KB> kcent) {
   constexpr int GC = PRE ? (G > 8 ? G : 8) : G;  // query columns per unit
   constexpr int QPG = GC / G;                     // prefill: query positions per unit
   using C = MainCfg<KB, QJL, VB, GC>;
@@ -452,7 +502,10 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
   Blk cur, nxt;
   load_block(min(blk_begin, nblk_cap - 1), cur);  // in flight while the tables are built
 
-  if constexpr (KB > 0) build_table<KBT, false>(smem + C::KOFF, a.k_cent, tid);
+  if constexpr (KB > 4)
+    build_table<KBT, false>(smem + C::KOFF, kcent.c, tid);
+  else if constexpr (KB > 0)
+    build_table<KBT, false>(smem + C::KOFF, a.k_cent, tid);
   if constexpr (QJL) build_table<1, true>(smem + C::SOFF, nullptr, tid);
   if constexpr (!C::SHARED) build_table<VB, false>(smem + C::VOFF, a.v_cent, tid);
   if constexpr (PRE) {
@@ -555,7 +608,15 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
         if constexpr (KB > 0 && C::has_c(ac)) {
           static_for<0, 4>([&](auto KB_) {
             constexpr int kb = decltype(KB_)::value;
-            d = mfma_f16(decode8<KBT, 32 * KB * t + 8 * KB * kb>(cur.kd, smem + C::KOFF), bc[ac][kb], d);
+            constexpr int P = 32 * KB * t + 8 * KB * kb;
+            if constexpr (KB > 4) {  // the two terms of every level against the same operand
+              f16x8 kh, kl;
+              decode8_pair<KBT, P>(cur.kd, smem + C::KOFF, kh, kl);
+              d = mfma_f16(kh, bc[ac][kb], d);
+              d = mfma_f16(kl, bc[ac][kb], d);
+            } else {
+              d = mfma_f16(decode8<KBT, P>(cur.kd, smem + C::KOFF), bc[ac][kb], d);
+            }
           });
         }
         if constexpr (QJL && C::has_s(ac)) {
@@ -900,7 +961,8 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a) {
 }
 
 template <int KB, bool QJL, int VB, int G>
-hipError_t launch_main(const MainArgs& a, int n_slices, int B, bool pre, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+hipError_t launch_main(const MainArgs& a, const attn::KeyCent<KB>& kc, int n_slices, int B, bool pre, hipStream_t s,
+                       hipEvent_t e0, hipEvent_t e1) {
   static_assert(MainCfg<KB, QJL, VB, G>::LDS <= 64 * 1024, "attention LDS budget");
   static_assert(MainCfg<KB, QJL, VB, (G > 8 ? G : 8)>::LDS <= 64 * 1024, "prefill LDS budget");
   auto kern = pre ? attend_kernel<KB, QJL, VB, G, false, true>
@@ -909,33 +971,46 @@ hipError_t launch_main(const MainArgs& a, int n_slices, int B, bool pre, hipStre
   // decode: (slices, kv-heads, rows); prefill: (kv-heads x query groups, 1, rows)
   const dim3 grid = pre ? dim3(a.Hkv * a.NG, 1, B) : dim3(n_slices, a.Hkv, B);
   if (e0 != nullptr || e1 != nullptr)
-    hipExtLaunchKernelGGL(kern, grid, dim3(NT), 0, s, e0, e1, 0, a);
+    hipExtLaunchKernelGGL(kern, grid, dim3(NT), 0, s, e0, e1, 0, a, kc);
   else
-    hipLaunchKernelGGL(kern, grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(kern, grid, dim3(NT), 0, s, a, kc);
   return hipGetLastError();
 }
 
 template <int KB, bool QJL, int VB>
-hipError_t dispatch_g(const MainArgs& a, int G, int n_slices, int B, bool pre, hipStream_t s, hipEvent_t e0,
-                      hipEvent_t e1) {
+hipError_t dispatch_g(const MainArgs& a, const attn::KeyCent<KB>& kc, int G, int n_slices, int B, bool pre,
+                      hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (G) {
-    case 4: return launch_main<KB, QJL, VB, 4>(a, n_slices, B, pre, s, e0, e1);
-    case 8: return launch_main<KB, QJL, VB, 8>(a, n_slices, B, pre, s, e0, e1);
-    case 16: return launch_main<KB, QJL, VB, 16>(a, n_slices, B, pre, s, e0, e1);
+    case 4: return launch_main<KB, QJL, VB, 4>(a, kc, n_slices, B, pre, s, e0, e1);
+    case 8: return launch_main<KB, QJL, VB, 8>(a, kc, n_slices, B, pre, s, e0, e1);
+    case 16: return launch_main<KB, QJL, VB, 16>(a, kc, n_slices, B, pre, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }
 
 template <int KB, bool QJL>
-hipError_t dispatch_v(const MainArgs& a, int VB, int G, int n_slices, int B, bool pre, hipStream_t s, hipEvent_t e0,
-                      hipEvent_t e1) {
+hipError_t dispatch_v(const MainArgs& a, const attn::KeyCent<KB>& kc, int VB, int G, int n_slices, int B, bool pre,
+                      hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (VB) {
-    case 1: return dispatch_g<KB, QJL, 1>(a, G, n_slices, B, pre, s, e0, e1);
-    case 2: return dispatch_g<KB, QJL, 2>(a, G, n_slices, B, pre, s, e0, e1);
-    case 3: return dispatch_g<KB, QJL, 3>(a, G, n_slices, B, pre, s, e0, e1);
-    case 4: return dispatch_g<KB, QJL, 4>(a, G, n_slices, B, pre, s, e0, e1);
+    case 1: return dispatch_g<KB, QJL, 1>(a, kc, G, n_slices, B, pre, s, e0, e1);
+    case 2: return dispatch_g<KB, QJL, 2>(a, kc, G, n_slices, B, pre, s, e0, e1);
+    case 3: return dispatch_g<KB, QJL, 3>(a, kc, G, n_slices, B, pre, s, e0, e1);
+    case 4: return dispatch_g<KB, QJL, 4>(a, kc, G, n_slices, B, pre, s, e0, e1);
   }
   return hipErrorInvalidValue;
+}
+
+// Body of dispatch_k<KB>: the wide key centroids (KB > 4), then the (sketch, value width, group
+// size) instance.  Keys without codes need the sketch.
+template <int KB>
+hipError_t dispatch_width(const MainArgs& a, const float* kcw, bool qjl, int vb, int G, int n_slices, int B, bool pre,
+                          hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  attn::KeyCent<KB> kc{};
+  if constexpr (KB > 4)
+    for (int l = 0; l < (1 << KB); ++l) kc.c[l] = kcw[l];
+  if (qjl) return dispatch_v<KB, true>(a, kc, vb, G, n_slices, B, pre, s, e0, e1);
+  if constexpr (KB == 0) return hipErrorInvalidValue;
+  else return dispatch_v<KB, false>(a, kc, vb, G, n_slices, B, pre, s, e0, e1);
 }
 
 }  // namespace

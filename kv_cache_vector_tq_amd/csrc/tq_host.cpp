@@ -34,7 +34,7 @@ ProfileEvents& profile_events() {
 
 int check_config(const tq_config& cfg) {
   if (cfg.d != TQ_HEAD_DIM) return fail(TQ_ERR_UNSUPPORTED, "only d = 128 is supported");
-  if (cfg.k_bits < 0 || cfg.k_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "k_bits must be in 0..4");
+  if (cfg.k_bits < 0 || cfg.k_bits > 8) return fail(TQ_ERR_UNSUPPORTED, "k_bits must be in 0..8");
   if (cfg.v_bits < 1 || cfg.v_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "v_bits must be in 1..4");
   if (cfg.k_qjl != 0 && cfg.k_qjl != 1) return fail(TQ_ERR_UNSUPPORTED, "k_qjl must be 0 or 1");
   if (cfg.k_bits == 0 && cfg.k_qjl == 0)
@@ -72,6 +72,12 @@ namespace {
 // Levels start evenly spaced on [-3, 3]; thresholds are midpoints; each level becomes
 // the conditional mean of its cell, (phi(a) - phi(b)) / (Phi(b) - Phi(a)).  Cell masses
 // use erfc on the side away from the mean so that tail cells keep their digits.
+// The iteration slows down as the level count grows (at 64 levels and more it is far from
+// converged after 10^5 steps), so after LLOYD_STEPS steps without convergence the same
+// equations c = F(c) are solved by Newton's method.  F_l depends on c_{l-1}, c_l, c_{l+1}
+// through its cell edges a = (c_{l-1} + c_l)/2 and b = (c_l + c_{l+1})/2, with
+// dF_l/da = phi(a) (F_l - a) / P_l and dF_l/db = phi(b) (b - F_l) / P_l, so the Jacobian is
+// tridiagonal and each step is one forward / backward elimination.
 double normal_pdf(double x) {
   if (std::isinf(x)) return 0.0;
   return std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI);
@@ -84,26 +90,75 @@ double normal_mass(double a, double b) {
   return 1.0 - 0.5 * std::erfc(b / s) - 0.5 * std::erfc(-a / s);
 }
 
+constexpr int LLOYD_STEPS = 1000;
+constexpr int NEWTON_STEPS = 50;
+constexpr double LLOYD_TOL = 1e-15;
+constexpr double NEWTON_TOL = 1e-11;  // fp64 evaluation noise of F is near 1e-13
+
+// Cell edges of levels lv (edges[0] = -inf, edges[L] = +inf, midpoints between).
+void cell_edges(const std::vector<double>& lv, std::vector<double>& edges) {
+  const int L = static_cast<int>(lv.size());
+  const double inf = std::numeric_limits<double>::infinity();
+  edges[0] = -inf;
+  edges[L] = inf;
+  for (int l = 1; l < L; ++l) edges[l] = 0.5 * (lv[l - 1] + lv[l]);
+}
+
 void lloyd_max(int bits, double* c, double* t, double* mse) {
   const int L = 1 << bits;
-  const double inf = std::numeric_limits<double>::infinity();
   std::vector<double> lv(L), nv(L), edges(L + 1);
   for (int l = 0; l < L; ++l) lv[l] = -3.0 + 6.0 * (l + 0.5) / L;
-  for (int it = 0; it < 100000; ++it) {
-    edges[0] = -inf;
-    edges[L] = inf;
-    for (int l = 1; l < L; ++l) edges[l] = 0.5 * (lv[l - 1] + lv[l]);
+  bool converged = false;
+  for (int it = 0; it < LLOYD_STEPS && !converged; ++it) {
+    cell_edges(lv, edges);
     double delta = 0.0;
     for (int l = 0; l < L; ++l) {
       nv[l] = (normal_pdf(edges[l]) - normal_pdf(edges[l + 1])) / normal_mass(edges[l], edges[l + 1]);
       delta = std::fmax(delta, std::fabs(nv[l] - lv[l]));
     }
     lv.swap(nv);
-    if (delta < 1e-15) break;
+    converged = delta < LLOYD_TOL;
   }
-  edges[0] = -inf;
-  edges[L] = inf;
-  for (int l = 1; l < L; ++l) edges[l] = 0.5 * (lv[l - 1] + lv[l]);
+  if (!converged) {
+    std::vector<double> lo(L), hi(L), w(L), x(L);
+    for (int it = 0; it < NEWTON_STEPS; ++it) {
+      cell_edges(lv, edges);
+      for (int l = 0; l < L; ++l) {
+        const double a = edges[l], b = edges[l + 1], m = normal_mass(a, b);
+        const double f = (normal_pdf(a) - normal_pdf(b)) / m;
+        lo[l] = std::isinf(a) ? 0.0 : normal_pdf(a) * (f - a) / m;  // dF_l/da
+        hi[l] = std::isinf(b) ? 0.0 : normal_pdf(b) * (b - f) / m;  // dF_l/db
+        nv[l] = f;
+      }
+      // (J - I) x = c - F(c): row l has 0.5 lo[l] at l - 1, 0.5 (lo[l] + hi[l]) - 1 at l and
+      // 0.5 hi[l] at l + 1.  Forward elimination keeps the reduced upper entry in w, the
+      // reduced right side in x.
+      double piv = 0.5 * (lo[0] + hi[0]) - 1.0;
+      w[0] = L > 1 ? 0.5 * hi[0] / piv : 0.0;
+      x[0] = (lv[0] - nv[0]) / piv;
+      for (int l = 1; l < L; ++l) {
+        const double sub = 0.5 * lo[l];
+        piv = 0.5 * (lo[l] + hi[l]) - 1.0 - sub * w[l - 1];
+        w[l] = l + 1 < L ? 0.5 * hi[l] / piv : 0.0;
+        x[l] = (lv[l] - nv[l] - sub * x[l - 1]) / piv;
+      }
+      for (int l = L - 2; l >= 0; --l) x[l] -= w[l] * x[l + 1];
+      double step = 0.0;
+      for (int l = 0; l < L; ++l) {
+        lv[l] += x[l];
+        step = std::fmax(step, std::fabs(x[l]));
+      }
+      if (step < NEWTON_TOL) break;
+    }
+    // the law is symmetric and so is its quantizer: mirror pairs are averaged, which removes
+    // the solve's fp64 noise from the middle threshold (exactly 0, as for narrow tables)
+    for (int l = 0; l < L / 2; ++l) {
+      const double v = 0.5 * (lv[L - 1 - l] - lv[l]);
+      lv[l] = -v;
+      lv[L - 1 - l] = v;
+    }
+  }
+  cell_edges(lv, edges);
   double s = 0.0;
   for (int l = 0; l < L; ++l) {
     const double dphi = normal_pdf(edges[l]) - normal_pdf(edges[l + 1]);
@@ -236,7 +291,7 @@ int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, tq_host_params* out
   if (rc != TQ_OK) return rc;
   std::memset(cb, 0, sizeof(*cb));
   cb->cfg = *cfg;
-  double c[16], t[16], mse = 0.0;
+  double c[TQ_MAX_K_LEVELS], t[TQ_MAX_K_LEVELS], mse = 0.0;
   if (cfg->k_bits > 0) {
     lloyd_max(cfg->k_bits, c, t, &mse);
     for (int l = 0; l < (1 << cfg->k_bits); ++l) cb->k_centroids[l] = static_cast<float>(c[l]);

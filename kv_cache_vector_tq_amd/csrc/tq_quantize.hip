@@ -17,188 +17,34 @@
 //   * rotation: bf16 inputs are exact, R_eff = R_hi + R_lo takes two passes (fp32 inputs
 //     are split into three exact bf16 terms first), all products exact, fp32 accumulation;
 //   * sketch: r (fp32) is split into three exact bf16 terms, S_b is bf16, so u = S_b r is
-//     the fp32-accumulated product of the fp32 residual.
+//     the fp32-accumulated product of the fp32 residual;
+//   * codes: up to 4 bits from the thresholds held in registers (a compare chain, or a
+//     binary search at 3 bits); 5..8-bit key codes by a binary search over the thresholds
+//     staged in LDS, one compare per code bit.
+// Each key code width is instantiated in a translation unit of its own (tq_quantize_k*.hip).
 // The k dimension of every MFMA maps lane group g, element e of k-block kb to coordinate
 // 32 g + 8 kb + e on both operands, so the sum runs over all 128 coordinates.
 #include <hip/hip_runtime.h>
-#include <hip/hip_ext.h>
 
 #include <algorithm>
 
-#include "tq_common.h"
-#include "tq_internal.h"
-#include "tq_qrot.h"
-#include "tq_quantize_tile.h"
+#include "tq_quantize_kernels.h"
 
 namespace tq {
 namespace {
 
-// From tile t on (stride nwg), finds the next tile the call writes (index tf); false when
-// there is none.  All values are uniform over the workgroup.
-__device__ __forceinline__ bool find_tile(const QuantLaunch& q, int t, int nwg, int& tf, TileRef& r) {
-  for (; t < q.n_tiles; t += nwg) {
-    const int tensor = t & 1;
-    const int rest = t >> 1;
-    const int i = rest % q.nblk_max;
-    const int bh = rest / q.nblk_max;
-    if (tensor == 0 ? !q.has_k : !q.has_v) continue;
-    // a scalar load (constant address space: start_pos does not change during the kernel), so
-    // waiting for it does not wait for the vector loads in flight
-    typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-    const int start = ((const_i32_ptr)(uintptr_t)q.k.start_pos)[bh / q.Hkv];
-    if (start < 0) continue;
-    const int end = min(start + q.k.n_new, q.k.T_cap);  // one past the last slot written
-    const int blk = start / 64 + i;
-    const int p0 = blk * 64;
-    if (p0 >= end) continue;
-    r = TileRef{tensor, bh / q.Hkv, bh % q.Hkv, start, blk, max(start, p0), min(end, p0 + 64)};
-    tf = t;
-    return true;
-  }
-  return false;
-}
-
-// Persistent workgroups walk tiles t = ((b * Hkv + h) * nblk_max + i) * 2 + tensor.  This is
-// workgroup blockIdx.x of gridDim.x, or of the first nwg_fused workgroups of a fused launch.
-// Each tile's inputs are loaded while the previous tile computes.
-template <int KB, bool QJL, int VB, bool F32, bool FUSED>
-__device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& sm, int nwg_fused) {
-  const int wg = static_cast<int>(blockIdx.x);
-  const int nwg = FUSED ? nwg_fused : static_cast<int>(gridDim.x);
-  const int tid = threadIdx.x;
-  Operands op;
-  // a workgroup that only sees value tiles (tiles alternate K, V; with one tile per workgroup
-  // the odd ones) does not need the sketch matrix.  The operands are requested first: they
-  // are the largest loads, and their latency overlaps the search for the first tile.
-  const bool sketch = QJL && q.has_k && (nwg < q.n_tiles || (wg & 1) == 0);
-  load_operands<QJL>(op, q.k, sketch, tid);
-  TileIn<F32> in;
-  // A one-token call with a workgroup per tile (a decode step): every step up to the packing
-  // works on the token as row 0 of the tile; its slot (start_pos) is needed only by the
-  // stores, so its load overlaps the input loads.  start_pos is read with a vector load (the
-  // index is offset by a lane count that is always 0): waiting for it then never waits for
-  // LDS traffic, as waiting for a scalar load would.
-  if (q.k.n_new == 1 && nwg >= q.n_tiles) {  // uniform
-    if (wg >= q.n_tiles) return;
-    const int tensor = wg & 1, bh = wg >> 1, b = bh / q.Hkv, h = bh % q.Hkv;  // one block per row
-    if (tensor == 0 ? !q.has_k : !q.has_v) return;
-    const int start_lane = q.k.start_pos[b + static_cast<int>(__builtin_amdgcn_mbcnt_lo(0u, 0u))];
-    const TileRef row0{tensor, b, h, 0, 0, 0, 1};
-    load_rows<F32>(q, row0, tid, in);
-    load_rows_norms<F32>(sm, row0, in, tid, q.k.zscale);
-    const int start = __builtin_amdgcn_readfirstlane(start_lane);
-    if (start < 0 || start >= q.k.T_cap) return;  // uniform: the row is not written
-    const TileRef cur{tensor, b, h, start, start / 64, start, start + 1};
-    uint32_t prev[4];
-    load_prev<VB>(q, cur, tid, prev);
-    lds_barrier();
-    if (tensor == 0)
-      quantize_tile<true, KB, QJL, F32>(q.k, sm, op, cur, prev, tid, true);
-    else
-      quantize_tile<false, VB, false, F32>(q.v, sm, op, cur, prev, tid, true);
-    return;
-  }
-  int t;
-  TileRef cur;
-  if (!find_tile(q, wg, nwg, t, cur)) return;  // uniform
-  // issued after the operands, so that waiting for the first tile's rows implies them
-  load_rows<F32>(q, cur, tid, in);
-  for (;;) {
-    int tn = 0;
-    TileRef nxt;
-    const bool more = find_tile(q, t + nwg, nwg, tn, nxt);
-    lds_barrier();  // the previous tile is done with LDS
-    load_rows_norms<F32>(sm, cur, in, tid, q.k.zscale);
-    uint32_t prev[4];
-    load_prev<VB>(q, cur, tid, prev);  // used at the end of the tile
-    // the next tile's rows are in flight while this tile computes
-    if (more) load_rows<F32>(q, nxt, tid, in);  // uniform
-    lds_barrier();
-    if (cur.tensor == 0)
-      quantize_tile<true, KB, QJL, F32>(q.k, sm, op, cur, prev, tid, false);
-    else
-      quantize_tile<false, VB, false, F32>(q.v, sm, op, cur, prev, tid, false);
-    if (!more) break;
-    cur = nxt;
-    t = tn;
-  }
-}
-
-template <int KB, bool QJL, int VB, bool F32>
-__global__ void __launch_bounds__(256, 2) quantize_kernel(QuantLaunch q) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
-  quantize_workgroup<KB, QJL, VB, F32, false>(q, sm, 0);
-}
-
-// Decode step: the first n_qwg workgroups quantize the new tokens, each further workgroup
-// rotates the queries of one (batch row, kv-head) unit (wave w: output coordinates
-// 32 w .. 32 w + 31), all in one launch; the two parts share no data.
-template <int KB, bool QJL, int VB, bool F32>
-__global__ void __launch_bounds__(256, 2) append_rotate_kernel(QuantLaunch q, PrologueArgs pa, int n_qwg) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
-  if (static_cast<int>(blockIdx.x) < n_qwg)
-    quantize_workgroup<KB, QJL, VB, F32, true>(q, sm, n_qwg);
-  else
-    rotate_query_tile<QJL>(pa, static_cast<int>(blockIdx.x) - n_qwg, threadIdx.x >> 6, threadIdx.x & 63);
-}
-
-// Launch shape: grid workgroups of quantize, plus rot_wgs rotation workgroups when pa is set.
-struct QuantGrid {
-  int grid;
-  const PrologueArgs* pa;
-  int rot_wgs;
-};
-
-template <int KB, bool QJL, int VB>
-hipError_t launch_quantize(const QuantLaunch& q, bool f32, const QuantGrid& g, hipStream_t s, hipEvent_t e0,
-                           hipEvent_t e1) {
-  const bool ext = e0 != nullptr || e1 != nullptr;
-  if (g.pa != nullptr) {
-    auto kern = f32 ? append_rotate_kernel<KB, QJL, VB, true> : append_rotate_kernel<KB, QJL, VB, false>;
-    const dim3 grid(g.grid + g.rot_wgs);
-    if (ext)
-      hipExtLaunchKernelGGL(kern, grid, dim3(256), 0, s, e0, e1, 0, q, *g.pa, g.grid);
-    else
-      hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, q, *g.pa, g.grid);
-  } else {
-    auto kern = f32 ? quantize_kernel<KB, QJL, VB, true> : quantize_kernel<KB, QJL, VB, false>;
-    if (ext)
-      hipExtLaunchKernelGGL(kern, dim3(g.grid), dim3(256), 0, s, e0, e1, 0, q);
-    else
-      hipLaunchKernelGGL(kern, dim3(g.grid), dim3(256), 0, s, q);
-  }
-  return hipGetLastError();
-}
-
-template <int KB, bool QJL>
-hipError_t dispatch_v(const QuantLaunch& q, int vb, bool f32, const QuantGrid& g, hipStream_t s, hipEvent_t e0,
-                      hipEvent_t e1) {
-  switch (vb) {
-    case 1: return launch_quantize<KB, QJL, 1>(q, f32, g, s, e0, e1);
-    case 2: return launch_quantize<KB, QJL, 2>(q, f32, g, s, e0, e1);
-    case 3: return launch_quantize<KB, QJL, 3>(q, f32, g, s, e0, e1);
-    case 4: return launch_quantize<KB, QJL, 4>(q, f32, g, s, e0, e1);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t dispatch(const QuantLaunch& q, const tq_config& c, bool f32, const QuantGrid& g, hipStream_t s,
+hipError_t dispatch(const QuantLaunch& q, const tq_codebook& cb, bool f32, const QuantGrid& g, hipStream_t s,
                     hipEvent_t e0, hipEvent_t e1) {
-  if (c.k_qjl) {
-    switch (c.k_bits) {
-      case 0: return dispatch_v<0, true>(q, c.v_bits, f32, g, s, e0, e1);
-      case 1: return dispatch_v<1, true>(q, c.v_bits, f32, g, s, e0, e1);
-      case 2: return dispatch_v<2, true>(q, c.v_bits, f32, g, s, e0, e1);
-      case 3: return dispatch_v<3, true>(q, c.v_bits, f32, g, s, e0, e1);
-      case 4: return dispatch_v<4, true>(q, c.v_bits, f32, g, s, e0, e1);
-    }
-  } else {
-    switch (c.k_bits) {
-      case 1: return dispatch_v<1, false>(q, c.v_bits, f32, g, s, e0, e1);
-      case 2: return dispatch_v<2, false>(q, c.v_bits, f32, g, s, e0, e1);
-      case 3: return dispatch_v<3, false>(q, c.v_bits, f32, g, s, e0, e1);
-      case 4: return dispatch_v<4, false>(q, c.v_bits, f32, g, s, e0, e1);
-    }
+  switch (cb.cfg.k_bits) {
+    case 0: return qk::dispatch_q0(q, cb, f32, g, s, e0, e1);
+    case 1: return qk::dispatch_q1(q, cb, f32, g, s, e0, e1);
+    case 2: return qk::dispatch_q2(q, cb, f32, g, s, e0, e1);
+    case 3: return qk::dispatch_q3(q, cb, f32, g, s, e0, e1);
+    case 4: return qk::dispatch_q4(q, cb, f32, g, s, e0, e1);
+    case 5: return qk::dispatch_q5(q, cb, f32, g, s, e0, e1);
+    case 6: return qk::dispatch_q6(q, cb, f32, g, s, e0, e1);
+    case 7: return qk::dispatch_q7(q, cb, f32, g, s, e0, e1);
+    case 8: return qk::dispatch_q8(q, cb, f32, g, s, e0, e1);
   }
   return hipErrorInvalidValue;
 }
@@ -301,7 +147,7 @@ int quantize_launch(const tq_codebook* cb, const tq_dev_params* p, const void* k
     qg.pa = &pa;
     qg.rot_wgs = rot->units;
   }
-  hipError_t e = dispatch(q, cb->cfg, f32, qg, s, e0, e1);
+  hipError_t e = dispatch(q, *cb, f32, qg, s, e0, e1);
   if (e != hipSuccess) return fail(TQ_ERR_DEVICE, std::string("quantize launch: ") + hipGetErrorString(e));
   return TQ_OK;
 }

@@ -205,9 +205,10 @@ __device__ __forceinline__ void load_rows_norms(Smem& sm, const TileRef& tr, con
 // The input rows and norms are in LDS already (load_rows_norms); prev holds the value words
 // a partial value tile rewrites (load_prev).  one: the tile's single token was loaded and is
 // computed as row 0 (a one-token call); only the stores use its slot.
+// wtab (5..8-bit keys only): the key table in LDS, 2^BITS levels then the thresholds.
 template <bool KEY, int BITS, bool QJL, bool F32>
 __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, const Operands& op, const TileRef& tr,
-                                              const uint32_t* prev, int tid, bool one) {
+                                              const uint32_t* prev, int tid, bool one, const float* wtab) {
   const int b = tr.b, h = tr.h, blk = tr.blk, lo_slot = tr.lo_slot, hi_slot = tr.hi_slot;
   constexpr int L = 1 << (BITS > 0 ? BITS : 1);
   float* s_tile = sm.tile;
@@ -287,9 +288,10 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   // pack below masks their rows) -----------------------------------------------------------
   // The codebook as wave-uniform register values (readfirstlane), so that the compare chain
   // selects values rather than addresses of the argument block.
-  float cent[L], thr[L];
+  constexpr int LR = BITS <= 4 ? L : 1;  // wide tables stay in LDS
+  float cent[LR], thr[LR];
 #pragma unroll
-  for (int l = 0; l < L; ++l) {
+  for (int l = 0; l < LR; ++l) {
     cent[l] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.centroids[l])));
     thr[l] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.thresholds[l])));
   }
@@ -314,6 +316,15 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
           const bool b1 = z >= (b0 ? thr[5] : thr[1]);
           const float t2 = b0 ? (b1 ? thr[6] : thr[4]) : (b1 ? thr[2] : thr[0]);
           const int idx = (b0 ? 4 : 0) | (b1 ? 2 : 0) | (z >= t2 ? 1 : 0);
+          s_idx[row * IDX_STRIDE + o] = static_cast<uint8_t>(idx);
+        } else if constexpr (BITS > 4) {
+          // binary search over the 2^BITS - 1 sorted thresholds in LDS: after the step of
+          // width w, the thresholds below idx are exactly those <= z among the ones seen
+          const float* wthr = wtab + L;
+          int idx = 0;
+#pragma unroll
+          for (int w = L / 2; w >= 1; w >>= 1) idx += z >= wthr[idx + w - 1] ? w : 0;
+          if constexpr (KEY && QJL) c = wtab[idx];
           s_idx[row * IDX_STRIDE + o] = static_cast<uint8_t>(idx);
         } else if constexpr (BITS > 0) {
           int idx = 0;

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert tq.tq_abi_version() == 3
+    assert tq.tq_abi_version() == 4
 
 
 @pytest.mark.parametrize("preset", ["turbo2", "turbo3", "turbo4", "qjl1"])
@@ -67,6 +67,21 @@ def test_parameter_build_matches_oracle_bit_for_bit(preset, seed):
         assert abs(cb.cb.k_mse - kmse) < 1e-15
 
 
+@pytest.mark.parametrize("k_bits", [5, 6, 7, 8])
+def test_wide_key_tables_match_oracle_bit_for_bit(k_bits):
+    # 5..8-bit key tables: the library's Lloyd iteration with its Newton finish gives the
+    # oracle's fp32 tables exactly; entries past 2^b levels stay zero
+    cb = tq.tq_build_codebook(k_bits, k_bits % 2, 4, 0)
+    kc, kt, kmse = codebook_f32(k_bits)
+    np.testing.assert_array_equal(cb.k_centroids(), kc)
+    np.testing.assert_array_equal(cb.k_thresholds(), kt)
+    assert abs(cb.cb.k_mse - kmse) < 1e-15
+    L = 1 << k_bits
+    assert not np.any(np.array(cb.cb.k_centroids[L:])) and not np.any(np.array(cb.cb.k_thresholds[L - 1:]))
+    with pytest.raises(tq.TQError):
+        tq.tq_build_codebook(9, 0, 4, 0)
+
+
 @pytest.mark.parametrize("preset", ["turbo3", "qjl1"])
 @pytest.mark.parametrize("seed", [0, 9])
 def test_hadamard_parameter_build_matches_oracle_bit_for_bit(preset, seed):
@@ -91,7 +106,7 @@ def test_unknown_rotation_rejected():
         tq.tq_build_codebook(2, 1, 3, rotation="dct")
 
 
-@pytest.mark.parametrize("bad", [dict(k_bits=0, k_qjl=0, v_bits=3), dict(k_bits=5, k_qjl=1, v_bits=3),
+@pytest.mark.parametrize("bad", [dict(k_bits=0, k_qjl=0, v_bits=3), dict(k_bits=9, k_qjl=1, v_bits=3),
                                  dict(k_bits=2, k_qjl=2, v_bits=3), dict(k_bits=2, k_qjl=1, v_bits=0),
                                  dict(k_bits=2, k_qjl=1, v_bits=5)])
 def test_bad_configs_rejected(bad):

@@ -25,11 +25,13 @@ D = 128
 # 2-bit preset of the fork named in "Когда в марте 2026 года Google опубликовала статью..."
 # (paragraph on community implementations), read the same way: 1-bit key code + sign,
 # 2-bit values.  "qjl1" keeps
-# only the 1-bit sign sketch for keys.
+# only the 1-bit sign sketch for keys.  "k8v4" is the asymmetric preset named in the same
+# overview's paragraph on K/V asymmetry: 8-bit key codes (no sketch), 4-bit values.
 PRESETS = {
     "turbo2": (1, 1, 2),
     "turbo3": (2, 1, 3),
     "turbo4": (3, 1, 4),
+    "k8v4": (8, 0, 4),
     "qjl1": (0, 1, 3),
 }
 
