@@ -63,7 +63,7 @@ def parse():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attend_kernel.json")
 # sources of the attention kernel: the counter figures hold only for the build they were taken on
 ATTEND_SOURCES = [os.path.join(ROOT, "kv_cache_vector_tq_amd", "csrc", f)
-                  for f in ["tq_attend_kernels.h", "tq_attend.hip"] + [f"tq_attend_k{kb}.hip" for kb in range(5)]]
+                  for f in ["tq_attend_kernels.h", "tq_attend.hip"] + [f"tq_attend_k{kb}.hip" for kb in range(9)]]
 
 
 def attend_sources_sha256() -> str:
