@@ -25,6 +25,15 @@
  *  - Return value 0 (TQ_OK) or a negative TQ_ERR_* code.  Every argument check runs on the
  *    host before any launch; tq_last_error() then describes the failure (thread-local).
  *  - Non-finite inputs give unspecified codes; they are not checked.
+ *
+ * State the library keeps between calls (everything else lives in caller-owned memory):
+ *  - per thread: the last error text (tq_last_error) and the timing-hook events
+ *    (tq_profile_events);
+ *  - per process, read-only after first use and guarded by a mutex: the compute-unit count of
+ *    each device, the f16 table factor of each codebook (a pure function of its levels), and
+ *    the environment knobs TQ_ATTN_MIN_BLOCKS / TQ_ATTN_MGROUP (read once; they change only the
+ *    context split of tq_attend_decode);
+ *  - per device: the fixed scratch array of tq_attend_decode_noalloc.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -158,7 +167,10 @@ typedef struct tq_cache_sizes {
   size_t bytes_per_token; /* stored bytes per token and kv-head, all arrays */
 } tq_cache_sizes;
 
-/* One-time parameter build, host only, deterministic in cfg->seed.
+/* One-time parameter build, host only, deterministic in cfg->seed ("Когда в марте 2026 года
+ * Google опубликовала статью...": a random orthogonal rotation, and a Lloyd-Max codebook computed
+ * once for the near-normal rotated coordinates; "Google TurboQuant простыми словами", section "Как
+ * работает TurboQuant", step 2: a Gaussian Johnson-Lindenstrauss projection for the sign bits).
  * Fills *cb with the key and value codebooks (Lloyd-Max fixed point for N(0,1)) and, when
  * out is not NULL, the parameter matrices of tq_host_params:
  *   Haar mode: G = 128x128 N(0,1) from SplitMix64 started at state 2*seed (Box-Muller,
@@ -181,7 +193,11 @@ int tq_build_codebook(const tq_config* cfg, tq_codebook* cb, tq_host_params* out
  * Errors: TQ_ERR_INVALID (bad sizes / NULL), TQ_ERR_UNSUPPORTED (bad config). */
 int tq_cache_layout(const tq_config* cfg, int B, int Hkv, int T_cap, tq_cache_sizes* out);
 
-/* Quantize-on-write of n_new tokens per (batch row, kv-head) into the packed cache.
+/* Quantize-on-write of n_new tokens per (batch row, kv-head) into the packed cache
+ * ("Когда в марте 2026 года Google опубликовала статью...": rotate, quantize every coordinate
+ * with the stored codebook, correct the residual with one QJL bit; "Google TurboQuant простыми
+ * словами", step 2: one sign bit per projected residual coordinate; section "Бенчмарки
+ * TurboQuant", list "Из независимых реализаций": one 4-byte side value per 128 values).
  * k, v: device inputs, element (b, h, t, j) at offset b*stride_b + h*stride_h + t*stride_t + j
  *   (strides in elements; the 128 coordinates of a vector are contiguous); dtype in_dtype.
  *   Either may be NULL to write only keys or only values.
@@ -200,7 +216,12 @@ int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, const void* k,
                    int64_t stride_h, int64_t stride_t, const int32_t* start_pos,
                    const tq_kv_cache* cache, void* hip_stream);
 
-/* One decode step of attention for all (batch row, q-head) straight from the packed cache.
+/* One decode step of attention for all (batch row, q-head) straight from the packed cache
+ * ("Когда в марте 2026 года Google опубликовала статью...": attention is computed from the
+ * compressed keys, with the 1-bit correction carried into the scores; "Google TurboQuant
+ * простыми словами", step 2: the sign term makes the inner-product estimate unbiased; "KV cache
+ * benchmark Qwen 3.6-35B-A3B", section "Неочевидный совет": decode is bound by memory bandwidth,
+ * so the codes are read once, directly).
  * q: device [B][Hq][128] in q_dtype.  q-head h reads kv-head h / (Hq / Hkv); Hq / Hkv must
  *   be 4, 8 or 16.  Every configuration tq_build_codebook accepts is supported (keys of 0..8
  *   code bits with or without the sign sketch, values of 1..4 bits).
@@ -232,7 +253,8 @@ int tq_attend_decode(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_
                      int max_seq_len, float scale, float* out, float* scores_out,
                      void* workspace, size_t* workspace_bytes, void* hip_stream);
 
-/* One decode step of a layer in two launches: quantize-on-write of one new token per
+/* One decode step of a layer in two launches (the calls above, per generated token):
+ * quantize-on-write of one new token per
  * (batch row, kv-head) exactly as tq_quantize_kv with n_new = 1 (k, v, kv_dtype, strides and
  * start_pos as there; the token is at offset b*kv_stride_b + h*kv_stride_h), then attention
  * exactly as tq_attend_decode.  The query rotation that tq_attend_decode launches on its own
