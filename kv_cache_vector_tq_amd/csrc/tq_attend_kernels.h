@@ -563,29 +563,50 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
     const float s1 = ldexpf(1.0f, -e1), s2 = ldexpf(1.0f, -e2);  // exact powers of two
     u1 = ldexpf(1.0f, e1);
     u2 = ldexpf(1.0f, e2);
-    // this lane's term in each accumulator (part = col / G)
-    int kd[C::NA];
+    // this lane's term in each accumulator (part = col / G), as bit masks that pick the hi or
+    // lo f16 term of a code or sign coordinate pair, or neither (branch-free selects: written as
+    // conditional assignments, the per-element choice compiled to divergent branches)
+    uint32_t mch[C::NA], mcl[C::NA], msh[C::NA], msl[C::NA];
     static_for<0, C::NA>([&](auto A_) {
-      kd[A_] = 0;
-      static_for<0, C::NP>([&](auto K_) {
-        if (part == decltype(K_)::value) kd[A_] = C::kind(decltype(A_)::value, decltype(K_)::value);
-      });
+      constexpr int ac = decltype(A_)::value;
+      int kd = C::kind(ac, 0);
+      static_for<1, C::NP>([&](auto K_) { kd = part == decltype(K_)::value ? C::kind(ac, decltype(K_)::value) : kd; });
+      mch[ac] = kd == 0 ? ~0u : 0u;
+      mcl[ac] = kd == 1 ? ~0u : 0u;
+      msh[ac] = kd == 2 ? ~0u : 0u;
+      msl[ac] = kd == 3 ? ~0u : 0u;
     });
-    const _Float16 z16 = static_cast<_Float16>(0.0f);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      u32x4 wc[C::NA], ws[C::NA];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x1 = qv1[2 * kb + j / 4][j % 4] * s1, x2 = qv2[2 * kb + j / 4][j % 4] * s2;
-        const _Float16 h1 = static_cast<_Float16>(x1), l1 = static_cast<_Float16>(x1 - static_cast<float>(h1));
-        const _Float16 h2 = static_cast<_Float16>(x2), l2 = static_cast<_Float16>(x2 - static_cast<float>(h2));
+      for (int jp = 0; jp < 4; ++jp) {  // coordinate pairs 2 jp, 2 jp + 1 of the k-block
+        uint32_t hp1, lp1, hp2, lp2;
+        {
+          const float x1a = qv1[2 * kb + jp / 2][2 * (jp % 2)] * s1, x1b = qv1[2 * kb + jp / 2][2 * (jp % 2) + 1] * s1;
+          const float x2a = qv2[2 * kb + jp / 2][2 * (jp % 2)] * s2, x2b = qv2[2 * kb + jp / 2][2 * (jp % 2) + 1] * s2;
+          const _Float16 h1a = static_cast<_Float16>(x1a), h1b = static_cast<_Float16>(x1b);
+          const _Float16 h2a = static_cast<_Float16>(x2a), h2b = static_cast<_Float16>(x2b);
+          hp1 = pack_f16x2(h1a, h1b);
+          lp1 = pack_f16x2(static_cast<_Float16>(x1a - static_cast<float>(h1a)),
+                           static_cast<_Float16>(x1b - static_cast<float>(h1b)));
+          hp2 = pack_f16x2(h2a, h2b);
+          lp2 = pack_f16x2(static_cast<_Float16>(x2a - static_cast<float>(h2a)),
+                           static_cast<_Float16>(x2b - static_cast<float>(h2b)));
+        }
         static_for<0, C::NA>([&](auto A_) {
           constexpr int ac = decltype(A_)::value;
           // operands only for the accumulators that take that kind of term
-          if constexpr (C::has_c(ac)) bc[ac][kb][j] = kd[ac] == 0 ? h1 : (kd[ac] == 1 ? l1 : z16);
-          if constexpr (C::has_s(ac)) bsg[ac][kb][j] = kd[ac] == 2 ? h2 : (kd[ac] == 3 ? l2 : z16);
+          if constexpr (C::has_c(ac)) wc[ac][jp] = (hp1 & mch[ac]) | (lp1 & mcl[ac]);
+          if constexpr (C::has_s(ac)) ws[ac][jp] = (hp2 & msh[ac]) | (lp2 & msl[ac]);
         });
       }
+      static_for<0, C::NA>([&](auto A_) {
+        constexpr int ac = decltype(A_)::value;
+        if constexpr (C::has_c(ac)) bc[ac][kb] = __builtin_bit_cast(f16x8, wc[ac]);
+        if constexpr (C::has_s(ac)) bsg[ac][kb] = __builtin_bit_cast(f16x8, ws[ac]);
+      });
+    }
   }
 
   // One block: scores, online softmax, value sums.  `d` holds the block's codes, `nrm` its norms.
