@@ -125,7 +125,7 @@ __device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& s
     if (start < 0 || start >= q.k.T_cap) return;  // uniform: the row is not written
     const TileRef cur{tensor, b, h, start, start / 64, start, start + 1};
     uint32_t prev[4];
-    load_prev<VB>(q, cur, tid, prev);
+    load_prev<VB>(q, cur, tid, false, prev);
     lds_barrier();
     if (tensor == 0)
       quantize_tile<true, KB, QJL, F32>(q.k, sm, op, cur, prev, tid, true, wtab);
@@ -145,7 +145,9 @@ __device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& s
     lds_barrier();  // the previous tile is done with LDS
     load_rows_norms<F32>(sm, cur, in, tid, q.k.zscale);
     uint32_t prev[4];
-    load_prev<VB>(q, cur, tid, prev);  // used at the end of the tile
+    // used at the end of the tile; values of up to 3 bits are packed in registers (lane-owned
+    // words), 4-bit values through LDS (thread-owned words)
+    load_prev<VB>(q, cur, tid, VB <= 3, prev);
     // the next tile's rows are in flight while this tile computes
     if (more) load_rows<F32>(q, nxt, tid, in);  // uniform
     lds_barrier();

@@ -119,16 +119,26 @@ __device__ __forceinline__ void load_rows(const QuantLaunch& q, const TileRef& r
   for (int i = 0; i < TileIn<F32>::NW; ++i) in.w[i] = *reinterpret_cast<const u32x4*>(src + 16 * i);
 }
 
-// For a value tile that does not cover its whole block: the value-code words it rewrites
-// (4 tokens share a word); zero otherwise.  VB: value code bits of the launch.
+// The VB value-code words of a block that thread tid packs and stores: lanemap = 0 (one-token
+// calls, packed from LDS): words VB (tid & 3) .. of chunk tid >> 2; lanemap = 1 (packed in the
+// rotation's register layout): words VB wave .. of chunk lane, wave = tid >> 6, lane = tid & 63.
 template <int VB>
-__device__ __forceinline__ void load_prev(const QuantLaunch& q, const TileRef& r, int tid, uint32_t* prev) {
+__device__ __forceinline__ int value_word_offset(int tid, bool lanemap) {
+  return lanemap ? (tid & 63) * 16 * VB + (tid >> 6) * 4 * VB : (tid >> 2) * 16 * VB + (tid & 3) * 4 * VB;
+}
+
+// For a value tile that does not cover its whole block: the value-code words it rewrites
+// (4 tokens share a field, 8 fields a thread's words); zero otherwise.  VB: value code bits of
+// the launch.
+template <int VB>
+__device__ __forceinline__ void load_prev(const QuantLaunch& q, const TileRef& r, int tid, bool lanemap,
+                                          uint32_t* prev) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) prev[i] = 0u;
   if (r.tensor == 1 && partial_tile(r)) {  // uniform
     const int64_t bh = (int64_t)r.b * q.Hkv + r.h;
     const uint32_t* pw = reinterpret_cast<const uint32_t*>(q.v.codes + (bh * (q.v.T_cap / 64) + r.blk) * (1024 * VB) +
-                                                           (tid >> 2) * 16 * VB + (tid & 3) * 4 * VB);
+                                                           value_word_offset<VB>(tid, lanemap));
 #pragma unroll
     for (int i = 0; i < VB; ++i) prev[i] = pw[i];
   }
@@ -295,6 +305,30 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
     cent[l] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.centroids[l])));
     thr[l] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.thresholds[l])));
   }
+  // Values of a multi-token call: lane (col, grp) of wave w holds rows 16 mt + 4 grp + i of output
+  // coordinate 32 w + 16 nt + col, which are exactly the 4 codes of value field 4 (2 w + nt) + mt
+  // of chunk col + 16 grp.  Its 8 fields (nt, mt) are that chunk's words VB w .. VB w + VB - 1,
+  // so the codes are packed in registers: field (nt, mt) at bit 4 VB (4 nt + mt), code i at
+  // + VB i.  (4-bit values keep the LDS path below: packing them in registers beside the 15-step
+  // code search spilled registers and made the c5 turbo4 bulk quantize 1.6x slower.  The words
+  // a partial tile rewrites are loaded with the matching ownership: load_prev's lanemap.)
+  constexpr bool VPACK = !KEY && BITS > 0 && BITS <= 3;
+  const bool lanepack = VPACK && !one;  // uniform
+  uint32_t vw[VPACK ? BITS : 1];
+#pragma unroll
+  for (int k = 0; k < (VPACK ? BITS : 1); ++k) vw[k] = 0u;
+  auto put_code = [&](int row, int o, int idx, int mt, int nt, int i) {
+    if constexpr (VPACK) {
+      if (lanepack) {
+        const int bit = 4 * BITS * (4 * nt + mt) + BITS * i;  // compile-time after unrolling
+        const int word = bit >> 5, off = bit & 31;
+        vw[word] |= static_cast<uint32_t>(idx) << off;
+        if (off + BITS > 32) vw[word + 1] |= static_cast<uint32_t>(idx) >> (32 - off);
+        return;
+      }
+    }
+    s_idx[row * IDX_STRIDE + o] = static_cast<uint8_t>(idx);
+  };
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     if (!mt_on[mt]) continue;
@@ -316,7 +350,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
           const bool b1 = z >= (b0 ? thr[5] : thr[1]);
           const float t2 = b0 ? (b1 ? thr[6] : thr[4]) : (b1 ? thr[2] : thr[0]);
           const int idx = (b0 ? 4 : 0) | (b1 ? 2 : 0) | (z >= t2 ? 1 : 0);
-          s_idx[row * IDX_STRIDE + o] = static_cast<uint8_t>(idx);
+          put_code(row, o, idx, mt, nt, i);
         } else if constexpr (BITS > 4) {
           // binary search over the 2^BITS - 1 sorted thresholds in LDS: after the step of
           // width w, the thresholds below idx are exactly those <= z among the ones seen
@@ -335,7 +369,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
             idx = ge ? l : idx;
             c = ge ? cent[l] : c;
           }
-          s_idx[row * IDX_STRIDE + o] = static_cast<uint8_t>(idx);
+          put_code(row, o, idx, mt, nt, i);
         }
         if constexpr (KEY && QJL) {
           // r = y - c / sqrt(d) = (z - c) / sqrt(d)
@@ -450,6 +484,41 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
           uint32_t w[1];
           pack32<1>(sv, w);
           *reinterpret_cast<uint32_t*>(a.signs + (bh * nblk + blk) * 1024 + Lc * 16 + part * 4) = w[0];
+        }
+      }
+    } else if (lanepack) {
+      // the words packed in registers during the code search
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + (bh * nblk + blk) * (1024 * BITS) +
+                                                  value_word_offset<BITS>(tid, true));
+      if (!partial) {
+#pragma unroll
+        for (int i = 0; i < (VPACK ? BITS : 1); ++i) dst[i] = vw[i];
+      } else {
+        // a tile that leaves other tokens of its block to other calls: the codes of rows outside
+        // [lo_slot, hi_slot) keep the words' previous bits (rows 16 mt + 4 grp + i)
+        uint32_t vm[VPACK ? BITS : 1];
+#pragma unroll
+        for (int k = 0; k < (VPACK ? BITS : 1); ++k) vm[k] = 0u;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int slot = p0 + 16 * mt + 4 * grp + i;
+              const uint32_t mk = (slot >= lo_slot && slot < hi_slot) ? ((1u << BITS) - 1u) : 0u;
+              const int bit = 4 * BITS * (4 * nt + mt) + BITS * i;
+              const int word = bit >> 5, off = bit & 31;
+              vm[word] |= mk << off;
+              if (off + BITS > 32) vm[word + 1] |= mk >> (32 - off);
+            }
+#pragma unroll
+        for (int i = 0; i < (VPACK ? BITS : 1); ++i) {
+          if (vm[i] == 0xFFFFFFFFu) {
+            dst[i] = vw[i];
+          } else if (vm[i] != 0u) {
+            dst[i] = (prev[i] & ~vm[i]) | (vw[i] & vm[i]);
+          }
         }
       }
     } else {
