@@ -382,6 +382,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   }
   lds_barrier();
 
+  uint32_t sword = 0u;  // keys with the sketch: this lane's sign word (see the sketch below)
   if constexpr (KEY && QJL) {
     // ---- residual norms; with more than one active sub-tile, r is split once into its three
     // exact bf16 terms (planes), else each wave splits the sub-tile's rows itself ----------------
@@ -416,6 +417,11 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
       }
     }
     // ---- sketch: u = S_b r, signs -----------------------------------------------------------
+    // Lane (col, grp) of wave w holds u of sketch rows 32 w + 16 nt + col for the rows (tokens)
+    // 16 mt + 4 grp + i, so two wave ballots of u >= 0 per (mt, i), one per nt, hold the 32-bit
+    // sign words (chunk rows 32 w .. 32 w + 31) of the four tokens 16 mt + 4 grp + i, grp = 0..3,
+    // in their 16-bit slices.  Lane (col, grp) keeps the word of token 16 (col / 4) + 4 grp +
+    // col % 4 and stores it below.
     const auto& sb = op.sb;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -445,14 +451,13 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
         }
       }
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int orow = 16 * mt + 4 * grp + i;
-          s_sgn[orow * IDX_STRIDE + 32 * wave + 16 * nt + col] = u[nt][i] >= 0.f ? 1 : 0;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const uint64_t b0 = __ballot(u[0][i] >= 0.f), b1 = __ballot(u[1][i] >= 0.f);
+        const uint32_t w = (static_cast<uint32_t>(b0 >> (16 * grp)) & 0xFFFFu) |
+                           (static_cast<uint32_t>(b1 >> (16 * grp)) << 16);
+        sword = col == 4 * mt + i ? w : sword;
+      }
     }
-    lds_barrier();
   }
 
   // ---- pack and store ------------------------------------------------------------------------
@@ -476,15 +481,15 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
 #pragma unroll
           for (int i = 0; i < BITS; ++i) dst[i] = w[i];
         }
-        if constexpr (QJL) {
-          uint8_t sv[32];
-          *reinterpret_cast<u32x4*>(sv) = *reinterpret_cast<const u32x4*>(s_sgn + sr * IDX_STRIDE + 32 * g);
-          *reinterpret_cast<u32x4*>(sv + 16) =
-              *reinterpret_cast<const u32x4*>(s_sgn + sr * IDX_STRIDE + 32 * g + 16);
-          uint32_t w[1];
-          pack32<1>(sv, w);
-          *reinterpret_cast<uint32_t*>(a.signs + (bh * nblk + blk) * 1024 + Lc * 16 + part * 4) = w[0];
-        }
+      }
+      if constexpr (QJL) {
+        // the sign word built from the ballots: token row 16 (col / 4) + 4 grp + col % 4 of this
+        // wave's chunk rows (a one-token call: lane 0 holds the word of row 0, the token)
+        const int rowk = one ? lo_slot - p0 : 16 * (col >> 2) + 4 * grp + (col & 3);
+        const int slot_k = p0 + rowk;
+        if ((!one || lane == 0) && slot_k >= lo_slot && slot_k < hi_slot)
+          *reinterpret_cast<uint32_t*>(a.signs + (bh * nblk + blk) * 1024 + ((rowk & 15) + 16 * wave) * 16 +
+                                       (rowk >> 4) * 4) = sword;
       }
     } else if (lanepack) {
       // the words packed in registers during the code search
