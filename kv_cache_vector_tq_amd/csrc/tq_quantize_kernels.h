@@ -151,10 +151,20 @@ __device__ __forceinline__ void quantize_workgroup(const QuantLaunch& q, Smem& s
     // the next tile's rows are in flight while this tile computes
     if (more) load_rows<F32>(q, nxt, tid, in);  // uniform
     lds_barrier();
-    if (cur.tensor == 0)
-      quantize_tile<true, KB, QJL, F32>(q.k, sm, op, cur, prev, tid, false, wtab);
-    else
-      quantize_tile<false, VB, false, F32>(q.v, sm, op, cur, prev, tid, false, nullptr);
+    // whole blocks (every tile of a bulk fill but the first and last of a row) take the
+    // instance without slot masks and sub-tile branches
+    const bool full = !partial_tile(cur);  // uniform
+    if (cur.tensor == 0) {
+      if (full)
+        quantize_tile<true, KB, QJL, F32, true>(q.k, sm, op, cur, prev, tid, false, wtab);
+      else
+        quantize_tile<true, KB, QJL, F32>(q.k, sm, op, cur, prev, tid, false, wtab);
+    } else {
+      if (full)
+        quantize_tile<false, VB, false, F32, true>(q.v, sm, op, cur, prev, tid, false, nullptr);
+      else
+        quantize_tile<false, VB, false, F32>(q.v, sm, op, cur, prev, tid, false, nullptr);
+    }
     if (!more) break;
     cur = nxt;
     t = tn;

@@ -216,10 +216,15 @@ __device__ __forceinline__ void load_rows_norms(Smem& sm, const TileRef& tr, con
 // a partial value tile rewrites (load_prev).  one: the tile's single token was loaded and is
 // computed as row 0 (a one-token call); only the stores use its slot.
 // wtab (5..8-bit keys only): the key table in LDS, 2^BITS levels then the thresholds.
-template <bool KEY, int BITS, bool QJL, bool F32>
+// FULL: the call writes the whole block (lo_slot = 64 blk, hi_slot = lo_slot + 64, not a
+// one-token call), so every sub-tile is active and no slot is masked: the bulk fill's tiles take
+// this instance, whose sub-tile loops have no branches for the compiler to schedule around.
+template <bool KEY, int BITS, bool QJL, bool F32, bool FULL = false>
 __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, const Operands& op, const TileRef& tr,
-                                              const uint32_t* prev, int tid, bool one, const float* wtab) {
-  const int b = tr.b, h = tr.h, blk = tr.blk, lo_slot = tr.lo_slot, hi_slot = tr.hi_slot;
+                                              const uint32_t* prev, int tid, bool one_call, const float* wtab) {
+  const int b = tr.b, h = tr.h, blk = tr.blk;
+  const int lo_slot = FULL ? 64 * blk : tr.lo_slot, hi_slot = FULL ? 64 * blk + 64 : tr.hi_slot;
+  const bool one = !FULL && one_call;
   constexpr int L = 1 << (BITS > 0 ? BITS : 1);
   float* s_tile = sm.tile;
   uint8_t* s_idx = sm.idx;
@@ -240,7 +245,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   }
   const int64_t bh = (int64_t)b * a.Hkv + h;
   const int nblk = a.T_cap / 64;
-  const bool partial = partial_tile(tr);  // uniform over the workgroup
+  const bool partial = !FULL && partial_tile(tr);  // uniform over the workgroup
 
 
   // ---- rotation: acc[mt][nt] = X[16 mt.., :] R[32 wave + 16 nt.., :]^T, R = r_hi + r_lo, or
