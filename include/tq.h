@@ -32,7 +32,7 @@
  *  - per process, read-only after first use and guarded by a mutex: the compute-unit count of
  *    each device, the f16 table factor of each codebook (a pure function of its levels), and
  *    the environment knobs TQ_ATTN_MIN_BLOCKS / TQ_ATTN_MGROUP (read once; they change only the
- *    context split of tq_attend_decode);
+ *    context split of tq_attend_decode); TQ_ATTN_REPL is read at every tq_attend_decode call;
  *  - per device: the fixed scratch array of tq_attend_decode_noalloc.
  */
 #ifndef TQ_H
@@ -244,7 +244,10 @@ int tq_quantize_kv(const tq_codebook* cb, const tq_dev_params* p, const void* k,
  *   the fp32 summation order, not the result's bound): TQ_ATTN_MIN_BLOCKS (default 2) is the
  *   smallest number of 64-key blocks a wave streams when the context is split over
  *   workgroups; TQ_ATTN_MGROUP (default 16, at most 32) is the number of context slices a
- *   first-level merge combines.
+ *   first-level merge combines.  TQ_ATTN_REPL (read at every call) selects the kernel instance
+ *   that keeps one copy of each 8-bit-key decode table per lane slot in LDS: 1 always, 0
+ *   never, unset when each wave streams at least 8 blocks.  The outputs are bit-identical
+ *   either way.
  * Errors: TQ_ERR_INVALID (NULL arguments, Hq not a multiple of Hkv, max_seq_len outside
  *   1..T_cap), TQ_ERR_UNSUPPORTED (group size or config), TQ_ERR_WORKSPACE (too small;
  *   required size written to *workspace_bytes), TQ_ERR_DEVICE (launch failure). */

@@ -306,6 +306,13 @@ int attend(const tq_codebook* cb, const tq_dev_params* p, const tq_kv_cache* cac
   ma.scores_out = scores_out;
   ma.blocks_per_wave = bpw;
   ma.n_slices = n_slices;
+  // decode tables replicated per lane slot when each wave streams REPL_MIN_BLOCKS blocks or
+  // more (building them costs more than they save on short streams); TQ_ATTN_REPL = 0 or 1
+  // forces them off or on (read at every call; the result is the same either way)
+  const char* repl_env = getenv("TQ_ATTN_REPL");
+  ma.repl = repl_env != nullptr && repl_env[0] == '0' ? 0
+            : repl_env != nullptr && repl_env[0] == '1' ? 1
+                                                        : (bpw >= REPL_MIN_BLOCKS ? 1 : 0);
   ma.mgroup = mgroup;
   const ProfileEvents& pe = profile_events();
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -440,6 +447,7 @@ extern "C" int tq_attend_prefill(const tq_codebook* cb, const tq_dev_params* p, 
   ma.NG = static_cast<int>(NG);
   ma.n_slices = 1;
   ma.mgroup = 1;
+  ma.repl = 1;
   const ProfileEvents& pe = profile_events();
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (pe.attend_start && pe.attend_stop) {

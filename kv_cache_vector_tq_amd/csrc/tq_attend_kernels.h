@@ -36,6 +36,7 @@ struct MainArgs {
   float* out;         // [B*Hq][128]
   float* scores_out;  // NULL or [B*Hq][T_cap]
   int Hkv, T_cap, max_seq_len, blocks_per_wave, n_slices, mgroup;
+  int repl;           // decode: replicated decode tables (the kernel instance; prefill always)
   float scale_log2;   // scale * log2(e)
   float scale;
   float k_cent[16];   // key centroids times a factor k_scale (table_scale in tq_attend.hip)
@@ -99,6 +100,7 @@ constexpr int MGROUP = 32;                       // slices per first-level merge
 constexpr int MAX_GROUPS = 32;                   // merge groups per (batch row, kv-head)
 constexpr int MAX_SLICES = MGROUP * MAX_GROUPS;  // context slices per (batch row, kv-head)
 constexpr int CNT_PER_UNIT = MAX_GROUPS + 1;     // arrival counters per (batch row, kv-head)
+constexpr int REPL_MIN_BLOCKS = 8;               // decode waves streaming this many blocks replicate tables
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -132,6 +134,26 @@ struct Tab {
   static constexpr int SHIFT = EBYTES == 16 ? 4 : (EBYTES == 8 ? 3 : (EBYTES == 4 ? 2 : 1));
   static constexpr int BYTES = (1 << K) * EBYTES;
 };
+
+// Geometry of Tab<B> as constexpr functions of a runtime-free B (0: no table).
+constexpr int tab_k(int B) { return B > 4 ? B : (B == 3 ? 12 : 8); }
+constexpr int tab_ebytes(int B) { return B > 4 ? 4 : 2 * (tab_k(B) / B); }
+constexpr int tab_bytes(int B) { return B == 0 ? 0 : (1 << tab_k(B)) * tab_ebytes(B); }
+
+// How a lookup finds its entry in LDS.  PTR: the table sits below 64 KB and the entry's byte
+// offset is added to the table's address (the constant part travels in the instruction's offset
+// field).  ORB: a 12-bit-key table at a 32 KB-aligned base anywhere in LDS; mask and base come
+// from registers (lo = base, mk = mask), so one AND-OR replaces the mask alone.  REP: a
+// replicated 8-bit-key table (below).
+enum { PTR = 0, ORB = 1, REP = 2 };
+
+// A replicated table (8-bit keys, B = 1, 2 or 4): entry e fills the 256 bytes at base + 256 e
+// with 256 / EBYTES copies of itself, and lane slot c = lane mod (256 / EBYTES) reads copy c.
+// The lanes of a wave then read disjoint banks whatever their keys (random keys into one copy
+// collide in the banks: measured at several percent of the batch-16 128K-context decode), and
+// the address base + 256 e + EBYTES c is one byte permute of the code word and a per-lane
+// constant lo = EBYTES c + base (base a multiple of 64 KB, in byte 2).
+constexpr int REP_BYTES = 256 * 256;
 
 __device__ __forceinline__ uint32_t pack_f16x2(_Float16 a, _Float16 b) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
@@ -182,6 +204,35 @@ __device__ void build_table(uint8_t* tab, const float* cent, int tid) {
   }
 }
 
+// Fills the replicated table of B-bit codes (B = 1, 2, 4; SIGN: the -1 / +1 values of sign
+// bits) at tab: two threads per entry, each writing half of its 256-byte row.
+template <int B, bool SIGN>
+__device__ void build_table_rep(uint8_t* tab, const float* cent, int tid) {
+  static_assert(tab_k(B) == 8 && NT == 512, "replicated tables: 8-bit keys, two threads per entry");
+  constexpr int L = 1 << B, CPL = 8 / B;
+  _Float16 c16[L];
+#pragma unroll
+  for (int l = 0; l < L; ++l) c16[l] = SIGN ? static_cast<_Float16>(l ? 1.0f : -1.0f) : static_cast<_Float16>(cent[l]);
+  const int e = tid >> 1, half = tid & 1;
+  uint16_t v[8];  // the entry's CPL values, repeated to 16 bytes
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const int code = (e >> (B * (h % CPL))) & (L - 1);
+    _Float16 x = c16[0];
+#pragma unroll
+    for (int l = 1; l < L; ++l) x = code == l ? c16[l] : x;  // no dynamic register indexing
+    v[h] = __builtin_bit_cast(uint16_t, x);
+  }
+  u32x4 w;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) w[h] = static_cast<uint32_t>(v[2 * h]) | (static_cast<uint32_t>(v[2 * h + 1]) << 16);
+  // the 8 chunks of the half row in an order rotated by the entry: the 64 lanes of a store then
+  // spread over all banks (in order, every lane's chunk would sit in the same two bank groups)
+  u32x4* dst = reinterpret_cast<u32x4*>(tab + 256 * e + 128 * half);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dst[(j + e) & 7] = w;
+}
+
 // Bits P .. P+N-1 of the little-endian dword array dw, shifted left by S.
 template <int P, int N, int S>
 __device__ __forceinline__ uint32_t field(const uint32_t* dw) {
@@ -197,23 +248,50 @@ __device__ __forceinline__ uint32_t field(const uint32_t* dw) {
   }
 }
 
-// The 8 codes (B bits each, or sign bits for B = 1 in the sign table) starting at bit P of dw ->
-// f16x8, through table Tab<B> at tab.
-template <int B, int P>
-__device__ __forceinline__ f16x8 decode8(const uint32_t* dw, const uint8_t* tab) {
+// Byte address (relative to tab) of the entry of the key at bit P of dw in a table of mode MODE
+// at LDS offset OFF (see PTR, ORB, REP).
+template <int B, int P, int MODE, int OFF>
+__device__ __forceinline__ uint32_t entry(const uint32_t* dw, uint32_t lo, uint32_t mk) {
   using T = Tab<B>;
-  constexpr int K = T::K, S = T::SHIFT;
+  if constexpr (MODE == REP) {
+    static_assert(T::K == 8 && P % 8 == 0, "replicated tables take byte-aligned 8-bit keys");
+    // bytes: lo.0 (lane slot), the key byte, lo.2 (base / 64 KB), 0
+    constexpr uint32_t sel = 0x0C020000u | ((4u + (P / 8) % 4) << 8);
+    return __builtin_amdgcn_perm(dw[P / 32], lo, sel);
+  } else if constexpr (MODE == ORB) {
+    static_assert(T::K == 12 && OFF % 32768 == 0, "OR-ed bases: 12-bit keys, 32 KB-aligned tables");
+    // the field of field<P, 12, SHIFT> before its mask, then (x & mk) | lo with mk = the mask
+    constexpr int w = P >> 5, o = P & 31, S = T::SHIFT;
+    uint32_t x;
+    if constexpr (o + T::K > 32)
+      x = __builtin_amdgcn_alignbit(dw[w + 1], dw[w], o - S);
+    else if constexpr (o >= S)
+      x = dw[w] >> (o - S);
+    else
+      x = dw[w] << (S - o);
+    return (x & mk) | lo;
+  } else {
+    return field<P, T::K, T::SHIFT>(dw);
+  }
+}
+
+// The 8 codes (B bits each, or sign bits for B = 1 in the sign table) starting at bit P of dw ->
+// f16x8, through table Tab<B>: at tab (MODE PTR) or at the workgroup's LDS base tab (ORB, REP).
+template <int B, int P, int MODE = PTR, int OFF = 0>
+__device__ __forceinline__ f16x8 decode8(const uint32_t* dw, const uint8_t* tab, uint32_t lo = 0, uint32_t mk = 0) {
+  using T = Tab<B>;
+  constexpr int K = T::K;
   if constexpr (T::EBYTES == 16) {
-    return *reinterpret_cast<const f16x8*>(tab + field<P, K, S>(dw));
+    return *reinterpret_cast<const f16x8*>(tab + entry<B, P, MODE, OFF>(dw, lo, mk));
   } else if constexpr (T::EBYTES == 8) {
-    const u32x2 x = *reinterpret_cast<const u32x2*>(tab + field<P, K, S>(dw));
-    const u32x2 y = *reinterpret_cast<const u32x2*>(tab + field<P + K, K, S>(dw));
+    const u32x2 x = *reinterpret_cast<const u32x2*>(tab + entry<B, P, MODE, OFF>(dw, lo, mk));
+    const u32x2 y = *reinterpret_cast<const u32x2*>(tab + entry<B, P + K, MODE, OFF>(dw, lo, mk));
     return __builtin_bit_cast(f16x8, u32x4{x[0], x[1], y[0], y[1]});
   } else {
-    return __builtin_bit_cast(f16x8, u32x4{*reinterpret_cast<const uint32_t*>(tab + field<P, K, S>(dw)),
-                                           *reinterpret_cast<const uint32_t*>(tab + field<P + K, K, S>(dw)),
-                                           *reinterpret_cast<const uint32_t*>(tab + field<P + 2 * K, K, S>(dw)),
-                                           *reinterpret_cast<const uint32_t*>(tab + field<P + 3 * K, K, S>(dw))});
+    return __builtin_bit_cast(f16x8, u32x4{*reinterpret_cast<const uint32_t*>(tab + entry<B, P, MODE, OFF>(dw, lo, mk)),
+                                           *reinterpret_cast<const uint32_t*>(tab + entry<B, P + K, MODE, OFF>(dw, lo, mk)),
+                                           *reinterpret_cast<const uint32_t*>(tab + entry<B, P + 2 * K, MODE, OFF>(dw, lo, mk)),
+                                           *reinterpret_cast<const uint32_t*>(tab + entry<B, P + 3 * K, MODE, OFF>(dw, lo, mk))});
   }
 }
 
@@ -361,7 +439,7 @@ __device__ __forceinline__ Merged merge_records(const float* hs, int count, int 
 }
 
 
-template <int KB, bool QJL, int VB, int G>
+template <int KB, bool QJL, int VB, int G, bool REPL>
 struct MainCfg {
   static constexpr int TPD = 16 / G;       // score tiles packed into one accumulator set
   static constexpr int NSETS = 4 / TPD;    // accumulator sets per 64-key block
@@ -391,17 +469,83 @@ struct MainCfg {
     return r;
   }
   static constexpr bool SHARED = (KB == VB);  // one table serves keys and values
-  static constexpr int KTAB = KB > 0 ? Tab<(KB > 0 ? KB : 1)>::BYTES : 0;
-  static constexpr int STAB = QJL ? Tab<1>::BYTES : 0;
-  static constexpr int VTAB = SHARED ? 0 : Tab<VB>::BYTES;
-  static constexpr int KOFF = 0, SOFF = KTAB, VOFF = SHARED ? 0 : KTAB + STAB;
-  // the G query records are staged behind the tables before the block loop (the epilogue,
-  // which aliases both, comes after it)
+  // ---- LDS layout of the decode tables.  Roles 0 = key codes, 1 = signs, 2 = value codes (none
+  // when SHARED), each a Tab<B> (B = 0: no table).  With REPL, 8-bit-key tables are replicated
+  // (REP, 64 KB each) as far as they fit in the 160 KB of LDS: signs first, then key codes, then
+  // value codes.  Tables that are not replicated sit below 64 KB (PTR) unless their keys are
+  // 12-bit (ORB: anywhere, 32 KB-aligned).  The G query records are staged behind the tables
+  // when they fit there, else over the start of the table space before the tables are built
+  // (QALIAS).  The epilogue reuses the whole space after the block loop.  Replication pays on
+  // long streams; its 64 KB stores per table and the serialized build of QALIAS cost more than
+  // they save on launches of a few blocks per wave, which keep REPL off.
+  static constexpr int LDS_MAX = 160 * 1024;
+  static constexpr int RB0 = KB, RB1 = QJL ? 1 : 0, RB2 = SHARED ? 0 : VB;
+  static constexpr int rb(int r) { return r == 0 ? RB0 : (r == 1 ? RB1 : RB2); }
+  static constexpr bool repable(int r) { return rb(r) == 1 || rb(r) == 2 || rb(r) == 4; }
   static constexpr int QSTAGE = G * QREC * 4;
-  static constexpr int TABLES = KTAB + STAB + VTAB;
-  // the epilogue reuses the table space once every wave has left the block loop
   static constexpr int MERGE = static_cast<int>(sizeof(Epi));
-  static constexpr int LDS = TABLES + QSTAGE > MERGE ? TABLES + QSTAGE : MERGE;
+  struct Plan {
+    int mode[3], off[3], tables, lds;
+    bool qalias, fits;
+  };
+  static constexpr Plan plan(int mask) {  // mask: roles asked to be replicated
+    Plan pl{{PTR, PTR, PTR}, {0, 0, 0}, 0, 0, false, true};
+    int low = 0;
+    bool any_rep = false;
+    for (int r = 0; r < 3; ++r) any_rep = any_rep || (rb(r) != 0 && ((mask >> r) & 1) && repable(r));
+    for (int r = 0; r < 3; ++r) {
+      const bool rep = ((mask >> r) & 1) && repable(r);
+      if (rb(r) == 0) continue;
+      if (rep) {
+        pl.mode[r] = REP;
+      } else if (rb(r) == 3 && any_rep) {  // without replication every table stays below 64 KB
+        pl.mode[r] = ORB;
+      } else {
+        pl.mode[r] = PTR;
+        pl.off[r] = low;
+        low += tab_bytes(rb(r));
+      }
+    }
+    if (low > 65536) pl.fits = false;
+    int pos = low;
+    if (any_rep) {
+      pos = low == 0 ? 0 : 65536;
+      for (int r = 0; r < 3; ++r)
+        if (rb(r) != 0 && pl.mode[r] == REP) {
+          pl.off[r] = pos;
+          pos += REP_BYTES;
+        }
+    }
+    for (int r = 0; r < 3; ++r)
+      if (rb(r) != 0 && pl.mode[r] == ORB) {
+        pos = (pos + 32767) / 32768 * 32768;
+        pl.off[r] = pos;
+        pos += tab_bytes(rb(r));
+      }
+    pl.tables = pos;
+    pl.qalias = pos + QSTAGE > LDS_MAX;
+    const int used = pl.qalias ? pos : pos + QSTAGE;
+    pl.lds = used > MERGE ? used : MERGE;
+    if (pl.lds > LDS_MAX || pos > LDS_MAX || (pl.qalias && QSTAGE > pos)) pl.fits = false;
+    return pl;
+  }
+  static constexpr Plan choose() {
+    // replication sets by preference: all, {S, K}, {S, V}, {K, V}, {S}, {K}, {V}, none
+    constexpr int order[8] = {7, 3, 6, 5, 2, 1, 4, 0};
+    for (int i = 0; i < 8; ++i) {
+      const Plan pl = plan(order[i]);
+      if (pl.fits) return pl;
+    }
+    return plan(0);
+  }
+  static constexpr Plan PL = REPL ? choose() : plan(0);
+  static constexpr int KMODE = PL.mode[0], SMODE = PL.mode[1], VMODE = SHARED ? PL.mode[0] : PL.mode[2];
+  static constexpr int KOFF = PL.off[0], SOFF = PL.off[1], VOFF = SHARED ? PL.off[0] : PL.off[2];
+  static constexpr int TABLES = PL.tables;
+  static constexpr bool QALIAS = PL.qalias;
+  static constexpr int QOFF = QALIAS ? 0 : TABLES;
+  static constexpr int LDS = PL.lds;
+  static constexpr bool FITS = PL.fits;
 };
 
 // Streams the 64-key blocks of one slice.  SCORES: also write the logits (parity runs).
@@ -410,11 +554,11 @@ struct MainCfg {
 // unit, whose 8 waves split the unit's blocks; queries are rotated in the kernel; outputs are
 // written directly.  (Eight columns rather than sixteen keep the hi and lo query terms in the
 // columns of one accumulator, which halves the query operands held in registers.)
-template <int KB, bool QJL, int VB, int G, bool SCORES, bool PRE>
+template <int KB, bool QJL, int VB, int G, bool SCORES, bool PRE, bool REPL>
 __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent<KB> kcent) {
   constexpr int GC = PRE ? (G > 8 ? G : 8) : G;  // query columns per unit
   constexpr int QPG = GC / G;                     // prefill: query positions per unit
-  using C = MainCfg<KB, QJL, VB, GC>;
+  using C = MainCfg<KB, QJL, VB, GC, REPL>;
   constexpr int TPD = C::TPD, NSETS = C::NSETS;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
   constexpr int KBT = KB > 0 ? KB : 1;  // key code width of the (unused when KB = 0) key table
@@ -486,7 +630,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
   };
   constexpr int QWORDS = GC * QREC / 4;
   constexpr int QPT = PRE ? 1 : (QWORDS + NT - 1) / NT;
-  float* const qst = reinterpret_cast<float*>(smem + C::TABLES);
+  float* const qst = reinterpret_cast<float*>(smem + C::QOFF);
   f32x4 qw[QPT];
   if constexpr (!PRE) {
     const float* qsrc = a.qrec + ((int64_t)b * Hq + kvh * G) * QREC;
@@ -495,19 +639,32 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
   }
   // The G query records of this kv-head (contiguous) go through LDS: one 16-byte load per
   // thread (two for G = 16), issued before the block loads, so that no wave's query waits
-  // behind other waves' block loads.
+  // behind other waves' block loads.  (Each lane loading its own 256 bytes of records instead
+  // measured 10 % slower on the 32K-context Llama-3.1-8B layer.)
   // Block loads are unconditional, from clamped (always in-bounds) block indices: a load under
   // a branch would make the compiler wait for every load in flight where the branches join,
   // which would serialize the prefetch with the current block's compute.
   Blk cur, nxt;
   load_block(min(blk_begin, nblk_cap - 1), cur);  // in flight while the tables are built
 
-  if constexpr (KB > 4)
-    build_table<KBT, false>(smem + C::KOFF, kcent.c, tid);
-  else if constexpr (KB > 0)
-    build_table<KBT, false>(smem + C::KOFF, a.k_cent, tid);
-  if constexpr (QJL) build_table<1, true>(smem + C::SOFF, nullptr, tid);
-  if constexpr (!C::SHARED) build_table<VB, false>(smem + C::VOFF, a.v_cent, tid);
+  auto build_tables = [&]() {
+    if constexpr (KB > 4)
+      build_table<KBT, false>(smem + C::KOFF, kcent.c, tid);
+    else if constexpr (KB > 0 && C::KMODE == REP)
+      build_table_rep<KBT, false>(smem + C::KOFF, a.k_cent, tid);
+    else if constexpr (KB > 0)
+      build_table<KBT, false>(smem + C::KOFF, a.k_cent, tid);
+    if constexpr (QJL && C::SMODE == REP)
+      build_table_rep<1, true>(smem + C::SOFF, nullptr, tid);
+    else if constexpr (QJL)
+      build_table<1, true>(smem + C::SOFF, nullptr, tid);
+    if constexpr (!C::SHARED && C::VMODE == REP)
+      build_table_rep<VB, false>(smem + C::VOFF, a.v_cent, tid);
+    else if constexpr (!C::SHARED)
+      build_table<VB, false>(smem + C::VOFF, a.v_cent, tid);
+  };
+  // with the query records staged over the table space, the tables follow the operands below
+  if constexpr (!C::QALIAS) build_tables();
   if constexpr (PRE) {
     // waves 0..3 rotate the unit's 16 queries, 32 output coordinates each, into the records
     if (wave < 4) {
@@ -522,7 +679,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
     for (int k = 0; k < QPT; ++k)
       if (tid + k * NT < QWORDS) *reinterpret_cast<f32x4*>(qst + 4 * (tid + k * NT)) = qw[k];
   }
-  __syncthreads();  // tables and query records ready
+  __syncthreads();  // query records (and tables unless they follow below) ready
   // Score operands.  For q-head hh = col % G: x1 = q1 c1 and x2 = q2 c2 with the constant factors
   // of the score folded in (c1 = log2(e) scale / sqrt(d) / k_scale (/ sqrt(d) in one-pass
   // rotation mode): the key term is q1 . c / sqrt(d); c2 = log2(e) scale sqrt(pi/2) / m: the sign
@@ -609,6 +766,31 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
     }
   }
 
+  if constexpr (C::QALIAS) {
+    __syncthreads();  // every wave has read the query records
+    build_tables();
+    __syncthreads();  // tables ready
+  }
+  // Per-lane constants of the replicated tables: the lane slot's byte offset in an entry's row,
+  // and the table's base / 64 KB in byte 2.
+  auto rep_lo = [&](int B, int off) -> uint32_t {
+    const int eb = tab_ebytes(B);
+    return static_cast<uint32_t>((lane & (256 / eb - 1)) * eb) | (static_cast<uint32_t>(off >> 16) << 16);
+  };
+  // ORB tables: base and mask as register values (an instruction takes one constant operand)
+  uint32_t orb_mask = (0xFFFu << 3);
+  if constexpr (C::KMODE == ORB || C::VMODE == ORB) asm volatile("" : "+v"(orb_mask));
+  auto lo_of = [&](int mode, int B, int off) -> uint32_t {
+    if (mode == REP) return rep_lo(B, off);
+    return mode == ORB ? static_cast<uint32_t>(off) : 0u;
+  };
+  uint32_t lo_k = lo_of(C::KMODE, KBT, C::KOFF), lo_s = lo_of(C::SMODE, 1, C::SOFF), lo_v = lo_of(C::VMODE, VB, C::VOFF);
+  if constexpr (C::KMODE == ORB) asm volatile("" : "+v"(lo_k));
+  if constexpr (C::VMODE == ORB) asm volatile("" : "+v"(lo_v));
+  uint8_t* const ktab = C::KMODE == PTR ? smem + C::KOFF : smem;
+  uint8_t* const stab = C::SMODE == PTR ? smem + C::SOFF : smem;
+  uint8_t* const vtab = C::VMODE == PTR ? smem + C::VOFF : smem;
+
   // One block: scores, online softmax, value sums.  `d` holds the block's codes, `nrm` its norms.
   auto process = [&](const Blk& cur, const Norms& nrm, int blk) {
 
@@ -636,14 +818,14 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
               d = mfma_f16(kh, bc[ac][kb], d);
               d = mfma_f16(kl, bc[ac][kb], d);
             } else {
-              d = mfma_f16(decode8<KBT, P>(cur.kd, smem + C::KOFF), bc[ac][kb], d);
+              d = mfma_f16(decode8<KBT, P, C::KMODE, C::KOFF>(cur.kd, ktab, lo_k, orb_mask), bc[ac][kb], d);
             }
           });
         }
         if constexpr (QJL && C::has_s(ac)) {
           static_for<0, 4>([&](auto KB_) {
             constexpr int kb = decltype(KB_)::value;
-            d = mfma_f16(decode8<1, 32 * t + 8 * kb>(cur.sd, smem + C::SOFF), bsg[ac][kb], d);
+            d = mfma_f16(decode8<1, 32 * t + 8 * kb, C::SMODE, C::SOFF>(cur.sd, stab, lo_s), bsg[ac][kb], d);
           });
         }
         v[ac] = d;
@@ -754,7 +936,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
       const f16x8 bp = __builtin_bit_cast(f16x8, bpw);
       static_for<0, 8>([&](auto MT) {
         constexpr int mt = decltype(MT)::value;
-        const f16x8 av = decode8<VB, 8 * VB * (2 * mt + kb2)>(cur.vd, smem + C::VOFF);
+        const f16x8 av = decode8<VB, 8 * VB * (2 * mt + kb2), C::VMODE, C::VOFF>(cur.vd, vtab, lo_v, orb_mask);
         acc[mt] = mfma_f16(av, bp, acc[mt]);
       });
     });
@@ -984,11 +1166,15 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
 template <int KB, bool QJL, int VB, int G>
 hipError_t launch_main(const MainArgs& a, const attn::KeyCent<KB>& kc, int n_slices, int B, bool pre, hipStream_t s,
                        hipEvent_t e0, hipEvent_t e1) {
-  static_assert(MainCfg<KB, QJL, VB, G>::LDS <= 64 * 1024, "attention LDS budget");
-  static_assert(MainCfg<KB, QJL, VB, (G > 8 ? G : 8)>::LDS <= 64 * 1024, "prefill LDS budget");
-  auto kern = pre ? attend_kernel<KB, QJL, VB, G, false, true>
-                  : (a.scores_out != nullptr ? attend_kernel<KB, QJL, VB, G, true, false>
-                                             : attend_kernel<KB, QJL, VB, G, false, false>);
+  static_assert(MainCfg<KB, QJL, VB, G, false>::FITS && MainCfg<KB, QJL, VB, G, true>::FITS, "attention LDS budget");
+  static_assert(MainCfg<KB, QJL, VB, (G > 8 ? G : 8), true>::FITS, "prefill LDS budget");
+  const bool repl = a.repl != 0;
+  auto kern = pre ? attend_kernel<KB, QJL, VB, G, false, true, true>
+                  : (a.scores_out != nullptr
+                         ? (repl ? attend_kernel<KB, QJL, VB, G, true, false, true>
+                                 : attend_kernel<KB, QJL, VB, G, true, false, false>)
+                         : (repl ? attend_kernel<KB, QJL, VB, G, false, false, true>
+                                 : attend_kernel<KB, QJL, VB, G, false, false, false>));
   // decode: (slices, kv-heads, rows); prefill: (kv-heads x query groups, 1, rows)
   const dim3 grid = pre ? dim3(a.Hkv * a.NG, 1, B) : dim3(n_slices, a.Hkv, B);
   if (e0 != nullptr || e1 != nullptr)

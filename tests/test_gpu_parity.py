@@ -2,6 +2,8 @@
 
 Every call goes through libtq's C ABI (kv_cache_vector_tq_amd binds it with ctypes).
 """
+import contextlib
+import os
 import sys
 
 import numpy as np
@@ -22,6 +24,25 @@ import kv_cache_vector_tq_amd as tq  # noqa: E402
 def say(*a):
     print("[gpu]", *a, flush=True)
     sys.stdout.flush()
+
+
+@contextlib.contextmanager
+def attention_tables(repl):
+    """TQ_ATTN_REPL for the calls inside: "1" forces the attention kernel instance with decode
+    tables replicated per lane slot (chosen by itself only for long streams), "auto" leaves the
+    choice to the library."""
+    old = os.environ.get("TQ_ATTN_REPL")
+    if repl == "auto":
+        os.environ.pop("TQ_ATTN_REPL", None)
+    else:
+        os.environ["TQ_ATTN_REPL"] = repl
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("TQ_ATTN_REPL", None)
+        else:
+            os.environ["TQ_ATTN_REPL"] = old
 
 
 def _setup(preset, B, Hkv, T_cap, seed=0, zero=True, rotation="haar"):
@@ -263,7 +284,8 @@ def test_many_units_partial_tiles(preset):
 
 
 @pytest.mark.parametrize("preset,G", [("turbo3", 4), ("turbo4", 8), ("qjl1", 8), ("turbo3", 16)])
-def test_attention_ragged_lengths(preset, G):
+@pytest.mark.parametrize("repl", ["auto", "1"])
+def test_attention_ragged_lengths(preset, G, repl):
     """Different sequence lengths per batch row (1, partial blocks, several slices)."""
     B, Hkv, T_cap = 4, 2, 2048
     cb, dp, cache = _setup(preset, B, Hkv, T_cap)
@@ -277,8 +299,9 @@ def test_attention_ragged_lengths(preset, G):
     lens = [1, 63, 1000, 2048]
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     scores = torch.zeros((B, Hkv * G, T_cap), dtype=torch.float32, device="cuda")
-    say("ragged-attn", preset, G, "attend")
-    out = tq.tq_attend_decode(cb, dp, cache, H.to_device(Q, "bf16"), seq, T_cap, scores_out=scores)
+    say("ragged-attn", preset, G, "attend", "tables", repl)
+    with attention_tables(repl):
+        out = tq.tq_attend_decode(cb, dp, cache, H.to_device(Q, "bf16"), seq, T_cap, scores_out=scores)
     torch.cuda.synchronize()
     hc, out, scores = H.cache_host(cache), out.cpu().numpy(), scores.cpu().numpy()
     orc = H.make_oracle(preset)
@@ -392,7 +415,8 @@ def test_hadamard_rotation(preset, G, dtype):
                                    ((0, 1, 1), 4), ((2, 1, 1), 16),
                                    ((8, 0, 4), 4), ((8, 1, 4), 8), ((5, 1, 3), 16), ((6, 0, 2), 8),
                                    ((7, 1, 4), 4), ((8, 0, 4), 16), ((5, 0, 1), 4), ((6, 1, 2), 4)])
-def test_bit_mix_variants(cfg, G):
+@pytest.mark.parametrize("repl", ["auto", "1"])
+def test_bit_mix_variants(cfg, G, repl):
     B, Hkv, T_cap = 2, 2, 4096
     lens = [4096, 2500]
     cb, dp, cache = _setup(cfg, B, Hkv, T_cap)
@@ -405,8 +429,9 @@ def test_bit_mix_variants(cfg, G):
                       torch.zeros(B, dtype=torch.int32, device="cuda"))
     seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
     scores = torch.zeros((B, Hkv * G, T_cap), dtype=torch.float32, device="cuda")
-    say("bit-mix", cfg, G, "attend")
-    out = tq.tq_attend_decode(cb, dp, cache, H.to_device(Q, "bf16"), seq, T_cap, scores_out=scores)
+    say("bit-mix", cfg, G, "attend", "tables", repl)
+    with attention_tables(repl):
+        out = tq.tq_attend_decode(cb, dp, cache, H.to_device(Q, "bf16"), seq, T_cap, scores_out=scores)
     torch.cuda.synchronize()
     hc, out, scores = H.cache_host(cache), out.cpu().numpy(), scores.cpu().numpy()
     orc = H.make_oracle(cfg)
