@@ -330,12 +330,13 @@ __device__ __forceinline__ float col_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The value of the lane N columns further on within its row of 16 lanes (row rotation), an
-// operand modifier of the add that consumes it.
+// The value of the lane N columns before this one, cyclically within its row of 16 lanes (row
+// rotation right), an operand modifier of the add that consumes it.  Every lane has a source,
+// so the destination's previous value is never kept: it is left undefined (no zeroing move).
 template <int N>
 __device__ __forceinline__ float row_ror(float v) {
   static_assert(N > 0 && N < 16, "rotation within a row");
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + N, 0xF, 0xF, true));
 }
 
 template <int N>
@@ -595,8 +596,9 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
   const int blk_end = min(blk_begin + bpw, nblk);
 
   // online softmax per lane column: m_run (log2 domain), l_run = sum 2^(lg - m_run);
-  // acc = sum P' V with P' = 2^(lg - m_run) nv / s_run and s_run >= every such product
-  float m_run = NEG_BIG, l_run = 0.f, s_run = 0.f;
+  // acc = sum P' V with P' = 2^(lg - m_run) nv / s_run and s_run >= 2^-12 times every such
+  // product (inv_run = 1 / s_run)
+  float m_run = NEG_BIG, l_run = 0.f, s_run = 0.f, inv_run = 0.f;
   f32x4 acc[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -802,6 +804,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
     // other one).  Each lane keeps the pair (p, q) of the tile of its column class in every set
     // (tile s TPD + tcls of set s) ------------------------------------------------------------
     f32x4 cp[NSETS], cq[NSETS];
+    [[maybe_unused]] f32x4 pm[4];  // shared accumulator: each tile's column sums (C or S by part)
     static_for<0, 4>([&](auto T_) {
       constexpr int t = decltype(T_)::value;
       f32x4 v[C::NA];
@@ -833,10 +836,8 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
       f32x4 p, q = f32x4{0.f, 0.f, 0.f, 0.f};
       if constexpr (C::MIXED) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = v[0][i] + row_ror<2 * GC>(v[0][i]);
-          q[i] = row_ror<GC>(p[i]);
-        }
+        for (int i = 0; i < 4; ++i) pm[t][i] = v[0][i] + row_ror<2 * GC>(v[0][i]);
+        return;  // tiles are selected below, once all four are summed
       } else if constexpr (C::NP >= 2) {  // NA = 1 (one kind of term) or 2 (C, S): hi, lo parts
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -858,6 +859,23 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
         }
       }
     });
+    if constexpr (C::MIXED) {
+      // The lane of part k (= its tile class) keeps tile k's sum and takes tile k's other sum
+      // from the lane of part k - 1 (the rotation's source), which offers its tile k (one row
+      // rotation by G columns instead of one per tile).
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float own = pm[0][i], offer = pm[1][i];
+        own = part == 1 ? pm[1][i] : own;
+        own = part == 2 ? pm[2][i] : own;
+        own = part == 3 ? pm[3][i] : own;
+        offer = part == 1 ? pm[2][i] : offer;
+        offer = part == 2 ? pm[3][i] : offer;
+        offer = part == 3 ? pm[0][i] : offer;
+        cp[0][i] = own;
+        cq[0][i] = row_ror<GC>(offer);
+      }
+    }
     // logit * log2(e) = n (u1 C + u2 rnorm S): C, S are p, q (or q, p in the odd parts of a
     // shared accumulator); with one kind of term, p alone
     const bool odd = C::MIXED && (part & 1);
@@ -894,12 +912,18 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
     }
     mb = col_max(mb);
     mvb = col_max(mvb);
-    const float m_new = fmaxf(m_run, mb);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // Lazy rescaling: a column keeps its (m_run, s_run) while the block's weights P' under them
+    // stay at most 2^12 (f16 holds such weights as exactly as weights below 1) and its logits
+    // within 2^32 of m_run; otherwise both move to the block's bounds, with weights at most 1.
+    // The accumulator is rescaled only when some column moved.  (Detecting an unchanged scale
+    // from f = s rcp(s) instead fails most of the time: that product is not exactly 1 in fp32.)
+    const bool keep = mb <= m_run + 32.f && __builtin_amdgcn_exp2f(mvb - m_run) <= s_run * 4096.f;
+    const float m_new = keep ? m_run : fmaxf(m_run, mb);
+    const float alpha = keep ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
     const float s_scaled = s_run * alpha;
-    const float s_new = fmaxf(s_scaled, __builtin_amdgcn_exp2f(mvb - m_new));
-    const float inv = s_new > 0.f ? __builtin_amdgcn_rcpf(s_new) : 0.f;
-    const float f = s_new > 0.f ? s_scaled * inv : 1.0f;
+    const float s_new = keep ? s_run : fmaxf(s_scaled, __builtin_amdgcn_exp2f(mvb - m_new));
+    const float inv = keep ? inv_run : (s_new > 0.f ? __builtin_amdgcn_rcpf(s_new) : 0.f);
+    const float f = (keep || !(s_new > 0.f)) ? 1.0f : s_scaled * inv;
     if (__any(f != 1.0f)) {  // rescale only when some column's scale moved
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[mt] *= f;
@@ -913,13 +937,14 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
       for (int i = 0; i < 4; ++i) {
         const float pr = __builtin_amdgcn_exp2f(lg[s][i] - m_new);  // 0 for keys past the sequence
         lsum += pr;
-        x[i] = pr > 0.f ? fminf(pr * nrm.vn[s][i] * inv, 1.0f) : 0.f;
+        x[i] = pr > 0.f ? fminf(pr * nrm.vn[s][i] * inv, 4096.f) : 0.f;
       }
       pw[s][0] = pack_f16x2(static_cast<_Float16>(x[0]), static_cast<_Float16>(x[1]));
       pw[s][1] = pack_f16x2(static_cast<_Float16>(x[2]), static_cast<_Float16>(x[3]));
     }
     m_run = m_new;
     s_run = s_new;
+    inv_run = inv;
     l_run = fmaf(l_run, alpha, lsum);
 
     // ---- value MFMAs: k-block kb2 holds tiles 2 kb2 (elements 0..3) and 2 kb2 + 1 (4..7) ---
@@ -942,7 +967,8 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
     });
   };
   // Two blocks per iteration with the buffers swapping roles, so that the prefetched block never
-  // has to be copied into the current one.
+  // has to be copied into the current one.  (Loading the next block's norms one block ahead as
+  // well measured neutral on the long streams and slower on short launches.)
   for (int blk = blk_begin; blk < blk_end; blk += 2) {
     {
       Norms nrm;
