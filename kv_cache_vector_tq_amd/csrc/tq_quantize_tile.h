@@ -304,10 +304,14 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   // The codebook as wave-uniform register values (readfirstlane), so that the compare chain
   // selects values rather than addresses of the argument block.
   constexpr int LR = BITS <= 4 ? L : 1;  // wide tables stay in LDS
+  // Keys with the sketch and codes of 1..4 bits select c / sqrt(d) instead of c: the residual
+  // is then one fma.  (Wide codes keep z - c, exact where z is near c: their residuals are short
+  // enough that rounding c / sqrt(d) first would show in the residual norm.)
+  constexpr float CSCALE = (KEY && QJL && BITS <= 4) ? INV_SQRT_D : 1.0f;
   float cent[LR], thr[LR];
 #pragma unroll
   for (int l = 0; l < LR; ++l) {
-    cent[l] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.centroids[l])));
+    cent[l] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.centroids[l]))) * CSCALE;
     thr[l] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a.thresholds[l])));
   }
   // Values of a multi-token call: lane (col, grp) of wave w holds rows 16 mt + 4 grp + i of output
@@ -377,9 +381,10 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
           put_code(row, o, idx, mt, nt, i);
         }
         if constexpr (KEY && QJL) {
-          // r = y - c / sqrt(d) = (z - c) / sqrt(d)
-          float r = ((BITS > 0) ? (z - c) : z) * INV_SQRT_D;
-          if (!(zsv[i] > 0.f)) r = 0.f;
+          // r = y - c / sqrt(d) = z / sqrt(d) - c / sqrt(d) (c holding c / sqrt(d) for 1..4-bit
+          // codes), or (z - c) / sqrt(d) for wide codes.  A zero row keeps this (nonzero)
+          // residual: its residual norm and sign word are set to 0 and all ones at the end.
+          const float r = BITS == 0 ? z * INV_SQRT_D : (BITS <= 4 ? fmaf(z, INV_SQRT_D, -c) : (z - c) * INV_SQRT_D);
           s_tile[row * XS_F32 + o] = r;
         }
       }
@@ -492,9 +497,11 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
         // wave's chunk rows (a one-token call: lane 0 holds the word of row 0, the token)
         const int rowk = one ? lo_slot - p0 : 16 * (col >> 2) + 4 * grp + (col & 3);
         const int slot_k = p0 + rowk;
+        // a zero row's signs are all ones (its residual was not zeroed)
+        const uint32_t sw = s_norm[one ? 0 : rowk] > 0.f ? sword : 0xFFFFFFFFu;
         if ((!one || lane == 0) && slot_k >= lo_slot && slot_k < hi_slot)
           *reinterpret_cast<uint32_t*>(a.signs + (bh * nblk + blk) * 1024 + ((rowk & 15) + 16 * wave) * 16 +
-                                       (rowk >> 4) * 4) = sword;
+                                       (rowk >> 4) * 4) = sw;
       }
     } else if (lanepack) {
       // the words packed in registers during the code search
