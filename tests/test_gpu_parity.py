@@ -3,6 +3,7 @@
 Every call goes through libtq's C ABI (kv_cache_vector_tq_amd binds it with ctypes).
 """
 import contextlib
+import math
 import os
 import sys
 
@@ -313,6 +314,44 @@ def test_attention_ragged_lengths(preset, G, repl):
             H.compare_attention(orc, Q[b, hs], kg, vg, lens[b], out[b, hs], scores[b, hs])
             # no score is written past the sequence length
             assert np.all(scores[b, hs, lens[b]:] == 0)
+
+
+@pytest.mark.parametrize("preset,G", [("turbo3", 4), ("turbo4", 8)])
+def test_attention_softmax_scale_edges(preset, G):
+    """Long per-wave streams (8 blocks per wave) through the online softmax's scale handling:
+    row 0 has logits rising along the sequence (the running maximum moves in many blocks), row 1
+    one key far above all others late in the sequence (a jump of the maximum by more than 2^32 in
+    the log2 domain, after many blocks that kept their scale), row 2 value norms over eight
+    decades (the weights' bound follows the value norms), row 3 plain Gaussian data."""
+    B, Hkv, T = 4, 8, 32768
+    cb, dp, cache = _setup(preset, B, Hkv, T)
+    rng = np.random.default_rng(23)
+    K = rng.standard_normal((B, Hkv, T, 128), dtype=np.float32)
+    V = rng.standard_normal((B, Hkv, T, 128), dtype=np.float32)
+    Q = wl.round_to_bf16(rng.standard_normal((B, Hkv * G, 128)).astype(np.float32))
+    ramp = np.linspace(0.0, 40.0, T, dtype=np.float32)[:, None]
+    for h in range(Hkv):
+        u = Q[0, h * G] / np.linalg.norm(Q[0, h * G])
+        K[0, h] += ramp * u[None, :]
+        u1 = Q[1, h * G] / np.linalg.norm(Q[1, h * G])
+        K[1, h, (8 * T) // 10] = 60.0 * u1 * math.sqrt(128)
+    V[2] *= (10.0 ** rng.uniform(-4.0, 4.0, size=(Hkv, T, 1))).astype(np.float32)
+    K, V = wl.round_to_bf16(K), wl.round_to_bf16(V)
+    start = torch.zeros(B, dtype=torch.int32, device="cuda")
+    say("scale-edges", preset, G, "quantize")
+    tq.tq_quantize_kv(cb, dp, cache, H.to_device(K, "bf16"), H.to_device(V, "bf16"), start)
+    seq = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    say("scale-edges", preset, G, "attend")
+    out = tq.tq_attend_decode(cb, dp, cache, H.to_device(Q, "bf16"), seq, T)
+    torch.cuda.synchronize()
+    hc, out = H.cache_host(cache), out.cpu().numpy()
+    orc = H.make_oracle(preset)
+    for b in range(B):
+        for h in (0, 5):
+            kg = H.unpack_keys(orc, hc, b, h, T)
+            vg = H.unpack_values(orc, hc, b, h, T)
+            hs = slice(h * G, (h + 1) * G)
+            H.compare_attention(orc, Q[b, hs], kg, vg, T, out[b, hs])
 
 
 @pytest.mark.parametrize("B,G,T_cap,lens", [(2, 8, 10240, [10240, 3001]), (1, 8, 40960, [40960 - 100]),
