@@ -122,10 +122,9 @@ __device__ __forceinline__ void static_for(F&& f) {
 //     2^B entries); the score takes a product with each term.  (One f16 term alone leaves the
 //     many distinct levels of a wide table a relative error up to 2^-12 each, which no common
 //     factor can remove and which reaches the logits; the pair holds each level to ~2^-24.)
-// Keys and values of the same width share one table.  (Tables with one copy of each entry per
-// lane slot, which make a wave's random lookups free of LDS bank conflicts, were measured
-// without gain on the batch-16 128K-context and 1M-context workloads: the loop is bound by its
-// dependent chain, not by LDS bandwidth.)
+// Keys and values of the same width share one table.  Long streams replicate the tables of
+// 8-bit keys per lane slot (REP below), which frees a wave's random lookups of LDS bank
+// conflicts.
 template <int B>
 struct Tab {
   static constexpr int K = B > 4 ? B : ((B == 3) ? 12 : 8);  // key bits
