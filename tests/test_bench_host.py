@@ -1,4 +1,5 @@
-"""Host-side checks of bench.py: the one-GPU refusal and the bulk-quantize byte accounting."""
+"""Host-side checks of bench.py: the one-GPU refusal, the bulk-quantize byte accounting and the
+counter-traffic record."""
 import json
 import os
 import subprocess
@@ -29,3 +30,20 @@ def test_bulk_bytes_match_the_layout(kb, kq, vb):
     the packed record out (the layout's bytes per token)."""
     B, Hkv, n = 3, 2, 1000
     assert bench.bulk_bytes(B, Hkv, n, kb, kq, vb) == B * Hkv * n * (512 + layout.bytes_per_token(kb, kq, vb)["total"])
+
+
+def test_counter_traffic_only_for_the_sources_it_was_taken_on(monkeypatch):
+    """The HBM bytes of the committed counter summary are reported for the workloads it covers
+    while the attention sources hash to the digest recorded with them, and are None otherwise
+    (so a changed kernel never carries stale counter figures)."""
+    rec = json.load(open(bench.TRAFFIC_FILE))
+    digest = bench.attend_sources_sha256()
+    for e in rec["entries"]:
+        assert abs(e["hbm_bytes_per_launch"] - e["fetch_bytes_per_launch"] - e["write_bytes_per_launch"]) <= 1
+        assert e["hbm_bytes_per_launch"] >= e["algorithmic_bytes_per_launch"]
+        expect = float(e["hbm_bytes_per_launch"]) if e["source_sha256"] == digest else None
+        assert bench.measured_traffic(e["workload"], e["preset"]) == expect
+    assert bench.measured_traffic("no_such_workload", "turbo3") is None
+    monkeypatch.setattr(bench, "attend_sources_sha256", lambda: "0" * 64)
+    for e in rec["entries"]:
+        assert bench.measured_traffic(e["workload"], e["preset"]) is None
