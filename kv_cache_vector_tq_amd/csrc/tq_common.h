@@ -41,6 +41,24 @@ __device__ __forceinline__ float bf2f(uint16_t b) {
   return __builtin_bit_cast(float, static_cast<uint32_t>(b) << 16);
 }
 
+// Splits 8 fp32 values in f16's range into two f16 terms hi + lo: hi truncated (round toward
+// zero), so that v - hi is exact in fp32, and lo that remainder rounded to nearest.  For v in
+// f16's normal range |v - hi - lo| <= 2^-21 |v|; below it the error is at most 2^-25.
+__device__ __forceinline__ void split2_f16(const float* v, f16x8& hi, f16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const auto hp = __builtin_amdgcn_cvt_pkrtz(v[2 * p], v[2 * p + 1]);
+    const _Float16 l0 = static_cast<_Float16>(v[2 * p] - static_cast<float>(hp[0]));
+    const _Float16 l1 = static_cast<_Float16>(v[2 * p + 1] - static_cast<float>(hp[1]));
+    h[p] = __builtin_bit_cast(uint32_t, hp);
+    l[p] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l0)) |
+           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, l1)) << 16);
+  }
+  hi = __builtin_bit_cast(f16x8, h);
+  lo = __builtin_bit_cast(f16x8, l);
+}
+
 // Exact split of 8 fp32 values into three bf16 terms: x = hi + mid + lo.  hi is x truncated
 // to its top 16 bits (a bf16 value); the remainder x - hi is exact in fp32 and has at most
 // 16 significant bits; mid is that remainder truncated the same way, and the last remainder

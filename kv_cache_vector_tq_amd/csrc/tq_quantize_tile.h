@@ -90,7 +90,7 @@ __device__ __forceinline__ void pack32(const uint8_t* c, uint32_t* w) {
 }
 
 struct Smem {
-  // input tile; later the fp32 residuals, then their three exact bf16 terms as planes
+  // input tile; later the fp32 residuals (times 2^10), then their two f16 terms as planes
   float tile[3 * PLANE / 2];
   uint8_t idx[64 * IDX_STRIDE];
   uint8_t sgn[64 * IDX_STRIDE];
@@ -100,10 +100,16 @@ struct Smem {
 };
 
 // Rotation (hi, lo) and sketch operands of one wave: lane (col, grp) holds row
-// 32 wave + 16 nt + col, columns 32 grp + 8 kb .. + 7.
+// 32 wave + 16 nt + col, columns 32 grp + 8 kb .. + 7.  The sketch rows are held as f16 values of
+// 2^4 S_b (exact: S_b is bf16, and the factor lifts its small entries into f16's normal range).
 struct Operands {
-  bf16x8 rh[2][4], rl[2][4], sb[2][4];
+  bf16x8 rh[2][4], rl[2][4];
+  f16x8 sb[2][4];
 };
+
+// Residual scale: the sketch takes 2^10 r, whose entries lie in f16's normal range down to
+// |r| = 2^-24 (the signs of the sketch are those of S_b r).
+constexpr float RSCALE = 1024.0f;
 
 // Issues the loads of tile r's input rows.  Rows outside [lo_slot, hi_slot) read a clamped
 // (written) row and are masked by the consumer.
@@ -304,10 +310,10 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
   // The codebook as wave-uniform register values (readfirstlane), so that the compare chain
   // selects values rather than addresses of the argument block.
   constexpr int LR = BITS <= 4 ? L : 1;  // wide tables stay in LDS
-  // Keys with the sketch and codes of 1..4 bits select c / sqrt(d) instead of c: the residual
-  // is then one fma.  (Wide codes keep z - c, exact where z is near c: their residuals are short
-  // enough that rounding c / sqrt(d) first would show in the residual norm.)
-  constexpr float CSCALE = (KEY && QJL && BITS <= 4) ? INV_SQRT_D : 1.0f;
+  // Keys with the sketch and codes of 1..4 bits select 2^10 c / sqrt(d) instead of c: the scaled
+  // residual is then one fma.  (Wide codes keep z - c, exact where z is near c: their residuals
+  // are short enough that rounding c / sqrt(d) first would show in the residual norm.)
+  constexpr float CSCALE = (KEY && QJL && BITS <= 4) ? RSCALE * INV_SQRT_D : 1.0f;
   float cent[LR], thr[LR];
 #pragma unroll
   for (int l = 0; l < LR; ++l) {
@@ -381,10 +387,11 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
           put_code(row, o, idx, mt, nt, i);
         }
         if constexpr (KEY && QJL) {
-          // r = y - c / sqrt(d) = z / sqrt(d) - c / sqrt(d) (c holding c / sqrt(d) for 1..4-bit
-          // codes), or (z - c) / sqrt(d) for wide codes.  A zero row keeps this (nonzero)
-          // residual: its residual norm and sign word are set to 0 and all ones at the end.
-          const float r = BITS == 0 ? z * INV_SQRT_D : (BITS <= 4 ? fmaf(z, INV_SQRT_D, -c) : (z - c) * INV_SQRT_D);
+          // 2^10 r with r = y - c / sqrt(d) = z / sqrt(d) - c / sqrt(d) (c holding 2^10 c / sqrt(d)
+          // for 1..4-bit codes), or (z - c) / sqrt(d) for wide codes.  A zero row keeps this
+          // (nonzero) residual: its residual norm and sign word are set to 0 and all ones at the end.
+          constexpr float RS = RSCALE * INV_SQRT_D;
+          const float r = BITS == 0 ? z * RS : (BITS <= 4 ? fmaf(z, RS, -c) : (z - c) * RS);
           s_tile[row * XS_F32 + o] = r;
         }
       }
@@ -394,8 +401,8 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
 
   uint32_t sword = 0u;  // keys with the sketch: this lane's sign word (see the sketch below)
   if constexpr (KEY && QJL) {
-    // ---- residual norms; with more than one active sub-tile, r is split once into its three
-    // exact bf16 terms (planes), else each wave splits the sub-tile's rows itself ----------------
+    // ---- residual norms; with more than one active sub-tile, 2^10 r is split once into its two
+    // f16 terms (planes), else each wave splits the sub-tile's rows itself -----------------------
     const bool planes = n_on > 1;  // uniform
     {
       const int row = tid >> 2, q = tid & 3;
@@ -409,24 +416,27 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
         for (int j = 0; j < 32; j += 4) ss = fmaf(v[j], v[j], fmaf(v[j + 1], v[j + 1], fmaf(v[j + 2], v[j + 2], fmaf(v[j + 3], v[j + 3], ss))));
         ss += __shfl_xor(ss, 1);
         ss += __shfl_xor(ss, 2);
-        if (q == 0) s_rnorm[row] = s_norm[row] > 0.f ? sqrtf(ss) : 0.f;
+        if (q == 0) s_rnorm[row] = s_norm[row] > 0.f ? sqrtf(ss) * (1.0f / RSCALE) : 0.f;
       }
       if (planes) {
-        bf16x8 ph[4], pm[4], pl[4];
+        f16x8 ph[4], pl[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) split3_bf16(v + 8 * i, ph[i], pm[i], pl[i]);
+        for (int i = 0; i < 4; ++i) split2_f16(v + 8 * i, ph[i], pl[i]);
         lds_barrier();  // every residual is read before the planes overwrite the tile
-        bf16x8* dst = reinterpret_cast<bf16x8*>(reinterpret_cast<uint16_t*>(s_tile) + row * XS_BF16 + 32 * q);
+        f16x8* dst = reinterpret_cast<f16x8*>(reinterpret_cast<uint16_t*>(s_tile) + row * XS_BF16 + 32 * q);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           dst[i] = ph[i];
-          dst[i + PLANE / 8] = pm[i];
-          dst[i + PLANE / 4] = pl[i];
+          dst[i + PLANE / 8] = pl[i];
         }
         lds_barrier();
       }
     }
-    // ---- sketch: u = S_b r, signs -----------------------------------------------------------
+    // ---- sketch: u = (2^4 S_b)(2^10 r), signs ------------------------------------------------
+    // Each product takes the two f16 terms of 2^10 r against the exact f16 2^4 S_b (fp32 sums).
+    // The terms hold 2^10 r to 2^-21 relative per entry, so u differs from 2^14 S_b r by at most
+    // 2^-21 ||S_b row|| ||2^10 r|| (about 7e-6 of 2^14 ||r|| for a row of 128 Gaussian entries):
+    // less than the 1e-5 ||r|| from 0 within which a sign is left undecided.
     // Lane (col, grp) of wave w holds u of sketch rows 32 w + 16 nt + col for the rows (tokens)
     // 16 mt + 4 grp + i, so two wave ballots of u >= 0 per (mt, i), one per nt, hold the 32-bit
     // sign words (chunk rows 32 w .. 32 w + 31) of the four tokens 16 mt + 4 grp + i, grp = 0..3,
@@ -440,24 +450,22 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
       const int row = 16 * mt + col;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        bf16x8 rh, rm, rl;
+        f16x8 rh, rl;
         if (planes) {
           const uint16_t* src = reinterpret_cast<const uint16_t*>(s_tile) + row * XS_BF16 + 32 * grp + 8 * kb;
-          rh = load_bf16x8(src);
-          rm = load_bf16x8(src + PLANE);
-          rl = load_bf16x8(src + 2 * PLANE);
+          rh = *reinterpret_cast<const f16x8*>(src);
+          rl = *reinterpret_cast<const f16x8*>(src + PLANE);
         } else {
           const float* src = s_tile + row * XS_F32 + 32 * grp + 8 * kb;
           float v[8];
           *reinterpret_cast<f32x4*>(v) = *reinterpret_cast<const f32x4*>(src);
           *reinterpret_cast<f32x4*>(v + 4) = *reinterpret_cast<const f32x4*>(src + 4);
-          split3_bf16(v, rh, rm, rl);
+          split2_f16(v, rh, rl);
         }
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          u[nt] = mfma_bf16(rh, sb[nt][kb], u[nt]);
-          u[nt] = mfma_bf16(rm, sb[nt][kb], u[nt]);
-          u[nt] = mfma_bf16(rl, sb[nt][kb], u[nt]);
+          u[nt] = mfma_f16(rh, sb[nt][kb], u[nt]);
+          u[nt] = mfma_f16(rl, sb[nt][kb], u[nt]);
         }
       }
 #pragma unroll
@@ -623,7 +631,13 @@ __device__ __forceinline__ void load_operands(Operands& op, const QuantArgs& k, 
     for (int kb = 0; kb < 4; ++kb) {
       op.rh[nt][kb] = load_bf16x8(k.r_hi + o * D + 32 * grp + 8 * kb);
       op.rl[nt][kb] = load_bf16x8(k.r_lo + o * D + 32 * grp + 8 * kb);
-      if constexpr (QJL) op.sb[nt][kb] = load_bf16x8(sb + o * D + 32 * grp + 8 * kb);
+      if constexpr (QJL) {
+        const u16x8 w = *reinterpret_cast<const u16x8*>(sb + o * D + 32 * grp + 8 * kb);
+        f16x8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = static_cast<_Float16>(__uint_as_float(static_cast<uint32_t>(w[e]) << 16) * 16.0f);
+        op.sb[nt][kb] = h;
+      }
     }
   }
 }
