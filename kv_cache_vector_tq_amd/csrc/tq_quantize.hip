@@ -12,12 +12,13 @@
 // kv-head, tensor) that the call writes, so each block has a single writer.  Keys and
 // values go through one launch; persistent workgroups (4 waves) keep the rotation and
 // sketch operands in registers and walk the tiles.  Wave w computes output coordinates
-// 32w..32w+31 of the tile's tokens with 16x16x32 bf16 MFMAs (16-token sub-tiles that hold
-// no token of the call are skipped):
+// 32w..32w+31 of the tile's tokens with 16x16x32 MFMAs (16-token sub-tiles that hold no token
+// of the call are skipped):
 //   * rotation: bf16 inputs are exact, R_eff = R_hi + R_lo takes two passes (fp32 inputs
 //     are split into three exact bf16 terms first), all products exact, fp32 accumulation;
-//   * sketch: r (fp32) is split into three exact bf16 terms, S_b is bf16, so u = S_b r is
-//     the fp32-accumulated product of the fp32 residual;
+//   * sketch: 2^10 r (fp32) is split into two f16 terms (2^-21 relative per entry) against
+//     2^4 S_b in f16 (exact), fp32 accumulation; the result differs from 2^14 S_b r by at most
+//     2^-21 ||S_b row|| ||2^10 r||, below the band within which the sign of u is left open;
 //   * codes: up to 4 bits from the thresholds held in registers (a compare chain, or a
 //     binary search at 3 bits); 5..8-bit key codes by a binary search over the thresholds
 //     staged in LDS, one compare per code bit.
