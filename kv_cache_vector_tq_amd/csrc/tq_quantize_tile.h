@@ -159,8 +159,12 @@ __device__ __forceinline__ void load_rows_norms(Smem& sm, const TileRef& tr, con
   const int p0 = tr.blk * 64, lo_slot = tr.lo_slot, hi_slot = tr.hi_slot;
   float* s_tile = sm.tile;
   float* s_norm = sm.norm;
-  // The norm is taken after an exact power-of-two rescaling by the row's largest magnitude,
-  // so that squares neither overflow nor underflow fp32 over the whole bf16 / fp32 range.
+  // The sum of squares is taken directly in fp32 and kept when it lies in [2^-60, 2^120] for
+  // every row of the wave: then no square overflowed, the squares lost below fp32's range sum to
+  // less than 2^-61 of it, and the rounding is that of the exactly rescaled sum.  Otherwise (a
+  // zero row, extreme magnitudes) the norm is taken after an exact power-of-two rescaling by
+  // the row's largest magnitude, so that squares neither overflow nor underflow fp32 over the
+  // whole bf16 / fp32 range.
   {
     const int row = tid >> 2, q = tid & 3;
     const int slot = p0 + row;
@@ -191,24 +195,32 @@ __device__ __forceinline__ void load_rows_norms(Smem& sm, const TileRef& tr, con
         }
       }
     }
-    float mx = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(v[e]));
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));
-    int ex = 0;
-    if (mx > 0.f) frexpf(mx, &ex);
-    // mx * 2^-ex lies in [0.5, 1); ldexp scales exactly over the whole fp32 range
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const float t = ldexpf(v[e], -ex);
-      ss = fmaf(t, t, ss);
-    }
+    for (int e = 0; e < 32; ++e) ss = fmaf(v[e], v[e], ss);
     ss += __shfl_xor(ss, 1);
     ss += __shfl_xor(ss, 2);
+    const bool exact = !__all(!valid || (ss >= 0x1p-60f && ss <= 0x1p120f));  // uniform
+    float mx = 0.f;
+    int ex = 0;
+    if (exact) {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(v[e]));
+      mx = fmaxf(mx, __shfl_xor(mx, 1));
+      mx = fmaxf(mx, __shfl_xor(mx, 2));
+      if (mx > 0.f) frexpf(mx, &ex);
+      // mx * 2^-ex lies in [0.5, 1); ldexp scales exactly over the whole fp32 range
+      ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const float t = ldexpf(v[e], -ex);
+        ss = fmaf(t, t, ss);
+      }
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+    }
     if (q == 0) {
-      const float n = mx > 0.f ? ldexpf(sqrtf(ss), ex) : 0.f;
+      const float n = !exact ? sqrtf(ss) : (mx > 0.f ? ldexpf(sqrtf(ss), ex) : 0.f);
       s_norm[row] = n;
       sm.zs[row] = n > 0.f ? zscale / n : 0.f;
     }
