@@ -316,6 +316,37 @@ def test_attention_ragged_lengths(preset, G, repl):
             assert np.all(scores[b, hs, lens[b]:] == 0)
 
 
+def test_attention_seq_len_clamped():
+    """Sequence lengths outside 1..max_seq_len are clamped into it on the device: rows with
+    lengths 0, -3 and beyond max_seq_len give bit for bit the outputs of lengths 1, 1 and
+    max_seq_len, and a row inside the range is unaffected by its neighbours."""
+    preset, G, B, Hkv, T_cap, max_len = "turbo3", 4, 4, 2, 1024, 700
+    cb, dp, cache = _setup(preset, B, Hkv, T_cap)
+    rng = np.random.default_rng(31)
+    K = wl.round_to_bf16(rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32))
+    V = wl.round_to_bf16(rng.standard_normal((B, Hkv, T_cap, 128)).astype(np.float32))
+    Q = H.to_device(wl.round_to_bf16(rng.standard_normal((B, Hkv * G, 128)).astype(np.float32)), "bf16")
+    tq.tq_quantize_kv(cb, dp, cache, H.to_device(K, "bf16"), H.to_device(V, "bf16"),
+                      torch.zeros(B, dtype=torch.int32, device="cuda"))
+    say("seq-len clamp", "attend")
+    got = tq.tq_attend_decode(cb, dp, cache, Q, torch.tensor([0, -3, 5000, 300], dtype=torch.int32, device="cuda"),
+                              max_len)
+    ref = tq.tq_attend_decode(cb, dp, cache, Q, torch.tensor([1, 1, max_len, 300], dtype=torch.int32, device="cuda"),
+                              max_len)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    # and the clamped rows are attention over 1 and max_seq_len keys
+    hc, out = H.cache_host(cache), ref.cpu().numpy()
+    orc = H.make_oracle(preset)
+    for b, T in ((0, 1), (2, max_len), (3, 300)):
+        for h in range(Hkv):
+            kg = H.unpack_keys(orc, hc, b, h, T)
+            vg = H.unpack_values(orc, hc, b, h, T)
+            hs = slice(h * G, (h + 1) * G)
+            H.compare_attention(orc, Q[b, hs].cpu().float().numpy(), kg, vg, T,
+                                out[b, hs])
+
+
 @pytest.mark.parametrize("preset,G", [("turbo3", 4), ("turbo4", 8)])
 def test_attention_softmax_scale_edges(preset, G):
     """Long per-wave streams (8 blocks per wave) through the online softmax's scale handling:
