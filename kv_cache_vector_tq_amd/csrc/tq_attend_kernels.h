@@ -794,6 +794,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
 
   // One block: scores, online softmax, value sums.  `d` holds the block's codes, `nrm` its norms.
   auto process = [&](const Blk& cur, const Norms& nrm, int blk) {
+    __builtin_amdgcn_s_setprio(1);  // MFMA-issuing phase: ahead of the other wave's softmax
 
     // ---- scores: tile t = keys 16 t .. 16 t + 15 of the block.  Per accumulator, the code and
     // sign MFMAs (operands zero outside their own terms' columns) sum into one register set.
@@ -875,6 +876,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
         cq[0][i] = row_ror<GC>(offer);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // logit * log2(e) = n (u1 C + u2 rnorm S): C, S are p, q (or q, p in the odd parts of a
     // shared accumulator); with one kind of term, p alone
     const bool odd = C::MIXED && (part & 1);
@@ -946,6 +948,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
     inv_run = inv;
     l_run = fmaf(l_run, alpha, lsum);
 
+    __builtin_amdgcn_s_setprio(1);
     // ---- value MFMAs: k-block kb2 holds tiles 2 kb2 (elements 0..3) and 2 kb2 + 1 (4..7) ---
     static_for<0, 2>([&](auto KB2) {
       constexpr int kb2 = decltype(KB2)::value;
@@ -964,6 +967,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
         acc[mt] = mfma_f16(av, bp, acc[mt]);
       });
     });
+    __builtin_amdgcn_s_setprio(0);
   };
   // Two blocks per iteration with the buffers swapping roles, so that the prefetched block never
   // has to be copied into the current one.  (Loading the next block's norms one block ahead as
