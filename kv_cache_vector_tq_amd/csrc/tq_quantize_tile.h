@@ -311,10 +311,14 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
       }
     }
   };
+  // The MFMA phases (rotation, sketch) run at raised issue priority: with two waves per SIMD the
+  // matrix core is fed while the other wave's code search fills the gaps.
+  __builtin_amdgcn_s_setprio(1);
   if (a.one_pass)  // uniform
     rotate(std::true_type{});
   else
     rotate(std::false_type{});
+  __builtin_amdgcn_s_setprio(0);
   lds_barrier();  // the input tile is dead from here on; its space holds residuals
 
   // ---- scale, scalar code, residual (sub-tiles without a token of the call are skipped; the
@@ -455,6 +459,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
     // in their 16-bit slices.  Lane (col, grp) keeps the word of token 16 (col / 4) + 4 grp +
     // col % 4 and stores it below.
     const auto& sb = op.sb;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (!mt_on[mt]) continue;
@@ -488,6 +493,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, Smem& sm, cons
         sword = col == 4 * mt + i ? w : sword;
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // ---- pack and store ------------------------------------------------------------------------
