@@ -603,8 +603,7 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
   for (int mt = 0; mt < 8; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Block data of one lane.  Codes of the next block are loaded while the current one is
-  // processed; the norms of the current block are loaded at its start (they are first needed
-  // after the score MFMAs).
+  // processed; so are its norms, up to 8 q-heads per kv-head (see the block loop below).
   struct Blk {
     uint32_t kd[KB > 0 ? 4 * KB : 1];
     uint32_t sd[4];
@@ -970,20 +969,36 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
     __builtin_amdgcn_s_setprio(0);
   };
   // Two blocks per iteration with the buffers swapping roles, so that the prefetched block never
-  // has to be copied into the current one.  (Loading the next block's norms one block ahead as
-  // well measured neutral on the long streams and slower on short launches.)
-  for (int blk = blk_begin; blk < blk_end; blk += 2) {
-    {
-      Norms nrm;
-      load_norms(blk, nrm);
+  // has to be copied into the current one.  Up to 8 q-heads per kv-head, the next block's norms
+  // are loaded one block ahead as well (norms loaded at the block's own start are waited for
+  // after its score MFMAs); with 16 q-heads the extra registers would spill, and the norms are
+  // loaded at the block's start.
+  if constexpr (G <= 8) {
+    Norms ncur, nnxt;
+    load_norms(min(blk_begin, nblk_cap - 1), ncur);
+    for (int blk = blk_begin; blk < blk_end; blk += 2) {
       load_block(min(blk + 1, blk_end - 1), nxt);
-      process(cur, nrm, blk);
+      load_norms(min(blk + 1, blk_end - 1), nnxt);
+      process(cur, ncur, blk);
+      if (blk + 1 >= blk_end) break;  // uniform
+      load_block(min(blk + 2, blk_end - 1), cur);
+      load_norms(min(blk + 2, blk_end - 1), ncur);
+      process(nxt, nnxt, blk + 1);
     }
-    if (blk + 1 >= blk_end) break;  // uniform
-    Norms nrm;
-    load_norms(blk + 1, nrm);
-    load_block(min(blk + 2, blk_end - 1), cur);
-    process(nxt, nrm, blk + 1);
+  } else {
+    for (int blk = blk_begin; blk < blk_end; blk += 2) {
+      {
+        Norms nrm;
+        load_norms(blk, nrm);
+        load_block(min(blk + 1, blk_end - 1), nxt);
+        process(cur, nrm, blk);
+      }
+      if (blk + 1 >= blk_end) break;  // uniform
+      Norms nrm;
+      load_norms(blk + 1, nrm);
+      load_block(min(blk + 2, blk_end - 1), cur);
+      process(nxt, nrm, blk + 1);
+    }
   }
 
   // Operands of R_eff^T for the unrotation, in case this workgroup becomes a merger: rows
