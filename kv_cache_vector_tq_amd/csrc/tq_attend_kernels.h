@@ -793,7 +793,10 @@ __global__ void __launch_bounds__(NT, 1) attend_kernel(MainArgs a, attn::KeyCent
 
   // One block: scores, online softmax, value sums.  `d` holds the block's codes, `nrm` its norms.
   auto process = [&](const Blk& cur, const Norms& nrm, int blk) {
-    __builtin_amdgcn_s_setprio(1);  // MFMA-issuing phase: ahead of the other wave's softmax
+    // Issue priority by phase: the score MFMAs (and the table reads feeding them) highest, the
+    // value MFMAs next, the softmax lowest, so that with two waves per SIMD the matrix core is
+    // fed while the other wave's softmax chain fills the gaps.
+    __builtin_amdgcn_s_setprio(2);
 
     // ---- scores: tile t = keys 16 t .. 16 t + 15 of the block.  Per accumulator, the code and
     // sign MFMAs (operands zero outside their own terms' columns) sum into one register set.
